@@ -1,0 +1,253 @@
+/*
+ * pa.h -- C ABI of the MI355X (gfx950) paged-attention library.
+ *
+ * The library implements one decode step of attention over a KV cache cut into
+ * fixed 16-token blocks that may sit anywhere in a preallocated physical pool,
+ * with per-request block tables mapping logical to physical blocks, blocks
+ * shared between requests with reference counts, and copy-on-write when a
+ * shared, partially filled block is appended to.  Sources (web pages on vLLM
+ * and PagedAttention, cited by title and section):
+ *   [ngrok]   techfeed.io summary of "Serving models at scale with vLLM",
+ *             sections "PagedAttention", "prefix caching", "the scheduler".
+ *   [tcd]     media.tcdigital.jp vLLM article, "paging", "logical and physical
+ *             block mapping", "memory sharing for parallel sampling".
+ *   [lens]    ta-paperlens "LLM serving from scratch", "prefill and decode",
+ *             eq. (1) and the KV-size example, "fragmentation and
+ *             PagedAttention", FIG 1, "scheduler skeleton".
+ *   [yj]      youngju.dev "vLLM inference optimization", "KV Cache problem",
+ *             "PagedAttention" (block diagram, PagedAttentionManager listing),
+ *             "copy-on-write prefix sharing".
+ *
+ * Conventions
+ *   - Every call returns a pa_status (or a plain value where noted); no C++
+ *     exception crosses this boundary.
+ *   - Host-side pool calls (pa_pool_*, pa_seq_*, pa_append_slots, ...) touch
+ *     host memory only and never call the GPU runtime.  A pool handle is not
+ *     thread-safe: one scheduler thread owns it.
+ *   - Device calls take raw device pointers owned by the caller and a HIP
+ *     stream (hipStream_t passed as void*; NULL = the null stream).  They only
+ *     enqueue work, never allocate or free device memory, and never
+ *     synchronise.  Arguments are validated on the host before any launch
+ *     (PA_ERR_INVALID); a failed launch returns PA_ERR_HIP.
+ *   - "fp16" means IEEE-754 binary16, passed as pa_half (its bit pattern).
+ *   - block_size is fixed at PA_BLOCK_SIZE = 16 tokens ([ngrok] "usually 16
+ *     tokens"; [yj] listing example).
+ *
+ * Device pool layout (one pool per K and per V, one layer):
+ *   K pool: [num_blocks][num_kv_heads][16][head_dim] fp16
+ *           slot s of block b, head h, dim c at ((b*H + h)*16 + s)*D + c
+ *   V pool: [num_blocks][num_kv_heads][head_dim][16] fp16
+ *           slot s of block b, head h, dim c at ((b*H + h)*D + c)*16 + s
+ *   A (block, kv head) tile is 16*D*2 bytes contiguous in each pool (4 KiB at
+ *   D = 128).  K keeps a token's row contiguous; V keeps each dimension's 16
+ *   slots contiguous, so that both feed the matrix cores' operand registers
+ *   directly.  A slot id is block*16 + offset.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_BLOCK_SIZE 16
+
+typedef uint16_t pa_half; /* IEEE binary16 bit pattern */
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID = 1,        /* bad argument or geometry; nothing changed        */
+  PA_ERR_OUT_OF_BLOCKS = 2,  /* free list cannot cover the request; nothing changed */
+  PA_ERR_UNKNOWN_SEQ = 3,    /* sequence id not present; nothing changed          */
+  PA_ERR_EXISTS = 4,         /* sequence id already present; nothing changed      */
+  PA_ERR_CAPACITY = 5,       /* a caller buffer is too small; nothing changed     */
+  PA_ERR_HIP = 6,            /* the HIP runtime reported an error                 */
+  PA_ERR_INTERNAL = 7        /* an invariant check failed                         */
+} pa_status;
+
+/* Text for a status code (static storage). */
+const char* pa_status_string(pa_status s);
+
+/* ------------------------------------------------------------------------ */
+/* Host block manager                                                        */
+/* ------------------------------------------------------------------------ */
+
+typedef struct pa_pool pa_pool;
+
+typedef struct pa_pool_desc {
+  int32_t num_blocks;          /* physical blocks in the pool, >= 1, num_blocks*16 < 2^31 */
+  int32_t block_size;          /* must be PA_BLOCK_SIZE                                     */
+  const int32_t* free_order;   /* NULL, or a permutation of [0, num_blocks): the initial
+                                  free stack from bottom to top (allocation pops the top).
+                                  NULL = ascending ids, as [yj]'s listing builds it.       */
+} pa_pool_desc;
+
+/* One copy-on-write copy: the first n_slots slots of every KV head of block
+ * src are copied to block dst, in both pools ([tcd] memory sharing). */
+typedef struct pa_copy {
+  int32_t src;
+  int32_t dst;
+  int32_t n_slots;
+} pa_copy;
+
+typedef struct pa_pool_stats {
+  int32_t num_blocks;
+  int32_t num_free;
+  int32_t num_seqs;
+  int32_t reserved;
+  int64_t allocs;   /* blocks taken off the free list (including CoW targets) */
+  int64_t frees;    /* blocks returned to the free list                       */
+  int64_t cows;     /* copy-on-write copies planned                          */
+} pa_pool_stats;
+
+/* Create a pool's host metadata ([yj] listing: the whole pool is known up
+ * front and every block starts free).  *out is owned by the caller and
+ * released with pa_pool_destroy.  PA_ERR_INVALID on bad geometry or a
+ * free_order that is not a permutation. */
+pa_status pa_pool_create(const pa_pool_desc* desc, pa_pool** out);
+void pa_pool_destroy(pa_pool* pool);
+
+/* Register an empty request (no blocks reserved: [ngrok] "PagedAttention").
+ * PA_ERR_EXISTS if seq_id is live. */
+pa_status pa_seq_add(pa_pool* pool, int64_t seq_id);
+
+/* Child shares all of parent's blocks; each block's reference count + 1
+ * ([tcd] memory sharing for parallel sampling).  PA_ERR_UNKNOWN_SEQ /
+ * PA_ERR_EXISTS. */
+pa_status pa_seq_fork(pa_pool* pool, int64_t parent, int64_t child);
+
+/* Drop the request: each block's count - 1 in logical order; a block reaching
+ * zero is pushed on the free stack (request finished or preempted: [ngrok]
+ * scheduler; [lens] scheduler skeleton). */
+pa_status pa_seq_free(pa_pool* pool, int64_t seq_id);
+
+/* Blocks pa_append_slots would take off the free list for the same arguments
+ * (new blocks + copy-on-write targets).  Pure. */
+pa_status pa_can_append(const pa_pool* pool, int32_t n, const int64_t* seq_ids,
+                        const int32_t* n_new, int32_t* blocks_needed);
+
+/* Reserve slots for n_new[i] tokens of seq_ids[i], i < n, sequences in the
+ * order given (ids must be distinct), tokens in position order.  For a token
+ * at position p of its request, o = p % 16:
+ *   o == 0          -> pop a block from the free stack and append it to the
+ *                      request's table ([ngrok]: a new block only when the
+ *                      last one is full; [yj] listing);
+ *   o > 0, shared   -> copy-on-write: pop a block, record {old, new, o},
+ *                      old's count - 1, table entry := new ([tcd]);
+ *   slot = table[p / 16] * 16 + o.
+ * slot_mapping receives sum(n_new) slots in (sequence, position) order
+ * (capacity slot_cap); copies receives the CoW list (capacity copy_cap,
+ * count in *n_copies).  Atomic: on PA_ERR_OUT_OF_BLOCKS ([yj] listing: no free
+ * block is an error), PA_ERR_CAPACITY, PA_ERR_UNKNOWN_SEQ or PA_ERR_INVALID
+ * the pool is unchanged, so the caller can preempt and retry. */
+pa_status pa_append_slots(pa_pool* pool, int32_t n, const int64_t* seq_ids,
+                          const int32_t* n_new, int32_t* slot_mapping, int64_t slot_cap,
+                          pa_copy* copies, int32_t copy_cap, int32_t* n_copies);
+
+/* Block tables of the listed requests, row-major [n][max_blocks] int32 padded
+ * with -1, and their token counts ([tcd]: the table maps logical to physical
+ * blocks).  Caller-owned host buffers.  PA_ERR_CAPACITY if a table is longer
+ * than max_blocks. */
+pa_status pa_block_tables(const pa_pool* pool, int32_t n, const int64_t* seq_ids,
+                          int32_t max_blocks, int32_t* tables, int32_t* seq_lens);
+
+/* One request's table (capacity cap) and length. */
+pa_status pa_seq_table(const pa_pool* pool, int64_t seq_id, int32_t* table, int32_t cap,
+                       int32_t* n_blocks, int32_t* seq_len);
+
+int32_t pa_num_free_blocks(const pa_pool* pool);
+pa_status pa_ref_count(const pa_pool* pool, int32_t block, int32_t* ref);
+pa_status pa_pool_get_stats(const pa_pool* pool, pa_pool_stats* stats);
+
+/* Free stack contents from bottom to top (capacity cap, count in *n). */
+pa_status pa_free_list(const pa_pool* pool, int32_t* out, int32_t cap, int32_t* n);
+
+/* Invariants: free + referenced = num_blocks; each block's count equals the
+ * number of tables holding it; each table has ceil(len/16) entries; the free
+ * stack holds distinct unreferenced blocks.  PA_ERR_INTERNAL if violated. */
+pa_status pa_pool_check(const pa_pool* pool);
+
+/* Bytes one token's K and V occupy: 2 * layers * kv_heads * head_dim *
+ * dtype_bytes ([lens] KV-size example: 131,072 for 32/8/128/fp16). */
+uint64_t pa_kv_bytes_per_token(int32_t layers, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t dtype_bytes);
+
+/* ------------------------------------------------------------------------ */
+/* Device kernels (gfx950)                                                   */
+/* ------------------------------------------------------------------------ */
+
+typedef struct pa_kv_view {
+  pa_half* k_pool;       /* device, layout above */
+  pa_half* v_pool;       /* device, layout above */
+  int32_t num_blocks;
+  int32_t block_size;    /* must be PA_BLOCK_SIZE */
+  int32_t num_kv_heads;  /* >= 1 */
+  int32_t head_dim;      /* 64 or 128 */
+} pa_kv_view;
+
+/* Store T new tokens' K and V into their slots ([yj] listing, the
+ * cache[block, slot] store of append_token).  k, v: device [T][kv_heads][D]
+ * fp16, contiguous.  slot_mapping: device int32 [T]; a negative slot skips the
+ * token; a slot >= num_blocks*16 is ignored (never written).  Bit copy. */
+pa_status pa_reshape_and_cache(const pa_half* k, const pa_half* v, const int32_t* slot_mapping,
+                               int32_t num_tokens, pa_kv_view kv, void* stream);
+
+/* Perform n copy-on-write copies (device array of pa_copy, as returned by
+ * pa_append_slots).  Entries with an out-of-range block or n_slots outside
+ * [0, 16] are skipped.  Bit copy.  Must be ordered before the
+ * pa_reshape_and_cache of the same step (same stream). */
+pa_status pa_copy_blocks(const pa_copy* copies, int32_t n, pa_kv_view kv, void* stream);
+
+/* Workspace bytes pa_paged_attention_decode needs: partial (o, m, l) for every
+ * (request, query head, partition) = B * n_q * ceil(max_seq_len/partition) *
+ * (head_dim + 2) * 4. */
+uint64_t pa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                                   int32_t max_seq_len, int32_t partition_size);
+
+/* One decode step of attention over the paged cache ([lens] "fragmentation
+ * and PagedAttention": the kernel follows the table to gather K and V while
+ * computing).  For request i, query head h, kv head g = h / (n_q / kv_heads):
+ *   out[i][h] = sum_j softmax_j(scale * q[i][h] . K_j) V_j,  j < seq_lens[i],
+ * K_j, V_j the j-th logical token, in block tables[i][j/16] at slot j%16.
+ *   out: device [B][n_q][D] fp16 (RNE from fp32).  q: device [B][n_q][D] fp16.
+ *   tables: device int32 [B][max_blocks]; seq_lens: device int32 [B], each in
+ *   [0, max_seq_len] and <= max_blocks*16 (a request of length 0 gets zeros).
+ *   n_q must be a multiple of kv_heads with n_q/kv_heads <= 16.
+ *   Requests are split into partitions of partition_size tokens (a multiple of
+ *   32, e.g. 512); each (kv head, request, partition) is one workgroup that
+ *   writes a partial softmax state, and a second kernel merges partitions by
+ *   log-sum-exp.  workspace: device, >= pa_decode_workspace_bytes(...).
+ *   A table entry outside [0, num_blocks) or a length above max_blocks*16
+ *   makes that request's output NaN (no out-of-bounds access). */
+pa_status pa_paged_attention_decode(pa_half* out, const pa_half* q, pa_kv_view kv,
+                                    const int32_t* tables, int32_t max_blocks,
+                                    const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                                    float scale, int32_t partition_size, int32_t max_seq_len,
+                                    void* workspace, uint64_t workspace_bytes, void* stream);
+
+/* Workspace bytes pa_paged_attention_prefill needs for a chunk of chunk_len
+ * query rows ending at key position q_start + chunk_len. */
+uint64_t pa_prefill_workspace_bytes(int32_t chunk_len, int32_t num_q_heads, int32_t head_dim,
+                                    int32_t q_start);
+
+/* Causal attention of one prefill chunk over the paged cache ([ngrok]
+ * chunked prefill; [lens] FIG 1, prefill grows with the square of the
+ * length).  Row r < chunk_len is the query at absolute position q_start + r
+ * and attends keys 0..q_start + r of the request whose block table is
+ * `table` (device int32, >= ceil((q_start+chunk_len)/16) entries); the
+ * chunk's own K/V must already be stored (pa_reshape_and_cache).
+ *   out: device [chunk_len][n_q][D] fp16; q: device [chunk_len][n_q][D] fp16.
+ *   head_dim must be 128; n_q/kv_heads <= 16 and divides n_q.
+ *   workspace: device, >= pa_prefill_workspace_bytes(...). */
+pa_status pa_paged_attention_prefill(pa_half* out, const pa_half* q, pa_kv_view kv,
+                                     const int32_t* table, int32_t table_len, int32_t q_start,
+                                     int32_t chunk_len, int32_t num_q_heads, float scale,
+                                     void* workspace, uint64_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,296 @@
+"""ctypes binding of ``libpagedattn.so`` (argument marshalling only).
+
+Every function here has the name of the C entry point it wraps (see
+include/pa.h) and does nothing but convert arguments: Python ints, numpy
+arrays for host buffers, and objects exposing ``data_ptr()`` (torch tensors)
+for device buffers.  All computation happens in the library; if the library
+is missing the import fails loudly -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
+
+PA_OK = 0
+PA_ERR_INVALID = 1
+PA_ERR_OUT_OF_BLOCKS = 2
+PA_ERR_UNKNOWN_SEQ = 3
+PA_ERR_EXISTS = 4
+PA_ERR_CAPACITY = 5
+PA_ERR_HIP = 6
+PA_ERR_INTERNAL = 7
+BLOCK_SIZE = 16
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+class OutOfBlocksError(PaError):
+    pass
+
+
+class pa_pool_desc(C.Structure):
+    _fields_ = [("num_blocks", C.c_int32), ("block_size", C.c_int32),
+                ("free_order", C.POINTER(C.c_int32))]
+
+
+class pa_copy(C.Structure):
+    _fields_ = [("src", C.c_int32), ("dst", C.c_int32), ("n_slots", C.c_int32)]
+
+
+class pa_pool_stats(C.Structure):
+    _fields_ = [("num_blocks", C.c_int32), ("num_free", C.c_int32), ("num_seqs", C.c_int32),
+                ("reserved", C.c_int32), ("allocs", C.c_int64), ("frees", C.c_int64),
+                ("cows", C.c_int64)]
+
+
+class pa_kv_view(C.Structure):
+    _fields_ = [("k_pool", C.c_void_p), ("v_pool", C.c_void_p), ("num_blocks", C.c_int32),
+                ("block_size", C.c_int32), ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32)]
+
+
+# name -> (restype, argtypes)
+_P = C.c_void_p
+_I32 = C.c_int32
+_I64 = C.c_int64
+_U64 = C.c_uint64
+_SIGS = {
+    "pa_status_string": (C.c_char_p, [C.c_int]),
+    "pa_pool_create": (C.c_int, [C.POINTER(pa_pool_desc), C.POINTER(_P)]),
+    "pa_pool_destroy": (None, [_P]),
+    "pa_seq_add": (C.c_int, [_P, _I64]),
+    "pa_seq_fork": (C.c_int, [_P, _I64, _I64]),
+    "pa_seq_free": (C.c_int, [_P, _I64]),
+    "pa_can_append": (C.c_int, [_P, _I32, _P, _P, C.POINTER(_I32)]),
+    "pa_append_slots": (C.c_int, [_P, _I32, _P, _P, _P, _I64, _P, _I32, C.POINTER(_I32)]),
+    "pa_block_tables": (C.c_int, [_P, _I32, _P, _I32, _P, _P]),
+    "pa_seq_table": (C.c_int, [_P, _I64, _P, _I32, C.POINTER(_I32), C.POINTER(_I32)]),
+    "pa_num_free_blocks": (_I32, [_P]),
+    "pa_ref_count": (C.c_int, [_P, _I32, C.POINTER(_I32)]),
+    "pa_pool_get_stats": (C.c_int, [_P, C.POINTER(pa_pool_stats)]),
+    "pa_free_list": (C.c_int, [_P, _P, _I32, C.POINTER(_I32)]),
+    "pa_pool_check": (C.c_int, [_P]),
+    "pa_kv_bytes_per_token": (_U64, [_I32, _I32, _I32, _I32]),
+    "pa_reshape_and_cache": (C.c_int, [_P, _P, _P, _I32, pa_kv_view, _P]),
+    "pa_copy_blocks": (C.c_int, [_P, _I32, pa_kv_view, _P]),
+    "pa_decode_workspace_bytes": (_U64, [_I32, _I32, _I32, _I32, _I32]),
+    "pa_paged_attention_decode": (C.c_int, [_P, _P, pa_kv_view, _P, _I32, _P, _I32, _I32,
+                                            C.c_float, _I32, _I32, _P, _U64, _P]),
+    "pa_prefill_workspace_bytes": (_U64, [_I32, _I32, _I32, _I32]),
+    "pa_paged_attention_prefill": (C.c_int, [_P, _P, pa_kv_view, _P, _I32, _I32, _I32, _I32,
+                                             C.c_float, _P, _U64, _P]),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m pagedattention_block_paged_reshape_amd.build` (no fallback exists)")
+    lib = C.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+LIB = _load()
+EXPORTED = tuple(_SIGS)
+
+
+def status_string(status: int) -> str:
+    return LIB.pa_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status == PA_ERR_OUT_OF_BLOCKS:
+        raise OutOfBlocksError(status, where)
+    if status != PA_OK:
+        raise PaError(status, where)
+
+
+def _host(a, dtype) -> np.ndarray:
+    arr = np.ascontiguousarray(np.asarray(a, dtype=dtype))
+    return arr
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data if a.size else 0
+
+
+def _dptr(t) -> Optional[int]:
+    """Device pointer of a torch tensor (or an int address, or None)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ---------------------------------------------------------------- host pool
+
+def pa_pool_create(num_blocks: int, free_order: Optional[Sequence[int]] = None,
+                   block_size: int = BLOCK_SIZE) -> int:
+    order = None if free_order is None else _host(free_order, np.int32)
+    desc = pa_pool_desc(int(num_blocks), int(block_size),
+                        None if order is None else order.ctypes.data_as(C.POINTER(C.c_int32)))
+    handle = _P()
+    _check(LIB.pa_pool_create(C.byref(desc), C.byref(handle)), "pa_pool_create")
+    return handle.value
+
+
+def pa_pool_destroy(pool: int) -> None:
+    LIB.pa_pool_destroy(pool)
+
+
+def pa_seq_add(pool: int, seq_id: int) -> None:
+    _check(LIB.pa_seq_add(pool, int(seq_id)), "pa_seq_add")
+
+
+def pa_seq_fork(pool: int, parent: int, child: int) -> None:
+    _check(LIB.pa_seq_fork(pool, int(parent), int(child)), "pa_seq_fork")
+
+
+def pa_seq_free(pool: int, seq_id: int) -> None:
+    _check(LIB.pa_seq_free(pool, int(seq_id)), "pa_seq_free")
+
+
+def pa_can_append(pool: int, seq_ids, n_new) -> int:
+    ids = _host(seq_ids, np.int64)
+    nn = _host(n_new, np.int32)
+    out = _I32()
+    _check(LIB.pa_can_append(pool, len(ids), _ptr(ids), _ptr(nn), C.byref(out)), "pa_can_append")
+    return out.value
+
+
+def pa_append_slots(pool: int, seq_ids, n_new):
+    """Returns (slot_mapping int32[T], copies int32[n][3] as (src, dst, n_slots))."""
+    ids = _host(seq_ids, np.int64)
+    nn = _host(n_new, np.int32)
+    T = int(nn.sum()) if nn.size else 0
+    slots = np.empty(max(T, 1), dtype=np.int32)
+    cap = len(ids)
+    copies = (pa_copy * max(cap, 1))()
+    n_copies = _I32()
+    _check(LIB.pa_append_slots(pool, len(ids), _ptr(ids), _ptr(nn), slots.ctypes.data, T,
+                               C.addressof(copies), cap, C.byref(n_copies)), "pa_append_slots")
+    cp = np.array([(c.src, c.dst, c.n_slots) for c in copies[:n_copies.value]],
+                  dtype=np.int32).reshape(-1, 3)
+    return slots[:T], cp
+
+
+def pa_block_tables(pool: int, seq_ids, max_blocks: int):
+    ids = _host(seq_ids, np.int64)
+    tables = np.empty((len(ids), max(int(max_blocks), 0)), dtype=np.int32)
+    lens = np.empty(len(ids), dtype=np.int32)
+    _check(LIB.pa_block_tables(pool, len(ids), _ptr(ids), int(max_blocks), _ptr(tables),
+                               _ptr(lens)), "pa_block_tables")
+    return tables, lens
+
+
+def pa_seq_table(pool: int, seq_id: int):
+    nb, ln = _I32(), _I32()
+    st = LIB.pa_seq_table(pool, int(seq_id), None, 0, C.byref(nb), C.byref(ln))
+    if st not in (PA_OK, PA_ERR_CAPACITY):
+        _check(st, "pa_seq_table")
+    buf = np.empty(max(nb.value, 1), dtype=np.int32)
+    _check(LIB.pa_seq_table(pool, int(seq_id), buf.ctypes.data, nb.value, C.byref(nb),
+                            C.byref(ln)), "pa_seq_table")
+    return buf[:nb.value], ln.value
+
+
+def pa_num_free_blocks(pool: int) -> int:
+    return int(LIB.pa_num_free_blocks(pool))
+
+
+def pa_ref_count(pool: int, block: int) -> int:
+    out = _I32()
+    _check(LIB.pa_ref_count(pool, int(block), C.byref(out)), "pa_ref_count")
+    return out.value
+
+
+def pa_pool_get_stats(pool: int) -> dict:
+    s = pa_pool_stats()
+    _check(LIB.pa_pool_get_stats(pool, C.byref(s)), "pa_pool_get_stats")
+    return {k: getattr(s, k) for k, _ in pa_pool_stats._fields_ if k != "reserved"}
+
+
+def pa_free_list(pool: int) -> np.ndarray:
+    n = _I32()
+    LIB.pa_free_list(pool, None, 0, C.byref(n))
+    buf = np.empty(max(n.value, 1), dtype=np.int32)
+    _check(LIB.pa_free_list(pool, buf.ctypes.data, n.value, C.byref(n)), "pa_free_list")
+    return buf[:n.value]
+
+
+def pa_pool_check(pool: int) -> None:
+    _check(LIB.pa_pool_check(pool), "pa_pool_check")
+
+
+def pa_kv_bytes_per_token(layers: int, num_kv_heads: int, head_dim: int, dtype_bytes: int) -> int:
+    return int(LIB.pa_kv_bytes_per_token(layers, num_kv_heads, head_dim, dtype_bytes))
+
+
+# ------------------------------------------------------------------ device
+
+def kv_view(k_pool, v_pool, num_blocks: int, num_kv_heads: int, head_dim: int) -> pa_kv_view:
+    return pa_kv_view(_dptr(k_pool), _dptr(v_pool), int(num_blocks), BLOCK_SIZE,
+                      int(num_kv_heads), int(head_dim))
+
+
+def pa_reshape_and_cache(k, v, slot_mapping, num_tokens: int, kv: pa_kv_view, stream=None) -> None:
+    _check(LIB.pa_reshape_and_cache(_dptr(k), _dptr(v), _dptr(slot_mapping), int(num_tokens), kv,
+                                    _stream(stream)), "pa_reshape_and_cache")
+
+
+def pa_copy_blocks(copies, n: int, kv: pa_kv_view, stream=None) -> None:
+    _check(LIB.pa_copy_blocks(_dptr(copies), int(n), kv, _stream(stream)), "pa_copy_blocks")
+
+
+def pa_decode_workspace_bytes(batch: int, num_q_heads: int, head_dim: int, max_seq_len: int,
+                              partition_size: int) -> int:
+    return int(LIB.pa_decode_workspace_bytes(batch, num_q_heads, head_dim, max_seq_len,
+                                             partition_size))
+
+
+def pa_paged_attention_decode(out, q, kv: pa_kv_view, tables, max_blocks: int, seq_lens,
+                              batch: int, num_q_heads: int, scale: float, partition_size: int,
+                              max_seq_len: int, workspace, workspace_bytes: int,
+                              stream=None) -> None:
+    _check(LIB.pa_paged_attention_decode(_dptr(out), _dptr(q), kv, _dptr(tables), int(max_blocks),
+                                         _dptr(seq_lens), int(batch), int(num_q_heads),
+                                         float(scale), int(partition_size), int(max_seq_len),
+                                         _dptr(workspace), int(workspace_bytes),
+                                         _stream(stream)), "pa_paged_attention_decode")
+
+
+def pa_prefill_workspace_bytes(chunk_len: int, num_q_heads: int, head_dim: int,
+                               q_start: int) -> int:
+    return int(LIB.pa_prefill_workspace_bytes(chunk_len, num_q_heads, head_dim, q_start))
+
+
+def pa_paged_attention_prefill(out, q, kv: pa_kv_view, table, table_len: int, q_start: int,
+                               chunk_len: int, num_q_heads: int, scale: float, workspace,
+                               workspace_bytes: int, stream=None) -> None:
+    _check(LIB.pa_paged_attention_prefill(_dptr(out), _dptr(q), kv, _dptr(table), int(table_len),
+                                          int(q_start), int(chunk_len), int(num_q_heads),
+                                          float(scale), _dptr(workspace), int(workspace_bytes),
+                                          _stream(stream)), "pa_paged_attention_prefill")

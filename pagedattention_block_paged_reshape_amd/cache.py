@@ -1,0 +1,172 @@
+"""A paged K/V cache on one GPU, driven through the C ABI.
+
+``PagedKVCache`` owns a host block pool (``pa_pool_*``) and the two device
+pool tensors of one layer, and strings the library's calls together in the
+order one step needs them (the scheduler sketch of ta-paperlens: reserve
+blocks for every running request, then run the forward pass):
+
+    pa_append_slots -> H2D(slot_mapping, copies) -> pa_copy_blocks
+        -> pa_reshape_and_cache -> pa_block_tables -> H2D(tables, lens)
+        -> pa_paged_attention_decode / pa_paged_attention_prefill
+
+PyTorch only provides device memory, streams and host<->device copies; every
+computation is one of the library's kernels.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+DEFAULT_PARTITION = 512
+
+
+class PagedKVCache:
+    def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int,
+                 free_order: Optional[Sequence[int]] = None, device="cuda:0",
+                 fill_byte: Optional[int] = None):
+        self.num_blocks = int(num_blocks)
+        self.n_kv = int(num_kv_heads)
+        self.d = int(head_dim)
+        self.device = torch.device(device)
+        self.pool = L.pa_pool_create(self.num_blocks, free_order)
+        shape_k = (self.num_blocks, self.n_kv, L.BLOCK_SIZE, self.d)
+        shape_v = (self.num_blocks, self.n_kv, self.d, L.BLOCK_SIZE)
+        self.k_pool = torch.empty(shape_k, dtype=torch.float16, device=self.device)
+        self.v_pool = torch.empty(shape_v, dtype=torch.float16, device=self.device)
+        if fill_byte is not None:
+            self.k_pool.view(torch.uint8).fill_(fill_byte)
+            self.v_pool.view(torch.uint8).fill_(fill_byte)
+        self.kv = L.kv_view(self.k_pool, self.v_pool, self.num_blocks, self.n_kv, self.d)
+
+    def close(self):
+        if self.pool:
+            L.pa_pool_destroy(self.pool)
+            self.pool = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- host-side request bookkeeping -------------------------------------
+    def add(self, seq_id: int):
+        L.pa_seq_add(self.pool, seq_id)
+
+    def fork(self, parent: int, child: int):
+        L.pa_seq_fork(self.pool, parent, child)
+
+    def free(self, seq_id: int):
+        L.pa_seq_free(self.pool, seq_id)
+
+    def seq_len(self, seq_id: int) -> int:
+        return L.pa_seq_table(self.pool, seq_id)[1]
+
+    # -- one append: reserve, copy-on-write, store --------------------------
+    def append(self, seq_ids, n_new, k_rows: torch.Tensor, v_rows: torch.Tensor,
+               stream: Optional[torch.cuda.Stream] = None):
+        """Reserve slots for the tokens, then store their K/V rows
+        ([T][n_kv][d] fp16 on the device, in (sequence, position) order).
+        Returns (slot_mapping, copies) as host arrays."""
+        slots, copies = L.pa_append_slots(self.pool, seq_ids, n_new)
+        T = len(slots)
+        if T != k_rows.shape[0] or T != v_rows.shape[0]:
+            raise ValueError(f"{T} slots reserved but {k_rows.shape[0]} K rows given")
+        stream = stream or torch.cuda.current_stream(self.device)
+        with torch.cuda.stream(stream):
+            if len(copies):
+                d_copies = torch.from_numpy(np.ascontiguousarray(copies)).to(
+                    self.device, non_blocking=False)
+                L.pa_copy_blocks(d_copies, len(copies), self.kv, stream)
+            if T:
+                d_slots = torch.from_numpy(slots).to(self.device, non_blocking=False)
+                L.pa_reshape_and_cache(k_rows, v_rows, d_slots, T, self.kv, stream)
+        return slots, copies
+
+    def tables(self, seq_ids, max_blocks: Optional[int] = None):
+        """Device block tables [B][max_blocks] and lengths [B], plus the max length."""
+        seq_ids = list(seq_ids)
+        lens = [self.seq_len(s) for s in seq_ids]
+        if max_blocks is None:
+            max_blocks = max([1] + [-(-x // L.BLOCK_SIZE) for x in lens])
+        tab, ln = L.pa_block_tables(self.pool, seq_ids, max_blocks)
+        return (torch.from_numpy(tab).to(self.device), torch.from_numpy(ln).to(self.device),
+                int(ln.max()) if len(ln) else 0, max_blocks)
+
+
+class DecodePlan:
+    """Device-resident arguments of one decode launch (tables, lengths,
+    workspace), so repeated launches time only the kernels."""
+
+    def __init__(self, cache: PagedKVCache, seq_ids, num_q_heads: int, scale: float,
+                 partition: int = DEFAULT_PARTITION, out: Optional[torch.Tensor] = None):
+        self.cache = cache
+        self.tables, self.lens, self.max_len, self.max_blocks = cache.tables(seq_ids)
+        self.batch = len(list(seq_ids))
+        self.n_q = int(num_q_heads)
+        self.scale = float(scale)
+        self.partition = int(partition)
+        ws = L.pa_decode_workspace_bytes(self.batch, self.n_q, cache.d, max(self.max_len, 1),
+                                         self.partition)
+        self.ws_bytes = ws
+        self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=cache.device)
+        self.out = out if out is not None else torch.empty(
+            (self.batch, self.n_q, cache.d), dtype=torch.float16, device=cache.device)
+
+    def run(self, q: torch.Tensor, stream=None) -> torch.Tensor:
+        L.pa_paged_attention_decode(self.out, q, self.cache.kv, self.tables, self.max_blocks,
+                                    self.lens, self.batch, self.n_q, self.scale, self.partition,
+                                    self.max_len, self.workspace, self.ws_bytes,
+                                    stream or torch.cuda.current_stream(self.cache.device))
+        return self.out
+
+
+class PrefillPlan:
+    """Device-resident arguments of one prefill-chunk launch."""
+
+    def __init__(self, cache: PagedKVCache, seq_id: int, q_start: int, chunk_len: int,
+                 num_q_heads: int, scale: float):
+        self.cache = cache
+        tab, _, self.seq_len, self.table_len = cache.tables([seq_id])
+        self.table = tab[0].contiguous()
+        self.q_start, self.chunk_len = int(q_start), int(chunk_len)
+        self.n_q, self.scale = int(num_q_heads), float(scale)
+        ws = L.pa_prefill_workspace_bytes(self.chunk_len, self.n_q, cache.d, self.q_start)
+        self.ws_bytes = ws
+        self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=cache.device)
+        self.out = torch.empty((self.chunk_len, self.n_q, cache.d), dtype=torch.float16,
+                               device=cache.device)
+
+    def run(self, q: torch.Tensor, stream=None) -> torch.Tensor:
+        L.pa_paged_attention_prefill(self.out, q, self.cache.kv, self.table, self.table_len,
+                                     self.q_start, self.chunk_len, self.n_q, self.scale,
+                                     self.workspace, self.ws_bytes,
+                                     stream or torch.cuda.current_stream(self.cache.device))
+        return self.out
+
+
+def run_program(cache: PagedKVCache, setup, k_rows: torch.Tensor, v_rows: torch.Tensor):
+    """Apply a list of ("add", id) / ("fork", parent, child) /
+    ("append", ids, n_new) operations, taking appended rows in order."""
+    cursor = 0
+    for op in setup:
+        if op[0] == "add":
+            cache.add(int(op[1]))
+        elif op[0] == "fork":
+            cache.fork(int(op[1]), int(op[2]))
+        elif op[0] == "append":
+            n = int(sum(op[2]))
+            cache.append(op[1], op[2], k_rows[cursor:cursor + n], v_rows[cursor:cursor + n])
+            cursor += n
+        else:
+            raise ValueError(op[0])
+    return cursor
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)

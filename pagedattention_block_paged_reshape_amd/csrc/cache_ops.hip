@@ -1,0 +1,121 @@
+// Cache writes on gfx950: storing new tokens' K/V into their paged slots, and
+// the copy-on-write block copies.
+//
+// Storing a token follows the append_token store into cache[block, slot] of
+// the PagedAttentionManager listing (youngju.dev "vLLM inference
+// optimization", PagedAttention section); the copy is the copy-on-write of a
+// shared block that diverges (media.tcdigital.jp, "memory sharing for
+// parallel sampling").  Both are bit copies.
+//
+// Pool layout (see include/pa.h): K [N][H][16][D], V [N][H][D][16].
+#include "pa_device.h"
+
+namespace pa {
+
+// One thread per (token, kv head, 8-dim chunk): a 16-byte K row chunk goes to
+// the slot's row; the matching V chunk is scattered into 8 slot columns.
+template <int D>
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+    const f16* __restrict__ k, const f16* __restrict__ v, const int32_t* __restrict__ slots,
+    int32_t num_tokens, int32_t n_kv, int32_t num_blocks, f16* __restrict__ kp,
+    f16* __restrict__ vp) {
+  constexpr int kChunks = D / 8;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t total = static_cast<int64_t>(num_tokens) * n_kv * kChunks;
+  if (idx >= total) return;
+  const int chunk = static_cast<int>(idx % kChunks);
+  const int64_t th = idx / kChunks;
+  const int h = static_cast<int>(th % n_kv);
+  const int64_t t = th / n_kv;
+  const int32_t s = slots[t];
+  if (s < 0 || s >= num_blocks * kBlock) return;
+  const int64_t blk = s / kBlock;
+  const int off = s % kBlock;
+  const int64_t src = (t * n_kv + h) * D + chunk * 8;
+  const f16x8 kv = *reinterpret_cast<const f16x8*>(k + src);
+  const f16x8 vv = *reinterpret_cast<const f16x8*>(v + src);
+  const int64_t tile = blk * n_kv + h;
+  *reinterpret_cast<f16x8*>(kp + (tile * kBlock + off) * D + chunk * 8) = kv;
+  f16* vcol = vp + (tile * D + chunk * 8) * kBlock + off;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) vcol[e * kBlock] = vv[e];
+}
+
+// One workgroup per (copy, kv head): slots [0, n) of the K tile are a
+// contiguous prefix; in the V tile each dimension's first n slots are copied.
+template <int D>
+__global__ __launch_bounds__(256) void copy_blocks_kernel(const pa_copy* __restrict__ copies,
+                                                          int32_t n_kv, int32_t num_blocks,
+                                                          f16* __restrict__ kp,
+                                                          f16* __restrict__ vp) {
+  const pa_copy c = copies[blockIdx.x];
+  const int h = blockIdx.y;
+  if (c.src < 0 || c.src >= num_blocks || c.dst < 0 || c.dst >= num_blocks) return;
+  if (c.n_slots <= 0 || c.n_slots > kBlock || c.src == c.dst) return;
+  const int n = c.n_slots;
+  const int64_t st = static_cast<int64_t>(c.src) * n_kv + h;
+  const int64_t dt = static_cast<int64_t>(c.dst) * n_kv + h;
+  const f16x8* ks = reinterpret_cast<const f16x8*>(kp + st * kBlock * D);
+  f16x8* kd = reinterpret_cast<f16x8*>(kp + dt * kBlock * D);
+  for (int i = threadIdx.x; i < n * D / 8; i += blockDim.x) kd[i] = ks[i];
+  const f16* vs = vp + st * D * kBlock;
+  f16* vd = vp + dt * D * kBlock;
+  for (int i = threadIdx.x; i < D * n; i += blockDim.x) {
+    const int dim = i / n, s = i % n;
+    vd[dim * kBlock + s] = vs[dim * kBlock + s];
+  }
+}
+
+static bool valid_view(const pa_kv_view& kv) {
+  return kv.k_pool != nullptr && kv.v_pool != nullptr && kv.num_blocks > 0 &&
+         static_cast<int64_t>(kv.num_blocks) * kBlock < (1LL << 31) &&
+         kv.block_size == kBlock && kv.num_kv_heads > 0 &&
+         (kv.head_dim == 64 || kv.head_dim == 128) && aligned16(kv.k_pool) &&
+         aligned16(kv.v_pool);
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" pa_status pa_reshape_and_cache(const pa_half* k, const pa_half* v,
+                                          const int32_t* slot_mapping, int32_t num_tokens,
+                                          pa_kv_view kv, void* stream) {
+  if (!valid_view(kv) || num_tokens < 0) return PA_ERR_INVALID;
+  if (num_tokens == 0) return PA_OK;
+  if (k == nullptr || v == nullptr || slot_mapping == nullptr || !aligned16(k) || !aligned16(v))
+    return PA_ERR_INVALID;
+  const int64_t total = static_cast<int64_t>(num_tokens) * kv.num_kv_heads * (kv.head_dim / 8);
+  const int64_t blocks = (total + 255) / 256;
+  if (blocks > INT32_MAX) return PA_ERR_INVALID;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const f16* kk = reinterpret_cast<const f16*>(k);
+  const f16* vv = reinterpret_cast<const f16*>(v);
+  f16* kp = reinterpret_cast<f16*>(kv.k_pool);
+  f16* vp = reinterpret_cast<f16*>(kv.v_pool);
+  if (kv.head_dim == 128)
+    reshape_and_cache_kernel<128><<<dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s>>>(
+        kk, vv, slot_mapping, num_tokens, kv.num_kv_heads, kv.num_blocks, kp, vp);
+  else
+    reshape_and_cache_kernel<64><<<dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s>>>(
+        kk, vv, slot_mapping, num_tokens, kv.num_kv_heads, kv.num_blocks, kp, vp);
+  return launch_status();
+}
+
+extern "C" pa_status pa_copy_blocks(const pa_copy* copies, int32_t n, pa_kv_view kv,
+                                    void* stream) {
+  if (!valid_view(kv) || n < 0) return PA_ERR_INVALID;
+  if (n == 0) return PA_OK;
+  if (copies == nullptr || kv.num_kv_heads > 65535) return PA_ERR_INVALID;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  f16* kp = reinterpret_cast<f16*>(kv.k_pool);
+  f16* vp = reinterpret_cast<f16*>(kv.v_pool);
+  const dim3 grid(static_cast<uint32_t>(n), static_cast<uint32_t>(kv.num_kv_heads));
+  if (kv.head_dim == 128)
+    copy_blocks_kernel<128><<<grid, dim3(256), 0, s>>>(copies, kv.num_kv_heads, kv.num_blocks,
+                                                       kp, vp);
+  else
+    copy_blocks_kernel<64><<<grid, dim3(256), 0, s>>>(copies, kv.num_kv_heads, kv.num_blocks,
+                                                      kp, vp);
+  return launch_status();
+}

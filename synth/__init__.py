@@ -9,4 +9,5 @@ from .workloads import (  # noqa: F401
     CONFIG_NAMES,
     make_workload,
     make_tiny_workload,
+    make_mixed_workload,
 )

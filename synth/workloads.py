@@ -278,3 +278,39 @@ def make_workload(cfg) -> Workload:
     if key == "5":
         return _cfg5()
     raise KeyError(cfg)
+
+
+def make_mixed_workload(decode_lengths: Sequence[int], q_start: int, chunk_len: int,
+                        n_q: int = 32, n_kv: int = 8, d: int = 128, seed: int = 11,
+                        dist: str = "normal", num_blocks: Optional[int] = None,
+                        name: str = "mixed") -> Workload:
+    """Decode requests of the given attended lengths plus one prompt whose
+    chunk [q_start, q_start + chunk_len) is prefilled in the same step (the
+    shape of configuration 5 at any size; tests)."""
+    rng = np.random.default_rng(seed)
+    lengths = np.asarray(list(decode_lengths), dtype=np.int64)
+    B = len(lengths)
+    blocks = int(sum(_ceil_div(int(x), BLOCK_SIZE) for x in lengths)) + \
+        _ceil_div(q_start + chunk_len, BLOCK_SIZE)
+    nb = _pool_size(blocks, extra=2) if num_blocks is None else num_blocks
+    free_order = rng.permutation(nb).astype(np.int32)
+    q = _draw(rng, (B, n_q, d), dist)
+    t_setup = int((lengths - 1).sum()) + q_start
+    setup_k = _draw(rng, (t_setup, n_kv, d), dist)
+    setup_v = _draw(rng, (t_setup, n_kv, d), dist)
+    step_k = _draw(rng, (B + chunk_len, n_kv, d), dist)
+    step_v = _draw(rng, (B + chunk_len, n_kv, d), dist)
+    q_chunk = _draw(rng, (chunk_len, n_q, d), dist)
+    dec = np.arange(B, dtype=np.int64)
+    pid = B
+    setup: List[Op] = [("add", int(i)) for i in range(B + 1)]
+    setup.append(("append", dec.tolist() + [pid], (lengths - 1).astype(int).tolist() + [q_start]))
+    return Workload(
+        name=name, n_q=n_q, n_kv=n_kv, d=d, scale=1.0 / math.sqrt(d), num_blocks=nb,
+        free_order=free_order, setup=setup, setup_k=setup_k, setup_v=setup_v,
+        step_ids=np.concatenate([dec, [pid]]).astype(np.int64),
+        step_n_new=np.array([1] * B + [chunk_len], dtype=np.int32),
+        step_k=step_k, step_v=step_v, decode_ids=dec, q=q,
+        prefill=PrefillChunk(seq_id=pid, q_start=q_start, chunk_len=chunk_len, q=q_chunk),
+        seed=seed, notes={"lengths": lengths.tolist(), "prompt": q_start + chunk_len},
+    )

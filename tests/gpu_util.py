@@ -1,0 +1,100 @@
+"""Helpers for the GPU parity tests: run a synthetic workload through the C
+ABI on cuda:0, run the same workload through the oracle, compare."""
+import sys
+
+import numpy as np
+import torch
+
+from pagedattention_block_paged_reshape_amd.cache import (DecodePlan, PagedKVCache, PrefillPlan,
+                                                          run_program)
+from oracle import decode_reference, prefill_reference, run_setup, run_step
+
+# Every pool byte starts as 0x7E: each fp16 reads 0x7E7E, a NaN, so a kernel
+# that reads a slot nobody wrote (or fails to mask one) produces NaN.
+FILL = 0x7E
+RTOL, ATOL = 1e-2, 2e-3     # elementwise |gpu - oracle| <= ATOL + RTOL * |oracle|
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_run(w, partition=512, fill=FILL, device="cuda:0", decode=True, prefill=True):
+    log(f"[gpu_run] {w.name}: blocks={w.num_blocks} B={w.batch} n_q={w.n_q} n_kv={w.n_kv} "
+        f"d={w.d} partition={partition} prefill={w.prefill is not None}")
+    cache = PagedKVCache(w.num_blocks, w.n_kv, w.d, w.free_order, device, fill_byte=fill)
+    dk = torch.from_numpy(w.setup_k).to(device)
+    dv = torch.from_numpy(w.setup_v).to(device)
+    run_program(cache, w.setup, dk, dv)
+    del dk, dv
+    sk = torch.from_numpy(w.step_k).to(device)
+    sv = torch.from_numpy(w.step_v).to(device)
+    slots, copies = cache.append(w.step_ids, w.step_n_new, sk, sv)
+    res = {"cache": cache, "step_slots": slots, "step_copies": copies}
+    if decode and w.batch:
+        plan = DecodePlan(cache, w.decode_ids, w.n_q, w.scale, partition)
+        q = torch.from_numpy(w.q).to(device)
+        res["decode"] = plan.run(q).clone()
+        res["plan"], res["q"] = plan, q
+    if prefill and w.prefill is not None:
+        pf = w.prefill
+        pp = PrefillPlan(cache, pf.seq_id, pf.q_start, pf.chunk_len, w.n_q, w.scale)
+        qc = torch.from_numpy(pf.q).to(device)
+        res["prefill"] = pp.run(qc).clone()
+        res["pplan"], res["qc"] = pp, qc
+    torch.cuda.synchronize()
+    return res
+
+
+def oracle_run(w):
+    st = run_setup(w)
+    run_step(w, st)
+    return st
+
+
+def assert_close(got, ref, what):
+    """``got`` fp16 (torch, any device), ``ref`` fp64 numpy of the same shape."""
+    g = got.float().cpu().numpy().astype(np.float64)
+    assert g.shape == ref.shape, (g.shape, ref.shape)
+    ok = np.isclose(g, ref, rtol=RTOL, atol=ATOL)
+    if not ok.all():
+        bad = np.argwhere(~ok)
+        i = tuple(bad[0])
+        err = np.abs(g - ref)
+        raise AssertionError(f"{what}: {len(bad)} of {ok.size} elements outside "
+                             f"atol={ATOL} rtol={RTOL}; first {i}: gpu={g[i]!r} oracle={ref[i]!r}; "
+                             f"max abs err {err.max():.3e}")
+    return float(np.abs(g - ref).max())
+
+
+def valid_slots(st):
+    """Per physical block, how many leading slots hold live tokens."""
+    n = np.zeros(st.alloc.num_blocks, dtype=np.int64)
+    for s, table in st.alloc.tables.items():
+        ln = st.alloc.lens[s]
+        for i, b in enumerate(table):
+            n[b] = max(n[b], min(16, ln - 16 * i))
+    return n
+
+
+def assert_pools_bit_exact(cache, st, fill=FILL):
+    """Valid slots of live blocks equal the oracle pool bit for bit; blocks
+    no request holds still carry the fill pattern."""
+    kd = cache.k_pool.cpu().numpy().view(np.uint16)
+    vd = cache.v_pool.cpu().numpy().view(np.uint16)
+    ko = st.pool.k.view(np.uint16)
+    vo = st.pool.v.view(np.uint16)
+    nvalid = valid_slots(st)
+    mask = np.arange(16)[None, :] < nvalid[:, None]                    # [N][16]
+    k_dev = kd.transpose(0, 2, 1, 3)[mask]
+    k_ref = ko.transpose(0, 2, 1, 3)[mask]
+    assert np.array_equal(k_dev, k_ref), "K pool differs from the oracle"
+    v_dev = vd.transpose(0, 3, 1, 2)[mask]
+    v_ref = vo.transpose(0, 3, 1, 2)[mask]
+    assert np.array_equal(v_dev, v_ref), "V pool differs from the oracle"
+    pattern = np.uint16(fill | (fill << 8))
+    untouched = nvalid == 0
+    assert (kd[untouched] == pattern).all(), "a block no request holds was written (K)"
+    assert (vd[untouched] == pattern).all(), "a block no request holds was written (V)"
+    return int(mask.sum())

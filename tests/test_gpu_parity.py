@@ -1,0 +1,225 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Cache writes and tables are compared bit for bit; attention outputs element by
+element within |gpu - oracle| <= 2e-3 + 1e-2 * |oracle| (fp16 inputs, fp32
+accumulation, fp16 output).  Every pool byte starts as a NaN pattern, so an
+unmasked read of an unwritten slot fails these tests."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import (ATOL, FILL, RTOL, assert_close, assert_pools_bit_exact, gpu_run, log,
+                      oracle_run)
+from oracle import decode_attention_one, decode_reference, prefill_reference
+from synth import make_mixed_workload, make_tiny_workload, make_workload
+from synth.workloads import Workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------ the 5 configs
+
+@pytest.mark.parametrize("cfg", ["1", "2", "4", "4b"])
+def test_config_cache_and_decode(cfg):
+    w = make_workload(cfg)
+    st = oracle_run(w)
+    res = gpu_run(w)
+    assert res["step_slots"].tolist() == st.step_slots.tolist()
+    assert [tuple(c) for c in res["step_copies"].tolist()] == st.step_copies
+    n = assert_pools_bit_exact(res["cache"], st)
+    err = assert_close(res["decode"], decode_reference(w, st), f"config {cfg} decode")
+    log(f"config {cfg}: {n} live slots bit-exact, decode max err {err:.2e}")
+    if cfg == "4":
+        assert len(st.step_copies) == 0
+    if cfg == "4b":
+        assert len(st.step_copies) == w.batch - 1
+
+
+def test_config3_full_size_decode():
+    """The decode workload the benchmark times (split-K 512 + reduce), every
+    output element against the oracle."""
+    w = make_workload(3)
+    st = oracle_run(w)
+    res = gpu_run(w, partition=512)
+    n = assert_pools_bit_exact(res["cache"], st)
+    err = assert_close(res["decode"], decode_reference(w, st), "config 3 decode")
+    log(f"config 3: {n} live slots bit-exact, decode max err {err:.2e}")
+
+
+def test_config5_mixed_step():
+    """8 decode requests at 32,768 tokens (64 partitions each) and the
+    512-token prefill chunk at offset 49,488 over one pool; decode checked in
+    full, prefill on sampled rows and all heads."""
+    w = make_workload(5)
+    st = oracle_run(w)
+    res = gpu_run(w, partition=512)
+    assert_pools_bit_exact(res["cache"], st)
+    err = assert_close(res["decode"], decode_reference(w, st), "config 5 decode")
+    rows = [0, 1, 15, 16, 127, 128, 255, 300, 447, 510, 511]
+    ref = prefill_reference(w, st, rows=rows)
+    errp = assert_close(res["prefill"][rows], ref, "config 5 prefill (sampled rows)")
+    log(f"config 5: decode max err {err:.2e}, prefill max err {errp:.2e}")
+
+
+# ---------------------------------------------------------- decode edges
+
+RAGGED = [1, 2, 15, 16, 17, 31, 32, 33, 127, 511, 512, 513, 1000, 1537, 2049]
+
+
+@pytest.mark.parametrize("partition", [16, 32, 48, 256, 512, 4096])
+def test_decode_partition_sizes(partition):
+    w = make_tiny_workload(RAGGED, n_q=32, n_kv=8, d=128, seed=21, dist="normal")
+    st = oracle_run(w)
+    res = gpu_run(w, partition=partition)
+    assert_close(res["decode"], decode_reference(w, st), f"partition {partition}")
+
+
+@pytest.mark.parametrize("n_q,n_kv,d", [(16, 1, 128), (8, 8, 64), (4, 2, 64), (64, 8, 128),
+                                        (12, 4, 128), (2, 2, 128), (16, 4, 64)])
+def test_decode_head_shapes(n_q, n_kv, d):
+    w = make_tiny_workload([1, 17, 64, 300, 700], n_q=n_q, n_kv=n_kv, d=d, seed=n_q * 7 + d,
+                           dist="normal")
+    st = oracle_run(w)
+    res = gpu_run(w, partition=256)
+    assert_close(res["decode"], decode_reference(w, st), f"heads {n_q}/{n_kv} d{d}")
+
+
+def test_decode_single_token_returns_its_value_exactly():
+    w = make_tiny_workload([1, 1, 1], n_q=16, n_kv=2, d=128, seed=5, dist="normal")
+    st = oracle_run(w)
+    res = gpu_run(w)
+    out = res["decode"].cpu().numpy().view(np.uint16)
+    for i in range(3):
+        for h in range(16):
+            assert np.array_equal(out[i, h], w.step_v[i, h // 8].view(np.uint16))
+
+
+def test_decode_deterministic_and_placement_invariant():
+    w = make_tiny_workload(RAGGED, n_q=32, n_kv=8, d=128, seed=33, dist="normal")
+    a = gpu_run(w)
+    again = a["plan"].run(a["q"]).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a["decode"].view(torch.int16), again.view(torch.int16))
+    for s in range(2):
+        w.free_order = np.random.default_rng(500 + s).permutation(w.num_blocks).astype(np.int32)
+        b = gpu_run(w)
+        assert torch.equal(a["decode"].view(torch.int16), b["decode"].view(torch.int16))
+
+
+def test_shared_prefix_equals_private_copies_bitwise():
+    shared = make_workload("4b")
+    B = 16
+    shared.decode_ids = shared.decode_ids[:B]
+    shared.step_ids = shared.step_ids[:B]
+    shared.step_n_new = shared.step_n_new[:B]
+    shared.step_k, shared.step_v, shared.q = shared.step_k[:B], shared.step_v[:B], shared.q[:B]
+    shared.setup = [op for op in shared.setup if op[0] != "fork" or op[2] < B]
+    P = shared.notes["prefix"]
+    private = Workload(
+        name="private-copies", n_q=shared.n_q, n_kv=shared.n_kv, d=shared.d,
+        scale=shared.scale, num_blocks=B * 70,
+        free_order=np.random.default_rng(1).permutation(B * 70).astype(np.int32),
+        setup=[("add", i) for i in range(B)] + [("append", list(range(B)), [P] * B)],
+        setup_k=np.concatenate([shared.setup_k[:P]] * B),
+        setup_v=np.concatenate([shared.setup_v[:P]] * B),
+        step_ids=shared.step_ids, step_n_new=shared.step_n_new, step_k=shared.step_k,
+        step_v=shared.step_v, decode_ids=shared.decode_ids, q=shared.q)
+    a = gpu_run(shared)
+    b = gpu_run(private)
+    assert len(a["step_copies"]) == B - 1 and len(b["step_copies"]) == 0
+    assert torch.equal(a["decode"].view(torch.int16), b["decode"].view(torch.int16))
+    st = oracle_run(shared)
+    assert_pools_bit_exact(a["cache"], st)
+    assert_close(a["decode"], decode_reference(shared, st), "shared prefix")
+
+
+def test_decode_bad_table_entry_and_empty_request():
+    import pagedattention_block_paged_reshape_amd as pa
+    w = make_tiny_workload([40, 40, 40], n_q=8, n_kv=2, d=128, seed=8, dist="normal")
+    st = oracle_run(w)
+    res = gpu_run(w)
+    plan = res["plan"]
+    good = res["decode"].clone()
+    plan.tables[1, 1] = w.num_blocks + 7          # out of range: request 1 must read NaN
+    plan.lens[2] = 0                              # empty request: zeros
+    out = plan.run(res["q"]).clone()
+    torch.cuda.synchronize()
+    assert torch.isnan(out[1].float()).all()
+    assert (out[2].float() == 0).all()
+    assert torch.equal(out[0].view(torch.int16), good[0].view(torch.int16))
+    assert_close(out[0:1], decode_reference(w, st)[0:1], "request next to a bad one")
+    # host-side validation rejects bad geometry before any launch
+    with pytest.raises(pa.PaError):
+        pa.pa_paged_attention_decode(out, res["q"], plan.cache.kv, plan.tables, plan.max_blocks,
+                                     plan.lens, 3, 7, 0.1, 512, plan.max_len, plan.workspace,
+                                     plan.ws_bytes)
+    with pytest.raises(pa.PaError):
+        pa.pa_paged_attention_decode(out, res["q"], plan.cache.kv, plan.tables, plan.max_blocks,
+                                     plan.lens, 3, 8, 0.1, 24, plan.max_len, plan.workspace,
+                                     plan.ws_bytes)
+
+
+def test_reshape_and_cache_skips_negative_and_out_of_range_slots():
+    import pagedattention_block_paged_reshape_amd as pa
+    from pagedattention_block_paged_reshape_amd.cache import PagedKVCache
+    cache = PagedKVCache(4, 2, 64, device="cuda:0", fill_byte=FILL)
+    k = torch.randn(3, 2, 64, device="cuda:0").half()
+    v = torch.randn(3, 2, 64, device="cuda:0").half()
+    slots = torch.tensor([5, -1, 4 * 16 + 3], dtype=torch.int32, device="cuda:0")
+    pa.pa_reshape_and_cache(k, v, slots, 3, cache.kv)
+    torch.cuda.synchronize()
+    kp = cache.k_pool.cpu()
+    vp = cache.v_pool.cpu()
+    assert torch.equal(kp[0, :, 5, :], k[0].cpu())
+    assert torch.equal(vp[0, :, :, 5], v[0].cpu())
+    written = torch.zeros(4, 16, dtype=torch.bool)
+    written[0, 5] = True
+    pattern = FILL | (FILL << 8)
+    kk = kp.view(torch.int16).permute(0, 2, 1, 3)
+    assert (kk[~written] == torch.tensor(pattern).to(torch.int16)).all()
+
+
+# ---------------------------------------------------------------- prefill
+
+@pytest.mark.parametrize("decode_lengths,q_start,chunk,n_q,n_kv,d", [
+    ([], 0, 48, 4, 2, 128),            # whole causal prompt from position 0
+    ([], 0, 200, 32, 8, 128),          # several query tiles, ragged tail
+    ([17], 37, 100, 32, 8, 128),       # unaligned start, ragged
+    ([5, 300], 1000, 300, 32, 8, 128),
+    ([], 640, 129, 16, 16, 128),       # G = 1
+    ([], 333, 77, 64, 8, 128),         # G = 8
+    ([], 90, 50, 16, 1, 128),          # G = 16
+    ([], 250, 130, 8, 2, 64),          # head_dim 64
+    ([], 4093, 512, 32, 8, 128),       # several key splits
+])
+def test_prefill_chunk_parity(decode_lengths, q_start, chunk, n_q, n_kv, d):
+    w = make_mixed_workload(decode_lengths, q_start, chunk, n_q=n_q, n_kv=n_kv, d=d,
+                            seed=q_start + chunk)
+    st = oracle_run(w)
+    res = gpu_run(w)
+    err = assert_close(res["prefill"], prefill_reference(w, st), "prefill chunk")
+    if w.batch:
+        assert_close(res["decode"], decode_reference(w, st), "decode in the mixed step")
+    log(f"prefill q_start={q_start} chunk={chunk} G={n_q // n_kv} d={d}: max err {err:.2e}")
+
+
+def test_prefill_last_row_matches_decode_kernel():
+    """The chunk's last row sees exactly the prompt's keys, as a decode of
+    the same request would."""
+    w = make_mixed_workload([], 700, 64, n_q=32, n_kv=8, d=128, seed=2)
+    res = gpu_run(w)
+    from pagedattention_block_paged_reshape_amd.cache import DecodePlan
+    plan = DecodePlan(res["cache"], [w.prefill.seq_id], w.n_q, w.scale, 512)
+    dec = plan.run(res["qc"][-1:].contiguous()).clone()
+    torch.cuda.synchronize()
+    a = res["prefill"][-1].float().cpu().numpy()
+    b = dec[0].float().cpu().numpy()
+    assert np.allclose(a, b, rtol=RTOL, atol=ATOL)
