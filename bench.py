@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark: paged decode attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
+
+A step is one pass of the whole decode hot path for the batch: reserve one
+slot per request on the host block manager, store the step's new K/V into the
+paged pool, refresh the device block tables, and run paged decode attention
+(split-K partition kernel + reduce).  The default workload is the
+Llama-3-70B-shaped decode layer: 256 requests, 64 query / 8 KV heads,
+head_dim 128, 16-token blocks, lengths lognormal(median 1000) clipped to
+[16, 4096], split-K partitions of 512 tokens, block tables scattered over the
+pool.  Inputs are seeded synthetic fp16 N(0,1) data, resident in HBM before
+timing starts.
+
+Prints one JSON line.  ``value`` is decode tokens/s per layer (requests
+advanced per second).  ``roofline`` reports the decode launch (partition +
+reduce kernels, timed with HIP events on the stream they run on) against the
+8 TB/s HBM peak using algorithmic bytes: every K and V byte of every attended
+token once per KV head, plus Q, O, block tables and lengths.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["pagedattention_block_paged_reshape_amd/csrc/decode.hip",
+                  "pagedattention_block_paged_reshape_amd/csrc/pa_device.h"]
+TRAFFIC_FILE = os.path.join(PROFILES, "decode_llama3-70b_traffic.md")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def algorithmic_decode_bytes(lens, n_q, n_kv, d) -> int:
+    lens = np.asarray(lens, dtype=np.int64)
+    kv = int(lens.sum()) * 2 * n_kv * d * 2              # K and V once per KV head
+    qo = 2 * len(lens) * n_q * d * 2                     # Q in, O out (fp16)
+    tables = 4 * int(((lens + 15) // 16).sum())          # block ids read
+    return kv + qo + tables + 4 * len(lens)              # + lengths
+
+
+def cpu_baseline(w, budget_s: float, steps_done: int):
+    """The fp64 oracle (as written, untuned) doing the same decode step:
+    append one token per request, store its K/V, attend over every request."""
+    from oracle import decode_reference, run_setup
+    log("[bench] cpu_baseline: building the oracle's pool model (not timed)")
+    st = run_setup(w)
+    ids, ones = w.step_ids.tolist(), [1] * w.batch
+    for _ in range(steps_done):                  # reach the GPU's final lengths
+        st.alloc.append(ids, ones)
+    t0, c0 = time.perf_counter(), time.process_time()
+    reps = 0
+    while True:
+        slots, copies = st.alloc.append(ids, ones)
+        st.pool.copy(copies)
+        st.pool.write(w.step_k, w.step_v, slots)
+        decode_reference(w, st)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    cpu = time.process_time() - c0
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        blas = None
+    return {
+        "value": reps * w.batch / el,
+        "unit": "decode tokens/s per layer",
+        "cores": max(1, int(round(cpu / el))),
+        "kind": "oracle",
+        "sample": f"{reps} full decode steps of the same workload ({w.batch} requests each: "
+                  f"append + store + fp64 attention) in {el:.1f} s wall; BLAS pool "
+                  f"{blas} threads, cpu/wall = {cpu / el:.2f}",
+    }
+
+
+def copy_calibration(nbytes: int, reps: int):
+    """A plain device copy of known size (for scaling HBM byte counters)."""
+    import torch
+    src = torch.empty(nbytes // 2, dtype=torch.float16, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="3", help="decode workload (2, 3, 4 or 5)")
+    ap.add_argument("--partition", type=int, default=512)
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush-mb", type=int, default=0,
+                    help="write this many MiB between steps to evict L2/MALL")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the kernels shard by request or KV head with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calibration_mb:
+        copy_calibration(args.copy_calibration_mb << 20, 5)
+        return
+
+    from synth import make_workload
+    from pagedattention_block_paged_reshape_amd.cache import PagedKVCache, run_program
+    from pagedattention_block_paged_reshape_amd.stepper import DecodeStepper
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] generating workload {args.config}")
+    w = make_workload(args.config)
+    total_steps = args.warmup + args.steps
+    cache = PagedKVCache(w.num_blocks, w.n_kv, w.d, w.free_order, dev)
+    log("[bench] uploading and storing the cached K/V through reshape_and_cache")
+    dk = torch.from_numpy(w.setup_k).to(dev)
+    dv = torch.from_numpy(w.setup_v).to(dev)
+    run_program(cache, w.setup, dk, dv)
+    del dk, dv
+    step_k = torch.from_numpy(w.step_k[:w.batch]).to(dev)
+    step_v = torch.from_numpy(w.step_v[:w.batch]).to(dev)
+    q = torch.from_numpy(w.q).to(dev)
+    lens0 = np.array([cache.seq_len(int(s)) for s in w.decode_ids])
+    cap = int(lens0.max()) + total_steps
+    stepper = DecodeStepper(cache, w.decode_ids, w.n_q, w.scale, cap, args.partition)
+    stream = torch.cuda.current_stream(dev)
+    flush = None
+    if args.flush_mb:
+        flush = torch.empty(args.flush_mb << 20, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        stepper.step(q, step_k, step_v, stream)
+    torch.cuda.synchronize()
+
+    ev = [{"cache": (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)),
+           "decode": (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))}
+          for _ in range(args.steps)]
+    bytes_per_step = []
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+        stepper.step(q, step_k, step_v, stream, events=ev[i])
+        bytes_per_step.append(algorithmic_decode_bytes(stepper.last_lens, w.n_q, w.n_kv, w.d))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    dec_ms = np.array([e["decode"][0].elapsed_time(e["decode"][1]) for e in ev])
+    cache_ms = np.array([e["cache"][0].elapsed_time(e["cache"][1]) for e in ev])
+    dec_bytes = float(np.mean(bytes_per_step))
+    achieved = dec_bytes / (dec_ms.mean() * 1e-3) / 1e9
+    tokens_per_s = w.batch * args.steps / wall
+    log(f"[bench] wall {wall * 1e3:.2f} ms for {args.steps} steps; decode launch mean "
+        f"{dec_ms.mean() * 1e3:.1f} us (p50 {np.median(dec_ms) * 1e3:.1f}, p99 "
+        f"{np.percentile(dec_ms, 99) * 1e3:.1f}); reshape_and_cache {cache_ms.mean() * 1e3:.1f} us; "
+        f"{achieved:.0f} GB/s algorithmic")
+
+    result = {
+        "metric": "paged decode attention achieved HBM GB/s (% of peak); decode tokens/s per layer",
+        "value": round(tokens_per_s, 1),
+        "unit": "decode tokens/s per layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"config {args.config} ({w.name}): B={w.batch}, {w.n_q}/{w.n_kv} heads, "
+                        f"head_dim {w.d}, block 16, pool {w.num_blocks} blocks scattered, "
+                        f"split-K partition {args.partition} + reduce",
+            "batch": w.batch,
+            "mean_context": round(float(np.mean(stepper.last_lens)), 1),
+            "partition": args.partition,
+            "flush_mb_between_steps": args.flush_mb,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": recorded_traffic(),
+            "kernel": "pa_paged_attention_decode (decode_partition_kernel + decode_reduce_kernel)",
+            "algorithmic_bytes_per_launch": int(dec_bytes),
+            "launch_us_mean": round(float(dec_ms.mean()) * 1e3, 2),
+            "launch_us_p50": round(float(np.median(dec_ms)) * 1e3, 2),
+            "launch_us_p99": round(float(np.percentile(dec_ms, 99)) * 1e3, 2),
+            "reshape_and_cache_us_mean": round(float(cache_ms.mean()) * 1e3, 2),
+            "kernel_source_sha256": kernel_source_hash(),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        del cache, stepper
+        torch.cuda.empty_cache()
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, total_steps)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

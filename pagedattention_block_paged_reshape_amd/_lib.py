@@ -181,12 +181,18 @@ def pa_can_append(pool: int, seq_ids, n_new) -> int:
     return out.value
 
 
-def pa_append_slots(pool: int, seq_ids, n_new):
-    """Returns (slot_mapping int32[T], copies int32[n][3] as (src, dst, n_slots))."""
+def pa_append_slots(pool: int, seq_ids, n_new, slots_out: Optional[np.ndarray] = None):
+    """Returns (slot_mapping int32[T], copies int32[n][3] as (src, dst, n_slots)).
+    ``slots_out`` (contiguous int32, >= T entries) receives the slots in place."""
     ids = _host(seq_ids, np.int64)
     nn = _host(n_new, np.int32)
     T = int(nn.sum()) if nn.size else 0
-    slots = np.empty(max(T, 1), dtype=np.int32)
+    if slots_out is not None:
+        if slots_out.dtype != np.int32 or not slots_out.flags.c_contiguous or slots_out.size < T:
+            raise ValueError("slots_out must be contiguous int32 with room for every slot")
+        slots = slots_out
+    else:
+        slots = np.empty(max(T, 1), dtype=np.int32)
     cap = len(ids)
     copies = (pa_copy * max(cap, 1))()
     n_copies = _I32()
@@ -197,10 +203,18 @@ def pa_append_slots(pool: int, seq_ids, n_new):
     return slots[:T], cp
 
 
-def pa_block_tables(pool: int, seq_ids, max_blocks: int):
+def pa_block_tables(pool: int, seq_ids, max_blocks: int, tables: Optional[np.ndarray] = None,
+                    lens: Optional[np.ndarray] = None):
+    """Host tables [n][max_blocks] and lengths [n]; ``tables``/``lens`` may be
+    caller buffers (contiguous int32) written in place."""
     ids = _host(seq_ids, np.int64)
-    tables = np.empty((len(ids), max(int(max_blocks), 0)), dtype=np.int32)
-    lens = np.empty(len(ids), dtype=np.int32)
+    if tables is None:
+        tables = np.empty((len(ids), max(int(max_blocks), 0)), dtype=np.int32)
+    if lens is None:
+        lens = np.empty(len(ids), dtype=np.int32)
+    for a, need in ((tables, len(ids) * max(int(max_blocks), 0)), (lens, len(ids))):
+        if a.dtype != np.int32 or not a.flags.c_contiguous or a.size < need:
+            raise ValueError("tables/lens must be contiguous int32 buffers of the right size")
     _check(LIB.pa_block_tables(pool, len(ids), _ptr(ids), int(max_blocks), _ptr(tables),
                                _ptr(lens)), "pa_block_tables")
     return tables, lens

@@ -1,0 +1,87 @@
+"""One decode step for a fixed batch of running requests, pipelined.
+
+Each step reserves one slot per request (``pa_append_slots``, host), stores
+the step's new K/V (``pa_reshape_and_cache``), refreshes the device block
+tables (``pa_block_tables`` + one async host-to-device copy) and attends
+(``pa_paged_attention_decode``), all enqueued on one stream.  Host staging
+buffers are pinned and used round-robin, so the host prepares step i+1 while
+the GPU still runs step i (the scheduler loop of ta-paperlens: blocks are
+reserved for every running request before the step's forward pass).
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib as L
+from .cache import DEFAULT_PARTITION, PagedKVCache
+
+
+class DecodeStepper:
+    def __init__(self, cache: PagedKVCache, seq_ids, num_q_heads: int, scale: float,
+                 max_len_cap: int, partition: int = DEFAULT_PARTITION, depth: int = 2):
+        self.cache = cache
+        self.ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+        self.B = len(self.ids)
+        self.ones = np.ones(self.B, dtype=np.int32)
+        self.n_q, self.scale, self.partition = int(num_q_heads), float(scale), int(partition)
+        self.max_len_cap = int(max_len_cap)
+        self.max_blocks = -(-self.max_len_cap // L.BLOCK_SIZE)
+        dev = cache.device
+        self.depth = depth
+        self.h_slots = [torch.empty(self.B, dtype=torch.int32, pin_memory=True) for _ in range(depth)]
+        self.h_tab = [torch.empty((self.B, self.max_blocks), dtype=torch.int32, pin_memory=True)
+                      for _ in range(depth)]
+        self.h_len = [torch.empty(self.B, dtype=torch.int32, pin_memory=True) for _ in range(depth)]
+        self.d_slots = [torch.empty(self.B, dtype=torch.int32, device=dev) for _ in range(depth)]
+        self.d_tab = torch.empty((self.B, self.max_blocks), dtype=torch.int32, device=dev)
+        self.d_len = torch.empty(self.B, dtype=torch.int32, device=dev)
+        self.done = [None] * depth
+        self.ws_bytes = L.pa_decode_workspace_bytes(self.B, self.n_q, cache.d, self.max_len_cap,
+                                                    self.partition)
+        self.workspace = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev)
+        self.out = torch.empty((self.B, self.n_q, cache.d), dtype=torch.float16, device=dev)
+        self.i = 0
+        self.last_lens: Optional[np.ndarray] = None
+
+    def step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+             stream: Optional[torch.cuda.Stream] = None, events=None) -> torch.Tensor:
+        """Enqueue one step.  ``events``: optional dict of (start, end) event
+        pairs named 'cache' and 'decode' recorded around those launches."""
+        stream = stream or torch.cuda.current_stream(self.cache.device)
+        r = self.i % self.depth
+        if self.done[r] is not None:
+            self.done[r].synchronize()          # the pinned buffers of slot r are free
+        slots_np = self.h_slots[r].numpy()
+        _, copies = L.pa_append_slots(self.cache.pool, self.ids, self.ones, slots_out=slots_np)
+        tab_np, len_np = self.h_tab[r].numpy(), self.h_len[r].numpy()
+        L.pa_block_tables(self.cache.pool, self.ids, self.max_blocks, tables=tab_np, lens=len_np)
+        max_len = int(len_np.max())
+        if max_len > self.max_len_cap:
+            raise ValueError("a request outgrew the stepper's max_len_cap")
+        self.last_lens = len_np.copy()
+        with torch.cuda.stream(stream):
+            self.d_slots[r].copy_(self.h_slots[r], non_blocking=True)
+            self.d_tab.copy_(self.h_tab[r], non_blocking=True)
+            self.d_len.copy_(self.h_len[r], non_blocking=True)
+            ev = torch.cuda.Event()
+            ev.record(stream)
+            self.done[r] = ev
+            if events is not None:
+                events["cache"][0].record(stream)
+            if len(copies):
+                d_copies = torch.from_numpy(np.ascontiguousarray(copies)).to(self.cache.device)
+                L.pa_copy_blocks(d_copies, len(copies), self.cache.kv, stream)
+            L.pa_reshape_and_cache(k_new, v_new, self.d_slots[r], self.B, self.cache.kv, stream)
+            if events is not None:
+                events["cache"][1].record(stream)
+                events["decode"][0].record(stream)
+            L.pa_paged_attention_decode(self.out, q, self.cache.kv, self.d_tab, self.max_blocks,
+                                        self.d_len, self.B, self.n_q, self.scale, self.partition,
+                                        max_len, self.workspace, self.ws_bytes, stream)
+            if events is not None:
+                events["decode"][1].record(stream)
+        self.i += 1
+        return self.out
