@@ -6,7 +6,7 @@
 A step is one pass of the whole decode hot path for the batch: reserve one
 slot per request on the host block manager, store the step's new K/V into the
 paged pool, refresh the device block tables, and run paged decode attention
-(split-K partition kernel + reduce).  The default workload is the
+(split-K work-list kernel + reduce).  The default workload is the
 Llama-3-70B-shaped decode layer: 256 requests, 64 query / 8 KV heads,
 head_dim 128, 16-token blocks, lengths lognormal(median 1000) clipped to
 [16, 4096], split-K partitions of 512 tokens, block tables scattered over the
@@ -14,7 +14,7 @@ pool.  Inputs are seeded synthetic fp16 N(0,1) data, resident in HBM before
 timing starts.
 
 Prints one JSON line.  ``value`` is decode tokens/s per layer (requests
-advanced per second).  ``roofline`` reports the decode launch (partition +
+advanced per second).  ``roofline`` reports the decode launch (work-list +
 reduce kernels, timed with HIP events on the stream they run on) against the
 8 TB/s HBM peak using algorithmic bytes: every K and V byte of every attended
 token once per KV head, plus Q, O, block tables and lengths.
@@ -235,7 +235,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": recorded_traffic(),
-            "kernel": "pa_paged_attention_decode (decode_partition_kernel + decode_reduce_kernel)",
+            "kernel": "pa_paged_attention_decode (decode_worklist_kernel + decode_reduce_kernel)",
             "algorithmic_bytes_per_launch": int(dec_bytes),
             "launch_us_mean": round(float(dec_ms.mean()) * 1e3, 2),
             "launch_us_p50": round(float(np.median(dec_ms)) * 1e3, 2),

@@ -200,9 +200,23 @@ pa_status pa_reshape_and_cache(const pa_half* k, const pa_half* v, const int32_t
  * pa_reshape_and_cache of the same step (same stream). */
 pa_status pa_copy_blocks(const pa_copy* copies, int32_t n, pa_kv_view kv, void* stream);
 
-/* Workspace bytes pa_paged_attention_decode needs: partial (o, m, l) for every
- * (request, query head, partition) = B * n_q * ceil(max_seq_len/partition) *
- * (head_dim + 2) * 4. */
+/* Work list for the work-list form of pa_paged_attention_decode (host, pure).
+ * Request b of length L is cut into ceil(ceil(L/16) / (partition_size/16))
+ * partitions; each (request, partition) becomes one entry (b << 16) | p, and a
+ * request of length 0 one entry (b << 16).  Entries are ordered by partition
+ * size in blocks, largest first, ties in (request, partition) order, so that
+ * the short units are the last ones the GPU starts.  seq_lens: host int32
+ * [batch], batch <= 65535.  Returns the number of entries; they are written to
+ * items (host) only if that number is <= cap.  Returns -PA_ERR_INVALID on a
+ * negative length, a bad partition_size or more than 65535 partitions. */
+int32_t pa_decode_work_items(const int32_t* seq_lens, int32_t batch, int32_t partition_size,
+                             int32_t* items, int32_t cap);
+
+/* Workspace bytes pa_paged_attention_decode needs (0 when max_seq_len <=
+ * partition_size): a partial softmax state for every (request, query head,
+ * partition): the normalised partial output in fp16 (head_dim
+ * values; |o| <= max |V|, so fp16 cannot overflow) and the running max and sum
+ * in fp32 = B * n_q * ceil(max_seq_len/partition) * (2 * head_dim + 8) bytes. */
 uint64_t pa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
                                    int32_t max_seq_len, int32_t partition_size);
 
@@ -215,16 +229,26 @@ uint64_t pa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t h
  *   tables: device int32 [B][max_blocks]; seq_lens: device int32 [B], each in
  *   [0, max_seq_len] and <= max_blocks*16 (a request of length 0 gets zeros).
  *   n_q must be a multiple of kv_heads with n_q/kv_heads <= 16.
- *   Requests are split into partitions of partition_size tokens (a multiple of
- *   32, e.g. 512); each (kv head, request, partition) is one workgroup that
- *   writes a partial softmax state, and a second kernel merges partitions by
- *   log-sum-exp.  workspace: device, >= pa_decode_workspace_bytes(...).
+ *   Requests are split into partitions of partition_size tokens (a multiple
+ *   of 16 in [16, 4096], e.g. 512); each (kv head, request, partition) unit is
+ *   computed by one workgroup, which writes the request's output directly if
+ *   it has one partition and a partial softmax state otherwise; a second
+ *   kernel merges the partitions by log-sum-exp.
+ *   work_items / n_items: NULL / 0 launches one workgroup per unit (grid
+ *   form).  Otherwise a device copy of the list pa_decode_work_items built
+ *   from the same lengths (n_items <= 2^30): then as many workgroups as stay
+ *   resident walk it, workgroup y of a kv head taking entries y, 2W-1-y,
+ *   2W+y, ... of W such workgroups (work-list form); units the lengths do not
+ *   contain are skipped.  Both forms give bitwise the same outputs.
+ *   workspace: device, 16-byte aligned, >= pa_decode_workspace_bytes(...);
+ *   may be NULL when that is 0.  Calls sharing a workspace must not overlap.
  *   A table entry outside [0, num_blocks) or a length above max_blocks*16
  *   makes that request's output NaN (no out-of-bounds access). */
 pa_status pa_paged_attention_decode(pa_half* out, const pa_half* q, pa_kv_view kv,
                                     const int32_t* tables, int32_t max_blocks,
                                     const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
                                     float scale, int32_t partition_size, int32_t max_seq_len,
+                                    const int32_t* work_items, int32_t n_items,
                                     void* workspace, uint64_t workspace_bytes, void* stream);
 
 /* Workspace bytes pa_paged_attention_prefill needs for a chunk of chunk_len

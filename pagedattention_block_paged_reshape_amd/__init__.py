@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     pa_block_tables,
     pa_can_append,
     pa_copy_blocks,
+    pa_decode_work_items,
     pa_decode_workspace_bytes,
     pa_free_list,
     pa_kv_bytes_per_token,

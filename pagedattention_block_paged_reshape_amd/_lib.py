@@ -83,8 +83,9 @@ _SIGS = {
     "pa_reshape_and_cache": (C.c_int, [_P, _P, _P, _I32, pa_kv_view, _P]),
     "pa_copy_blocks": (C.c_int, [_P, _I32, pa_kv_view, _P]),
     "pa_decode_workspace_bytes": (_U64, [_I32, _I32, _I32, _I32, _I32]),
+    "pa_decode_work_items": (_I32, [_P, _I32, _I32, _P, _I32]),
     "pa_paged_attention_decode": (C.c_int, [_P, _P, pa_kv_view, _P, _I32, _P, _I32, _I32,
-                                            C.c_float, _I32, _I32, _P, _U64, _P]),
+                                            C.c_float, _I32, _I32, _P, _I32, _P, _U64, _P]),
     "pa_prefill_workspace_bytes": (_U64, [_I32, _I32, _I32, _I32]),
     "pa_paged_attention_prefill": (C.c_int, [_P, _P, pa_kv_view, _P, _I32, _I32, _I32, _I32,
                                              C.c_float, _P, _U64, _P]),
@@ -95,7 +96,7 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it with "
-            "`python -m pagedattention_block_paged_reshape_amd.build` (no fallback exists)")
+            "`python pagedattention_block_paged_reshape_amd/build.py` (no fallback exists)")
     lib = C.CDLL(LIB_PATH)
     for name, (res, args) in _SIGS.items():
         fn = getattr(lib, name)
@@ -285,15 +286,34 @@ def pa_decode_workspace_bytes(batch: int, num_q_heads: int, head_dim: int, max_s
                                              partition_size))
 
 
+def pa_decode_work_items(seq_lens, partition_size: int, out: Optional[np.ndarray] = None):
+    """Host work list (int32, largest first) for the work-list decode form.
+    ``out`` (contiguous int32) receives it in place when large enough."""
+    lens = _host(seq_lens, np.int32)
+    n = int(LIB.pa_decode_work_items(_ptr(lens), len(lens), int(partition_size), None, 0))
+    if n < 0:
+        _check(-n, "pa_decode_work_items")
+    if out is None or out.size < n:
+        out = np.empty(max(n, 1), dtype=np.int32)
+    elif out.dtype != np.int32 or not out.flags.c_contiguous:
+        raise ValueError("out must be a contiguous int32 array")
+    m = int(LIB.pa_decode_work_items(_ptr(lens), len(lens), int(partition_size), out.ctypes.data,
+                                     out.size))
+    if m != n:
+        raise PaError(PA_ERR_INTERNAL, "pa_decode_work_items")
+    return out[:n]
+
+
 def pa_paged_attention_decode(out, q, kv: pa_kv_view, tables, max_blocks: int, seq_lens,
                               batch: int, num_q_heads: int, scale: float, partition_size: int,
-                              max_seq_len: int, workspace, workspace_bytes: int,
-                              stream=None) -> None:
+                              max_seq_len: int, work_items, n_items: int, workspace,
+                              workspace_bytes: int, stream=None) -> None:
     _check(LIB.pa_paged_attention_decode(_dptr(out), _dptr(q), kv, _dptr(tables), int(max_blocks),
                                          _dptr(seq_lens), int(batch), int(num_q_heads),
                                          float(scale), int(partition_size), int(max_seq_len),
-                                         _dptr(workspace), int(workspace_bytes),
-                                         _stream(stream)), "pa_paged_attention_decode")
+                                         _dptr(work_items), int(n_items), _dptr(workspace),
+                                         int(workspace_bytes), _stream(stream)),
+           "pa_paged_attention_decode")
 
 
 def pa_prefill_workspace_bytes(chunk_len: int, num_q_heads: int, head_dim: int,

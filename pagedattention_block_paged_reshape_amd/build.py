@@ -1,6 +1,6 @@
 """Build the C-ABI shared library (host block manager + gfx950 HIP kernels).
 
-    python -m pagedattention_block_paged_reshape_amd.build
+    python pagedattention_block_paged_reshape_amd/build.py
 
 compiles every source under csrc/ with hipcc for gfx950 (the host block
 manager with g++) and links ``libpagedattn.so`` next to this file.
@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libpagedattn.so")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["cache_ops.hip", "decode.hip", "prefill.hip"]
-HOST_SOURCES = ["block_pool.cpp"]
+HOST_SOURCES = ["block_pool.cpp", "decode_plan.cpp"]
 
 # Packed-FP32 VALU ops are kept out of the generated code.
 HIPCC_FLAGS = [
@@ -31,6 +31,9 @@ HIPCC_FLAGS = [
     "-munsafe-fp-atomics",
 ]
 GXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
+# Per-file extras: the decode kernel keeps its MFMA accumulators in VGPRs,
+# which it rescales with ordinary VALU ops every block (no AGPR round trips).
+EXTRA_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc() -> str:
@@ -57,7 +60,7 @@ def build(verbose: bool = False) -> str:
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
         objs.append(obj)
-        jobs.append([hipcc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c",
+        jobs.append([hipcc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-I", INCLUDE, "-I", CSRC, "-c",
                      os.path.join(CSRC, src), "-o", obj])
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD, src + ".o")

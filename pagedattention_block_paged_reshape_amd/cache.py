@@ -90,38 +90,56 @@ class PagedKVCache:
 
     def tables(self, seq_ids, max_blocks: Optional[int] = None):
         """Device block tables [B][max_blocks] and lengths [B], plus the max length."""
-        seq_ids = list(seq_ids)
-        lens = [self.seq_len(s) for s in seq_ids]
-        if max_blocks is None:
-            max_blocks = max([1] + [-(-x // L.BLOCK_SIZE) for x in lens])
-        tab, ln = L.pa_block_tables(self.pool, seq_ids, max_blocks)
+        tab, ln, max_blocks = self.host_tables(seq_ids, max_blocks)
         return (torch.from_numpy(tab).to(self.device), torch.from_numpy(ln).to(self.device),
                 int(ln.max()) if len(ln) else 0, max_blocks)
 
+    def host_tables(self, seq_ids, max_blocks: Optional[int] = None):
+        """Host block tables [B][max_blocks], lengths [B] and max_blocks."""
+        seq_ids = list(seq_ids)
+        if max_blocks is None:
+            lens = [self.seq_len(s) for s in seq_ids]
+            max_blocks = max([1] + [-(-x // L.BLOCK_SIZE) for x in lens])
+        tab, ln = L.pa_block_tables(self.pool, seq_ids, max_blocks)
+        return tab, ln, max_blocks
+
 
 class DecodePlan:
-    """Device-resident arguments of one decode launch (tables, lengths,
-    workspace), so repeated launches time only the kernels."""
+    """Device-resident arguments of one decode launch (tables, lengths, work
+    list, workspace), so repeated launches time only the kernels.
+    ``worklist`` selects the work-list (persistent) form; otherwise one
+    workgroup per (kv head, request, partition)."""
 
     def __init__(self, cache: PagedKVCache, seq_ids, num_q_heads: int, scale: float,
-                 partition: int = DEFAULT_PARTITION, out: Optional[torch.Tensor] = None):
+                 partition: int = DEFAULT_PARTITION, out: Optional[torch.Tensor] = None,
+                 worklist: bool = True):
         self.cache = cache
-        self.tables, self.lens, self.max_len, self.max_blocks = cache.tables(seq_ids)
-        self.batch = len(list(seq_ids))
+        tab, ln, self.max_blocks = cache.host_tables(seq_ids)
+        self.tables = torch.from_numpy(tab).to(cache.device)
+        self.lens = torch.from_numpy(ln).to(cache.device)
+        self.max_len = int(ln.max()) if len(ln) else 0
+        self.batch = len(ln)
         self.n_q = int(num_q_heads)
         self.scale = float(scale)
         self.partition = int(partition)
-        ws = L.pa_decode_workspace_bytes(self.batch, self.n_q, cache.d, max(self.max_len, 1),
+        if worklist:
+            items = L.pa_decode_work_items(ln, self.partition)
+            self.items = torch.from_numpy(np.ascontiguousarray(items)).to(cache.device)
+            self.n_items = len(items)
+        else:
+            self.items, self.n_items = None, 0
+        ws = L.pa_decode_workspace_bytes(self.batch, self.n_q, cache.d, self.max_len,
                                          self.partition)
         self.ws_bytes = ws
-        self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=cache.device)
+        self.workspace = torch.zeros(max(ws, 16), dtype=torch.uint8, device=cache.device)
         self.out = out if out is not None else torch.empty(
             (self.batch, self.n_q, cache.d), dtype=torch.float16, device=cache.device)
 
     def run(self, q: torch.Tensor, stream=None) -> torch.Tensor:
         L.pa_paged_attention_decode(self.out, q, self.cache.kv, self.tables, self.max_blocks,
                                     self.lens, self.batch, self.n_q, self.scale, self.partition,
-                                    self.max_len, self.workspace, self.ws_bytes,
+                                    self.max_len, self.items, self.n_items, self.workspace,
+                                    self.ws_bytes,
                                     stream or torch.cuda.current_stream(self.cache.device))
         return self.out
 

@@ -9,161 +9,249 @@
 //     out[i][h] = sum_j softmax_j(scale * q[i][h] . K_j) * V_j,  j < len_i,
 // token j living in physical block table[i][j/16], slot j%16.  Decode reads
 // the whole cache once per step and does little arithmetic per byte
-// (ta-paperlens, "prefill and decode"), so this kernel is built to stream the
-// pool at HBM rate.
+// (ta-paperlens, "prefill and decode"), so these kernels are built to stream
+// the pool at HBM rate.
 //
 // Design (MI355X):
-//  * One workgroup (4 wavefronts) per (kv head, request, partition of
-//    `part_blocks` blocks).  blockIdx.x is the kv head, so with 8 kv heads
-//    each head's workgroups land on one XCD (workgroups are dealt to the 8
-//    XCDs round-robin), keeping any shared-prefix blocks of that head in one
-//    L2.
-//  * The G query heads that share a kv head are the 16 columns of a
-//    16x16 MFMA tile (padded when G < 16), so each K/V byte is read once per
-//    kv head, not once per query head.
-//  * Each wavefront takes every 4th block of the partition.  A block's K tile
+//  * Work unit = (kv head, request, partition of `part_blocks` blocks), done
+//    by one workgroup of 4 wavefronts.  Two launch forms share the code:
+//      - grid form: one workgroup per unit, grid (kv head, request,
+//        partition), empty units exit at once;
+//      - work-list form (persistent): as many workgroups as stay resident;
+//        each kv head's workgroups walk a host-built list of units, largest
+//        first, dealt in snake order, so no workgroup launch sits between
+//        units, the next unit's first block is in flight during a unit's
+//        epilogue, and the last units to start are the small ones.
+//    blockIdx.x is the kv head in both, so with 8 kv heads each head's
+//    workgroups land on one XCD (workgroups are dealt to the 8 XCDs
+//    round-robin), keeping that head's shared-prefix blocks in one L2.
+//  * The G query heads that share a kv head are the 16 columns of a 16x16
+//    MFMA tile (padded when G < 16), so each K/V byte is read once per kv
+//    head, not once per query head.
+//  * Each wavefront takes every 4th block of the unit.  A block's K tile
 //    ([16 tokens][D], 16*D*2 bytes contiguous) is loaded straight into the
-//    MFMA A-operand registers (16 B per lane per K-step): S^T = K . Q^T gives
-//    lane l the scores of 4 tokens for query head l%16.  Those scores, after
-//    the online-softmax update, are already laid out as the B operand of
-//    O^T += V^T . P^T, whose A operand is the V tile ([D][16 tokens]
-//    contiguous, 8 B per lane per MFMA).  No LDS round trip is needed in the
-//    main loop; the next block's tiles are in flight while the current one
-//    is computed.
+//    MFMA A-operand registers: S^T = K . Q^T gives lane l the scores of 4
+//    tokens for query head l%16.  Those scores, after the online-softmax
+//    update, are already laid out as the B operand of O^T += V^T . P^T, whose
+//    A operand is the V tile ([D][16 tokens] contiguous).  Two register sets
+//    alternate so that one block's loads are in flight while the other is
+//    computed; no LDS round trip in the main loop.
 //  * Softmax runs in fp32 in base 2 (scores pre-multiplied by scale*log2 e);
 //    the per-head running max is reduced across the 4 lane groups with two
 //    xor shuffles, the running sum is kept per lane and reduced at the end.
-//  * The 4 wavefronts' states are merged through LDS.  A request that fits in
-//    one partition writes its fp16 output directly; longer ones write an fp32
-//    partial (o normalised, m, l) that the reduce kernel merges by
-//    log-sum-exp.
+//  * The 4 wavefronts merge through LDS with no closing barrier: each posts
+//    its state and counts itself in; the last to arrive merges in fixed wave
+//    order (deterministic) and stores.  A request that fits in one partition
+//    gets its fp16 output directly; longer ones store an fp16 normalised
+//    partial plus fp32 (max, sum), merged by the reduce kernel.
 #include <math.h>
 
 #include "pa_device.h"
 
 namespace pa {
 
-constexpr int kDecodeWaves = 4;
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 2
+#endif
+#ifndef PA_MERGE_SLOTS
+#define PA_MERGE_SLOTS 2
+#endif
+constexpr int kDecodeWaves = PA_DECODE_WAVES;  // wavefronts per workgroup
+constexpr int kDecodeThreads = kDecodeWaves * kWave;
+constexpr int kMergeSlots = PA_MERGE_SLOTS;    // LDS merge slots of the work-list form
+constexpr int kMaxWaveBlocks = 128;            // block ids a wavefront holds (2 per lane)
+constexpr int kSpinLimit = 1 << 22;  // safety bound on the LDS slot wait
 
+struct DecodeArgs {
+  const f16* q;
+  const f16* kp;
+  const f16* vp;
+  const int32_t* tables;
+  const int32_t* seq_lens;
+  int32_t max_blocks;
+  int32_t num_blocks;
+  int32_t n_kv;
+  int32_t G;
+  float scale_log2;
+  int32_t part_blocks;
+  int32_t p_max;
+  f16* out;
+  f16* ws_o;    // [B][n_q][p_max][D] fp16
+  float* ws_m;  // [B][n_q][p_max]
+  float* ws_l;  // [B][n_q][p_max]
+};
+
+// One wavefront's share of a unit: running max and sum per query head and
+// the unnormalised O^T tile (o[c][j] = O^T[c*16 + 4*(lane/16) + j][lane%16]).
 template <int D>
-__global__ __launch_bounds__(256) void decode_partition_kernel(
-    const f16* __restrict__ q, const f16* __restrict__ kp, const f16* __restrict__ vp,
-    const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_lens,
-    int32_t max_blocks, int32_t num_blocks, int32_t n_kv, int32_t G, float scale_log2,
-    int32_t part_blocks, int32_t p_max, f16* __restrict__ out, float* __restrict__ ws_o,
-    float* __restrict__ ws_m, float* __restrict__ ws_l) {
-  constexpr int KS = D / 32;  // K-steps of the score MFMA
-  constexpr int DT = D / 16;  // 16-wide dimension tiles of the output
-  const int g = blockIdx.x;
-  const int b = blockIdx.y;
-  const int p = blockIdx.z;
-  const int n_q = n_kv * G;
+struct WaveState {
+  float m;
+  float l;
+  f32x4 o[D / 16];
+};
 
-  int L = seq_lens[b];
-  bool bad = false;
+// A request's length, clamped to what the tables and the partition grid can
+// hold; anything clamped marks the request bad (its outputs become NaN).
+__device__ __forceinline__ int clamp_len(const DecodeArgs& a, int b, bool& bad) {
+  int L = scalar_load(a.seq_lens, b);
   if (L < 0) {
     L = 0;
     bad = true;
   }
-  if (L > max_blocks * kBlock) {
-    L = max_blocks * kBlock;
+  if (L > a.max_blocks * kBlock) {
+    L = a.max_blocks * kBlock;
     bad = true;
   }
-  const int part_tokens = part_blocks * kBlock;
-  if (L > p_max * part_tokens) {  // longer than the max_seq_len the grid was sized for
-    L = p_max * part_tokens;
+  if (L > a.p_max * a.part_blocks * kBlock) {
+    L = a.p_max * a.part_blocks * kBlock;
     bad = true;
   }
-  const int n_parts = (L + part_tokens - 1) / part_tokens;
+  return L;
+}
 
-  if (L == 0) {
-    if (p == 0) {
-      const float fill = bad ? __builtin_nanf("") : 0.0f;
-      for (int i = threadIdx.x; i < G * D; i += blockDim.x)
-        out[(static_cast<int64_t>(b) * n_q + g * G + i / D) * D + (i % D)] = static_cast<f16>(fill);
+// A work unit (request b, partition p) as one wavefront sees it: the
+// partition's blocks kb0 + wave + kDecodeWaves*i, i < cnt, and their physical
+// ids (lane j of my_pb / my_pb2 holds the id of the wave's block j / 64 + j;
+// at most 128 of them, which bounds partition_size).  A unit the lengths do not contain (a work
+// list built from other lengths) is run as empty and not stored.
+struct Unit {
+  int b;
+  int p;
+  int L;        // attended length (0 for an empty or absent unit)
+  int n_parts;  // partitions of the request
+  int kb0;
+  int cnt;
+  int my_pb;   // id of the wave's block lane (lane < 64)
+  int my_pb2;  // id of the wave's block 64 + lane
+  bool ok;
+  bool bad;
+};
+
+__device__ __forceinline__ Unit no_unit() {
+  Unit u;
+  u.b = u.p = u.L = u.n_parts = u.kb0 = u.cnt = u.my_pb = u.my_pb2 = 0;
+  u.ok = false;
+  u.bad = false;
+  return u;
+}
+
+__device__ __forceinline__ Unit make_unit(const DecodeArgs& a, int b, int p, int wave, int lane) {
+  Unit u;
+  u.b = b;
+  u.p = p;
+  u.bad = false;
+  const int L = clamp_len(a, b, u.bad);
+  const int part_tokens = a.part_blocks * kBlock;
+  u.n_parts = (L + part_tokens - 1) / part_tokens;
+  u.ok = L > 0 ? p < u.n_parts : p == 0;
+  u.L = u.ok ? L : 0;
+  u.kb0 = (u.ok ? p : 0) * a.part_blocks;
+  const int kb_end = min(u.kb0 + a.part_blocks, (u.L + kBlock - 1) / kBlock);
+  const int nb = max(kb_end - u.kb0, 0);
+  u.cnt = nb > wave ? (nb - wave + kDecodeWaves - 1) / kDecodeWaves : 0;
+  const int32_t* trow = a.tables + static_cast<int64_t>(b) * a.max_blocks;
+  u.my_pb = 0;
+  u.my_pb2 = 0;
+  auto fetch_id = [&](int j, int& dst) {
+    if (j < u.cnt) {
+      const int pb = trow[u.kb0 + wave + kDecodeWaves * j];
+      if (static_cast<uint32_t>(pb) < static_cast<uint32_t>(a.num_blocks))
+        dst = pb;
+      else
+        u.bad = true;  // replaced by block 0; the request's output becomes NaN
     }
-    return;
-  }
-  if (p >= n_parts) return;
+  };
+  fetch_id(lane, u.my_pb);
+  if (u.cnt > kWave) fetch_id(kWave + lane, u.my_pb2);
+  return u;
+}
 
-  const int wave = uniform(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int col = lane & 15;  // token row of K loads; query head of Q / outputs
+
+// Q^T as the B operand: lane holds query head lane%16 (zero when >= G), dims
+// kk*32 + 8*(lane/16) .. +8.
+template <int D>
+__device__ __forceinline__ void load_q(const DecodeArgs& a, int g, int b, int lane, f16x8* qf) {
+  const int col = lane & 15;
+  const int lg = lane >> 4;
+  const f16* qrow =
+      a.q + (static_cast<int64_t>(b) * a.n_kv * a.G + g * a.G + col) * D + lg * 8;
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk)
+    qf[kk] = col < a.G ? *reinterpret_cast<const f16x8*>(qrow + kk * 32)
+                       : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+}
+
+// K and V tiles of physical block pb, kv head g, straight into MFMA operand
+// registers (K: 16 B per lane per K-step; V^T: 8 B per lane per dim tile).
+template <int D>
+__device__ __forceinline__ void load_block(const DecodeArgs& a, int g, int pb, int lane,
+                                           f16x8* kd, f16x4* vd) {
+  const int col = lane & 15;
+  const int lg = lane >> 4;
+  const int64_t tile = static_cast<int64_t>(pb) * a.n_kv + g;
+  const f16* kt = a.kp + tile * (kBlock * D) + col * D + lg * 8;
+  const f16* vt = a.vp + tile * (kBlock * D) + col * kBlock + lg * 4;
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) kd[kk] = *reinterpret_cast<const f16x8*>(kt + kk * 32);
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) vd[c] = *reinterpret_cast<const f16x4*>(vt + c * 16 * kBlock);
+}
+
+// Physical block behind the wave's i-th load: unit u's blocks first; past
+// them the next unit's first block (so that it is in flight during u's
+// epilogue), or u's last block again (an L2 hit) when there is none.
+__device__ __forceinline__ int unit_block(const Unit& u, int i) {
+  return i < kWave ? __builtin_amdgcn_readlane(u.my_pb, i)
+                   : __builtin_amdgcn_readlane(u.my_pb2, i - kWave);
+}
+
+__device__ __forceinline__ int pick_block(const Unit& u, const Unit& nx, int i) {
+  if (i < u.cnt) return unit_block(u, i);
+  if (nx.cnt > 0) return unit_block(nx, 0);
+  return u.cnt > 0 ? unit_block(u, u.cnt - 1) : 0;
+}
+
+// The wavefront's pass over its blocks of unit u on kv head g.  On entry
+// kA/vA hold u's first block (when u.cnt > 0); on exit they hold nx's first
+// block (when nx.cnt > 0).
+template <int D>
+__device__ __forceinline__ void run_unit(const DecodeArgs& a, int g, int wave, int lane,
+                                         const Unit& u, const Unit& nx, const f16x8* qf,
+                                         f16x8* kA, f16x4* vA, f16x8* kB, f16x4* vB,
+                                         WaveState<D>& st) {
+  constexpr int KS = D / 32;  // K-steps of the score MFMA
+  constexpr int DT = D / 16;  // 16-wide dimension tiles of the output
   const int lg = lane >> 4;   // lane group: which 8 (K) or 4 (V, P) k-values
 
-  const int kb0 = p * part_blocks;
-  const int kb_end = min(kb0 + part_blocks, (L + kBlock - 1) / kBlock);
-  const int nb = kb_end - kb0;
-  const int cnt = nb > wave ? (nb - wave + kDecodeWaves - 1) / kDecodeWaves : 0;
-
-  // Q^T as the B operand: lane holds query head `col`, dims kk*32 + lg*8 .. +8.
-  f16x8 qf[KS];
-  {
-    const f16* qrow = q + (static_cast<int64_t>(b) * n_q + g * G + col) * D + lg * 8;
+  st.m = -INFINITY;
+  st.l = 0.0f;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      if (col < G)
-        qf[kk] = *reinterpret_cast<const f16x8*>(qrow + kk * 32);
-      else
-        qf[kk] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    }
+  for (int c = 0; c < DT; ++c) st.o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (u.cnt == 0) {
+    if (nx.cnt > 0) load_block<D>(a, g, pick_block(u, nx, 0), lane, kA, vA);
+    return;
   }
+  const int L = u.L;
 
-  float m_run = -INFINITY;
-  float l_run = 0.0f;
-  f32x4 o[DT];
-#pragma unroll
-  for (int c = 0; c < DT; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int32_t* trow = tables + static_cast<int64_t>(b) * max_blocks;
-  const int64_t head_tile = static_cast<int64_t>(n_kv);
-
-  f16x8 kf[KS];
-  f16x4 vf[DT];
-
-  auto load_block = [&](int kb, f16x8* kd, f16x4* vd) {
-    int pb = trow[kb];
-    if (static_cast<uint32_t>(pb) >= static_cast<uint32_t>(num_blocks)) {
-      bad = true;
-      pb = 0;
-    }
-    const int64_t tile = static_cast<int64_t>(pb) * head_tile + g;
-    const f16* kt = kp + tile * (kBlock * D) + col * D + lg * 8;
-    const f16* vt = vp + tile * (kBlock * D) + col * kBlock + lg * 4;
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) kd[kk] = *reinterpret_cast<const f16x8*>(kt + kk * 32);
-#pragma unroll
-    for (int c = 0; c < DT; ++c)
-      vd[c] = *reinterpret_cast<const f16x4*>(vt + c * 16 * kBlock);
-  };
-
-  if (cnt > 0) load_block(kb0 + wave, kf, vf);
-
-  for (int i = 0; i < cnt; ++i) {
-    const int kb = kb0 + wave + kDecodeWaves * i;
-    f16x8 kn[KS];
-    f16x4 vn[DT];
-    const bool more = i + 1 < cnt;
-    if (more) load_block(kb + kDecodeWaves, kn, vn);
-
-    // S^T tile: lane gets tokens kb*16 + 4*lg + j for query head col.
+  // Online-softmax update with the wave's i-th block.
+  auto compute = [&](int i, const f16x8* kf, f16x4* vf) {
+    const int kb = u.kb0 + wave + kDecodeWaves * i;
+    // S^T tile: lane gets tokens kb*16 + 4*lg + j for query head lane%16.
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) s = mfma16x16x32(kf[kk], qf[kk], s);
-
     const int tok0 = kb * kBlock + 4 * lg;
-    const bool partial = (kb + 1) * kBlock > L;  // uniform: only the request's last block
+    const int valid = L - tok0;  // this lane's tokens j < valid are live
     float sv[4];
     float mloc = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float x = s[j] * scale_log2;
-      sv[j] = (!partial || tok0 + j < L) ? x : -INFINITY;
+      sv[j] = j < valid ? s[j] * a.scale_log2 : -INFINITY;
       mloc = fmaxf(mloc, sv[j]);
     }
     mloc = wave_max_xor16_32(mloc);
-    const float m_new = fmaxf(m_run, mloc);
-    const float alpha = exp2f(m_run - m_new);
+    const float m_new = fmaxf(st.m, mloc);
+    const float alpha = exp2f(st.m - m_new);
     f16x4 pf;
     float psum = 0.0f;
 #pragma unroll
@@ -172,113 +260,347 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(
       pf[j] = ph;
       psum += static_cast<float>(ph);
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (partial) {
-      // slots past the request's end hold stale bytes: zero them so that
-      // 0 * (stale) cannot inject NaN/Inf
+    st.l = st.l * alpha + psum;
+    st.m = m_new;
+    if ((kb + 1) * kBlock > L) {
+      // The request's last block: slots past its end hold stale bytes; clear
+      // them so that 0 * stale cannot inject NaN/Inf into the MFMA.
+      const uint32_t lo = valid >= 2 ? 0xFFFFFFFFu : (valid == 1 ? 0x0000FFFFu : 0u);
+      const uint32_t hi = valid >= 4 ? 0xFFFFFFFFu : (valid == 3 ? 0x0000FFFFu : 0u);
 #pragma unroll
-      for (int c = 0; c < DT; ++c)
+      for (int c = 0; c < DT; ++c) {
+        uint2 bits = __builtin_bit_cast(uint2, vf[c]);
+        bits.x &= lo;
+        bits.y &= hi;
+        vf[c] = __builtin_bit_cast(f16x4, bits);
+      }
+    }
+    // Rescale only when some head's running max moved (alpha != 1).
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (tok0 + j >= L) vf[c][j] = static_cast<f16>(0.0f);
+      for (int c = 0; c < DT; ++c) st.o[c] *= alpha;
     }
 #pragma unroll
-    for (int c = 0; c < DT; ++c) {
-      o[c] *= alpha;
-      o[c] = mfma16x16x16(vf[c], pf, o[c]);
-    }
-    if (more) {
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) kf[kk] = kn[kk];
-#pragma unroll
-      for (int c = 0; c < DT; ++c) vf[c] = vn[c];
-    }
+    for (int c = 0; c < DT; ++c) st.o[c] = mfma16x16x16(vf[c], pf, st.o[c]);
+  };
+
+  // Two register sets in ping-pong: while one block is computed the next
+  // one's loads are in flight; no register copies, so the compiler's wait
+  // counts only cover the block being consumed.  Every load is
+  // unconditional (pick_block), the last one into kA/vA being nx's first.
+  for (int i = 0; i < u.cnt; i += 2) {
+    load_block<D>(a, g, pick_block(u, nx, i + 1), lane, kB, vB);
+    compute(i, kA, vA);
+    load_block<D>(a, g, pick_block(u, nx, i + 2), lane, kA, vA);
+    if (i + 1 < u.cnt) compute(i + 1, kB, vB);
   }
+}
 
-  l_run = wave_sum_xor16_32(l_run);
+// LDS of one merge: per-wave (m, l) per head and O^T rows [wave][head][D+4].
+template <int D>
+struct MergeSlot {
+  float* m;  // [kDecodeWaves][16]
+  float* l;  // [kDecodeWaves][16]
+  float* o;  // [kDecodeWaves][G][D + 4]
+  int* arrive;
+  int* bad;
+};
 
-  // Merge the 4 wavefronts.  o[c][j] is O^T[c*16 + 4*lg + j][col].
-  __shared__ float sm_m[kDecodeWaves][16];
-  __shared__ float sm_l[kDecodeWaves][16];
-  __shared__ float sm_o[kDecodeWaves][D][17];
-  __shared__ int sm_bad;
-  if (threadIdx.x == 0) sm_bad = 0;
-  __syncthreads();
+// Post the wave's state; returns true for the last of the 4 to arrive.
+template <int D>
+__device__ __forceinline__ bool post_state(const MergeSlot<D>& ms, const WaveState<D>& st, int G,
+                                           int wave, int lane, bool bad) {
+  constexpr int DT = D / 16;
+  constexpr int OROW = D + 4;
+  const int col = lane & 15;
+  const int lg = lane >> 4;
+  const float l = wave_sum_xor16_32(st.l);
   if (lg == 0) {
-    sm_m[wave][col] = m_run;
-    sm_l[wave][col] = l_run;
+    ms.m[wave * 16 + col] = st.m;
+    ms.l[wave * 16 + col] = l;
   }
+  if (col < G) {
+    float* row = ms.o + (wave * G + col) * OROW + 4 * lg;
 #pragma unroll
-  for (int c = 0; c < DT; ++c)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sm_o[wave][c * 16 + 4 * lg + j][col] = o[c][j];
-  if (bad && lane == 0) sm_bad = 1;
-  __syncthreads();
-  const bool any_bad = sm_bad != 0;
+    for (int c = 0; c < DT; ++c) *reinterpret_cast<f32x4*>(row + c * 16) = st.o[c];
+  }
+  if (bad) __hip_atomic_store(ms.bad, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  int arrived = 0;
+  if (lane == 0)
+    arrived = __hip_atomic_fetch_add(ms.arrive, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+  arrived = __shfl(arrived, 0);
+  return arrived == kDecodeWaves - 1;
+}
 
-  for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
-    const int h = idx / D;
-    const int dim = idx % D;
+// Merge the 4 posted states of unit (g, b, p) in fixed wave order and store:
+// each lane produces 8 consecutive dims of one head (one 16-byte store).
+template <int D>
+__device__ __forceinline__ void merge_store(const DecodeArgs& a, const MergeSlot<D>& ms, int g,
+                                            int b, int p, int L, int n_parts, int lane) {
+  constexpr int OROW = D + 4;
+  const int G = a.G;
+  const int n_q = a.n_kv * G;
+  const bool any_bad =
+      __hip_atomic_load(ms.bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
+  for (int idx = lane; idx < G * (D / 8); idx += kWave) {
+    const int h = idx / (D / 8);
+    const int d0 = (idx % (D / 8)) * 8;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, sm_m[w][h]);
-    float wsum = 0.0f, acc = 0.0f;
+    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, ms.m[w * 16 + h]);
+    float wsum = 0.0f;
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+    if (L > 0) {
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) {
-      const float e = exp2f(sm_m[w][h] - M);
-      wsum += e * sm_l[w][h];
-      acc += e * sm_o[w][dim][h];
+      for (int w = 0; w < kDecodeWaves; ++w) {
+        const float e = exp2f(ms.m[w * 16 + h] - M);
+        wsum += e * ms.l[w * 16 + h];
+        const float* row = ms.o + (w * G + h) * OROW + d0;
+        a0 += e * *reinterpret_cast<const f32x4*>(row);
+        a1 += e * *reinterpret_cast<const f32x4*>(row + 4);
+      }
     }
-    float r = acc / wsum;
-    if (any_bad) r = __builtin_nanf("");
+    // an empty request reads as zeros; a flagged one as NaN
+    const float inv = any_bad ? __builtin_nanf("") : (L > 0 ? 1.0f / wsum : 0.0f);
+    f16x8 r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      r[k] = static_cast<f16>(a0[k] * inv);
+      r[k + 4] = static_cast<f16>(a1[k] * inv);
+    }
     const int64_t qh = static_cast<int64_t>(b) * n_q + g * G + h;
-    if (n_parts == 1) {
-      out[qh * D + dim] = static_cast<f16>(r);
+    if (n_parts <= 1) {
+      *reinterpret_cast<f16x8*>(a.out + qh * D + d0) = r;
     } else {
-      const int64_t slot = qh * p_max + p;
-      ws_o[slot * D + dim] = r;
-      if (dim == 0) {
-        ws_m[slot] = any_bad ? __builtin_nanf("") : M;
-        ws_l[slot] = wsum;
+      // partials of one unit are contiguous: [B][n_kv][p_max][G][D]
+      const int64_t slot = ((static_cast<int64_t>(b) * a.n_kv + g) * a.p_max + p) * G + h;
+      *reinterpret_cast<f16x8*>(a.ws_o + slot * D + d0) = r;
+      if (d0 == 0) {
+        a.ws_m[slot] = any_bad ? __builtin_nanf("") : M;
+        a.ws_l[slot] = wsum;
       }
     }
   }
 }
 
-// Merge the partitions of each (request, query head): with M = max_p m_p and
-// w_p = l_p * 2^(m_p - M), out = sum_p w_p o_p / sum_p w_p.
+// Grid form: one workgroup per (kv head, request, partition).
 template <int D>
-__global__ __launch_bounds__(64) void decode_reduce_kernel(
-    const int32_t* __restrict__ seq_lens, int32_t max_blocks, int32_t n_q, int32_t part_tokens,
-    int32_t p_max, const float* __restrict__ ws_o, const float* __restrict__ ws_m,
-    const float* __restrict__ ws_l, f16* __restrict__ out) {
-  constexpr int PER = D / 64;
-  const int h = blockIdx.x;
+__global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(DecodeArgs a) {
+  const int g = blockIdx.x;
   const int b = blockIdx.y;
-  int L = seq_lens[b];
-  if (L < 0) return;                                    // partition kernel wrote NaN
-  if (L > max_blocks * kBlock) L = max_blocks * kBlock;  // partials are NaN-flagged
-  const int n_parts = min((L + part_tokens - 1) / part_tokens, p_max);
-  if (n_parts <= 1) return;
-  const int64_t base = (static_cast<int64_t>(b) * n_q + h) * p_max;
-  float M = -INFINITY;
-  for (int pp = 0; pp < n_parts; ++pp) M = fmaxf(M, ws_m[base + pp]);
-  float wsum = 0.0f;
-  float acc[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
-  for (int pp = 0; pp < n_parts; ++pp) {
-    const float w = ws_l[base + pp] * exp2f(ws_m[base + pp] - M);
-    wsum += w;
-    const float* op = ws_o + (base + pp) * D;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] += w * op[threadIdx.x + 64 * e];
+  const int p = blockIdx.z;
+  bool bad = false;
+  const int L = clamp_len(a, b, bad);
+  const int part_tokens = a.part_blocks * kBlock;
+  const int n_parts = (L + part_tokens - 1) / part_tokens;
+  if (L > 0 ? p >= n_parts : p > 0) return;
+
+  __shared__ float sm_m[kDecodeWaves * 16];
+  __shared__ float sm_l[kDecodeWaves * 16];
+  __shared__ int sm_arrive;
+  __shared__ int sm_bad;
+  extern __shared__ f32x4 sm_o4[];  // [kDecodeWaves][G][D + 4] floats, 16-byte aligned
+  if (threadIdx.x == 0) {
+    sm_arrive = 0;
+    sm_bad = 0;
   }
-  const float inv = 1.0f / wsum;
-  f16* orow = out + (static_cast<int64_t>(b) * n_q + h) * D;
+  __syncthreads();
+
+  const int wave = uniform(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const Unit u = make_unit(a, b, p, wave, lane);
+  const Unit nx = no_unit();
+  f16x8 qf[D / 32], kA[D / 32], kB[D / 32];
+  f16x4 vA[D / 16], vB[D / 16];
+  if (u.cnt > 0) {
+    load_q<D>(a, g, b, lane, qf);
+    load_block<D>(a, g, pick_block(u, nx, 0), lane, kA, vA);
+  }
+  WaveState<D> st;
+  run_unit<D>(a, g, wave, lane, u, nx, qf, kA, vA, kB, vB, st);
+  const MergeSlot<D> ms{sm_m, sm_l, reinterpret_cast<float*>(sm_o4), &sm_arrive, &sm_bad};
+  if (post_state<D>(ms, st, a.G, wave, lane, u.bad))
+    merge_store<D>(a, ms, g, b, p, u.L, n_parts, lane);
+}
+
+// Work-list form: gridDim.y resident workgroups per kv head walk `items`
+// ((request << 16) | partition, largest first) in a snake deal: in round r
+// workgroup y takes item r*wph + y, in reverse order on odd rounds, so every
+// workgroup gets a near-equal share of blocks and the small units come last.
+// While a unit is computed the next unit's block ids are already loaded, and
+// its first block and query rows are in flight during the unit's epilogue.
+// LDS merge slots rotate over consecutive units so that a fast wavefront can
+// post the next unit while the last one of an earlier unit still merges.
+template <int D>
+__global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(3)))
+void decode_worklist_kernel(DecodeArgs a, const int32_t* __restrict__ items, int32_t n_items) {
+  constexpr int OROW = D + 4;
+  const int g = blockIdx.x;
+  const int wph = gridDim.y;
+  const int y = blockIdx.y;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+
+  __shared__ float sm_m[kMergeSlots][kDecodeWaves * 16];
+  __shared__ float sm_l[kMergeSlots][kDecodeWaves * 16];
+  __shared__ int sm_arrive[kMergeSlots];
+  __shared__ int sm_bad[kMergeSlots];
+  __shared__ int sm_merged[kMergeSlots];
+  extern __shared__ f32x4 sm_o4[];  // [kMergeSlots][kDecodeWaves][G][D + 4] floats
+  if (threadIdx.x < kMergeSlots) {
+    sm_arrive[threadIdx.x] = 0;
+    sm_bad[threadIdx.x] = 0;
+    sm_merged[threadIdx.x] = 0;
+  }
+  __syncthreads();
+  const int slot_floats = kDecodeWaves * a.G * OROW;
+
+  auto item = [&](int k) { return (k & 1) ? (k + 1) * wph - 1 - y : k * wph + y; };
+  auto unit_at = [&](int t) {
+    const uint32_t packed = static_cast<uint32_t>(scalar_load(items, t));
+    return make_unit(a, static_cast<int>(packed >> 16), static_cast<int>(packed & 0xFFFFu), wave,
+                     lane);
+  };
+
+  if (item(0) >= n_items) return;
+  Unit u = unit_at(item(0));
+  f16x8 qf[D / 32], kA[D / 32], kB[D / 32];
+  f16x4 vA[D / 16], vB[D / 16];
+  load_q<D>(a, g, u.b, lane, qf);
+  if (u.cnt > 0) load_block<D>(a, g, pick_block(u, no_unit(), 0), lane, kA, vA);
+
+  for (int k = 0;; ++k) {
+    const bool more = item(k + 1) < n_items;
+    const Unit nx = more ? unit_at(item(k + 1)) : no_unit();
+    WaveState<D> st;
+    run_unit<D>(a, g, wave, lane, u, nx, qf, kA, vA, kB, vB, st);
+    if (more) load_q<D>(a, g, nx.b, lane, qf);  // in flight during the epilogue
+
+    const int buf = k % kMergeSlots;
+    // slot `buf` was last used by unit k - kMergeSlots: wait until it has been merged
+    int spins = 0;
+    while (__hip_atomic_load(&sm_merged[buf], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) !=
+           k / kMergeSlots) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kSpinLimit) return;
+    }
+    const MergeSlot<D> ms{sm_m[buf], sm_l[buf],
+                          reinterpret_cast<float*>(sm_o4) + buf * slot_floats, &sm_arrive[buf],
+                          &sm_bad[buf]};
+    if (post_state<D>(ms, st, a.G, wave, lane, u.bad)) {
+      if (u.ok) merge_store<D>(a, ms, g, u.b, u.p, u.L, u.n_parts, lane);
+      if (lane == 0) {
+        sm_arrive[buf] = 0;
+        sm_bad[buf] = 0;
+        __hip_atomic_fetch_add(&sm_merged[buf], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+    }
+    if (!more) return;
+    u = nx;
+  }
+}
+
+// Merge the partitions of each (request, query head): with M = max_p m_p and
+// w_p = l_p * 2^(m_p - M), out = sum_p w_p o_p / sum_p w_p.  One workgroup per
+// (kv head, request); the 32 lanes of head h load the (m, l) of up to 32
+// partitions at once and reduce them with shuffles, then each lane
+// accumulates D/32 dims over the partitions with 8 loads in flight at a time.
+// Requests that fit in one partition were written by the partition kernel
+// and are skipped.
+template <int D>
+__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
+  constexpr int PER = D / 32;
+  constexpr int UNROLL = 8;
+  typedef _Float16 f16xP __attribute__((ext_vector_type(PER)));
+  const int g = blockIdx.x;
+  const int b = blockIdx.y;
+  int L = a.seq_lens[b];
+  if (L < 0) return;                                         // written as NaN already
+  if (L > a.max_blocks * kBlock) L = a.max_blocks * kBlock;  // partials are NaN-flagged
+  const int part_tokens = a.part_blocks * kBlock;
+  const int n_parts = min((L + part_tokens - 1) / part_tokens, a.p_max);
+  if (n_parts <= 1) return;
+  const int G = a.G;
+  const int n_q = a.n_kv * G;
+  const int j = threadIdx.x & 31;
+  // partials of (b, g): [p_max][G][D] contiguous, (m, l) as [p_max][G]
+  const int64_t bg = (static_cast<int64_t>(b) * a.n_kv + g) * a.p_max * G;
+  for (int h = threadIdx.x >> 5; h < G; h += blockDim.x >> 5) {
+    const int64_t qh = static_cast<int64_t>(b) * n_q + g * G + h;
+    auto load_o = [&](int p) {
+      return *reinterpret_cast<const f16xP*>(a.ws_o + (bg + static_cast<int64_t>(p) * G + h) * D +
+                                             j * PER);
+    };
+    // the first partials' rows are requested together with the (m, l) loads
+    f16xP v[UNROLL];
 #pragma unroll
-  for (int e = 0; e < PER; ++e) orow[threadIdx.x + 64 * e] = static_cast<f16>(acc[e] * inv);
+    for (int u = 0; u < UNROLL; ++u)
+      if (u < n_parts) v[u] = load_o(u);
+    float M = -INFINITY;
+    for (int p0 = 0; p0 < n_parts; p0 += 32)
+      if (p0 + j < n_parts) M = fmaxf(M, a.ws_m[bg + (p0 + j) * G + h]);
+#pragma unroll
+    for (int sh = 1; sh < 32; sh <<= 1) M = fmaxf(M, __shfl_xor(M, sh, 32));
+    float wsum = 0.0f;
+    float acc[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
+    for (int p0 = 0; p0 < n_parts; p0 += 32) {
+      const int np = min(32, n_parts - p0);
+      const int64_t sj = bg + (p0 + j) * G + h;
+      const float wj = j < np ? a.ws_l[sj] * exp2f(a.ws_m[sj] - M) : 0.0f;
+      float ws = wj;
+#pragma unroll
+      for (int sh = 1; sh < 32; sh <<= 1) ws += __shfl_xor(ws, sh, 32);
+      wsum += ws;
+      for (int u0 = 0; u0 < np; u0 += UNROLL) {
+        if (p0 + u0 > 0) {
+#pragma unroll
+          for (int u = 0; u < UNROLL; ++u)
+            if (u0 + u < np) v[u] = load_o(p0 + u0 + u);
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+          const float w = __shfl(wj, u0 + u, 32);
+          if (u0 + u < np) {
+#pragma unroll
+            for (int e = 0; e < PER; ++e) acc[e] += w * static_cast<float>(v[u][e]);
+          }
+        }
+      }
+    }
+    const float inv = 1.0f / wsum;
+    f16xP rr;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) rr[e] = static_cast<f16>(acc[e] * inv);
+    *reinterpret_cast<f16xP*>(a.out + qh * D + j * PER) = rr;
+  }
+}
+
+// Resident workgroups of the work-list kernel on the current device (cached
+// per head_dim and G; the dynamic LDS depends on G).
+static int worklist_resident_wgs(int D, int G, size_t lds) {
+  static int per_cu[2][17];
+  static int cus = 0;
+  int& slot = per_cu[D == 128 ? 1 : 0][G];
+  if (slot == 0) {
+    int n = 0;
+    const void* fn = D == 128 ? reinterpret_cast<const void*>(&decode_worklist_kernel<128>)
+                              : reinterpret_cast<const void*>(&decode_worklist_kernel<64>);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kDecodeThreads, lds) != hipSuccess || n < 1)
+      n = 1;
+    slot = n;
+  }
+  if (cus == 0) {
+    int dev = 0, c = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        c > 0)
+      cus = c;
+    else
+      cus = 1;
+  }
+  return slot * cus;
 }
 
 }  // namespace pa
@@ -288,10 +610,16 @@ using namespace pa;
 extern "C" uint64_t pa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
                                               int32_t head_dim, int32_t max_seq_len,
                                               int32_t partition_size) {
-  if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len <= 0 || partition_size <= 0)
+  if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len < 0 || partition_size <= 0)
     return 0;
-  const uint64_t parts = (static_cast<uint64_t>(max_seq_len) + partition_size - 1) / partition_size;
-  return static_cast<uint64_t>(batch) * num_q_heads * parts * (head_dim + 2) * sizeof(float);
+  const uint64_t parts = max_seq_len == 0
+                             ? 1
+                             : (static_cast<uint64_t>(max_seq_len) + partition_size - 1) /
+                                   partition_size;
+  // fp16 normalised partial outputs, then fp32 running max and sum
+  const uint64_t partials =
+      parts > 1 ? static_cast<uint64_t>(batch) * num_q_heads * parts * (head_dim * 2 + 8) : 0;
+  return partials;
 }
 
 extern "C" pa_status pa_paged_attention_decode(pa_half* out, const pa_half* q, pa_kv_view kv,
@@ -299,6 +627,7 @@ extern "C" pa_status pa_paged_attention_decode(pa_half* out, const pa_half* q, p
                                                const int32_t* seq_lens, int32_t batch,
                                                int32_t num_q_heads, float scale,
                                                int32_t partition_size, int32_t max_seq_len,
+                                               const int32_t* work_items, int32_t n_items,
                                                void* workspace, uint64_t workspace_bytes,
                                                void* stream) {
   if (kv.k_pool == nullptr || kv.v_pool == nullptr || kv.block_size != kBlock ||
@@ -309,11 +638,15 @@ extern "C" pa_status pa_paged_attention_decode(pa_half* out, const pa_half* q, p
   if (num_q_heads <= 0 || num_q_heads % kv.num_kv_heads != 0) return PA_ERR_INVALID;
   const int G = num_q_heads / kv.num_kv_heads;
   if (G > 16) return PA_ERR_INVALID;
-  if (partition_size <= 0 || partition_size % kBlock != 0) return PA_ERR_INVALID;
+  if (partition_size <= 0 || partition_size % kBlock != 0 ||
+      partition_size > kDecodeWaves * kMaxWaveBlocks * kBlock)
+    return PA_ERR_INVALID;
   if (!(scale == scale)) return PA_ERR_INVALID;
+  if (n_items < 0 || n_items > (1 << 30) || (n_items > 0 && work_items == nullptr))
+    return PA_ERR_INVALID;
   if (batch == 0) return PA_OK;
   if (out == nullptr || q == nullptr || tables == nullptr || seq_lens == nullptr ||
-      !aligned16(q) || !aligned16(kv.k_pool) || !aligned16(kv.v_pool))
+      !aligned16(q) || !aligned16(out) || !aligned16(kv.k_pool) || !aligned16(kv.v_pool))
     return PA_ERR_INVALID;
   if (static_cast<int64_t>(max_seq_len) > static_cast<int64_t>(max_blocks) * kBlock)
     return PA_ERR_INVALID;
@@ -321,42 +654,65 @@ extern "C" pa_status pa_paged_attention_decode(pa_half* out, const pa_half* q, p
   const int p_max = max_seq_len == 0 ? 1 : (max_seq_len + partition_size - 1) / partition_size;
   if (p_max > 65535) return PA_ERR_INVALID;
   const int D = kv.head_dim;
-  float *ws_o = nullptr, *ws_m = nullptr, *ws_l = nullptr;
+  const bool worklist = work_items != nullptr;
+  const uint64_t need =
+      pa_decode_workspace_bytes(batch, num_q_heads, D, max_seq_len, partition_size);
+  if (p_max > 1 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+    return PA_ERR_INVALID;
+
+  DecodeArgs a;
+  a.q = reinterpret_cast<const f16*>(q);
+  a.kp = reinterpret_cast<const f16*>(kv.k_pool);
+  a.vp = reinterpret_cast<const f16*>(kv.v_pool);
+  a.tables = tables;
+  a.seq_lens = seq_lens;
+  a.max_blocks = max_blocks;
+  a.num_blocks = kv.num_blocks;
+  a.n_kv = kv.num_kv_heads;
+  a.G = G;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.part_blocks = part_blocks;
+  a.p_max = p_max;
+  a.out = reinterpret_cast<f16*>(out);
+  a.ws_o = nullptr;
+  a.ws_m = nullptr;
+  a.ws_l = nullptr;
   if (p_max > 1) {
-    const uint64_t need =
-        pa_decode_workspace_bytes(batch, num_q_heads, D, max_seq_len, partition_size);
-    if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
-      return PA_ERR_INVALID;
     const int64_t slots = static_cast<int64_t>(batch) * num_q_heads * p_max;
-    ws_o = static_cast<float*>(workspace);
-    ws_m = ws_o + slots * D;
-    ws_l = ws_m + slots;
+    a.ws_o = static_cast<f16*>(workspace);
+    a.ws_m = reinterpret_cast<float*>(a.ws_o + slots * D);
+    a.ws_l = a.ws_m + slots;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const float scale_log2 = scale * 1.4426950408889634f;
-  const dim3 grid(static_cast<uint32_t>(kv.num_kv_heads), static_cast<uint32_t>(batch),
-                  static_cast<uint32_t>(p_max));
-  const f16* qq = reinterpret_cast<const f16*>(q);
-  const f16* kp = reinterpret_cast<const f16*>(kv.k_pool);
-  const f16* vp = reinterpret_cast<const f16*>(kv.v_pool);
-  f16* oo = reinterpret_cast<f16*>(out);
-  if (D == 128)
-    decode_partition_kernel<128><<<grid, dim3(256), 0, s>>>(
-        qq, kp, vp, tables, seq_lens, max_blocks, kv.num_blocks, kv.num_kv_heads, G, scale_log2,
-        part_blocks, p_max, oo, ws_o, ws_m, ws_l);
-  else
-    decode_partition_kernel<64><<<grid, dim3(256), 0, s>>>(
-        qq, kp, vp, tables, seq_lens, max_blocks, kv.num_blocks, kv.num_kv_heads, G, scale_log2,
-        part_blocks, p_max, oo, ws_o, ws_m, ws_l);
+  if (worklist) {
+    if (n_items > 0) {
+      const size_t lds = static_cast<size_t>(kMergeSlots) * kDecodeWaves * G * (D + 4) * sizeof(float);
+      int wph = worklist_resident_wgs(D, G, lds) / kv.num_kv_heads;
+      if (wph < 1) wph = 1;
+      if (wph > n_items) wph = n_items;
+      if (wph > 65535) wph = 65535;
+      const dim3 grid(static_cast<uint32_t>(kv.num_kv_heads), static_cast<uint32_t>(wph));
+      if (D == 128)
+        decode_worklist_kernel<128><<<grid, dim3(kDecodeThreads), lds, s>>>(a, work_items, n_items);
+      else
+        decode_worklist_kernel<64><<<grid, dim3(kDecodeThreads), lds, s>>>(a, work_items, n_items);
+    }
+  } else {
+    const size_t lds = static_cast<size_t>(kDecodeWaves) * G * (D + 4) * sizeof(float);
+    const dim3 grid(static_cast<uint32_t>(kv.num_kv_heads), static_cast<uint32_t>(batch),
+                    static_cast<uint32_t>(p_max));
+    if (D == 128)
+      decode_partition_kernel<128><<<grid, dim3(kDecodeThreads), lds, s>>>(a);
+    else
+      decode_partition_kernel<64><<<grid, dim3(kDecodeThreads), lds, s>>>(a);
+  }
   if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   if (p_max > 1) {
-    const dim3 rgrid(static_cast<uint32_t>(num_q_heads), static_cast<uint32_t>(batch));
+    const dim3 rgrid(static_cast<uint32_t>(kv.num_kv_heads), static_cast<uint32_t>(batch));
     if (D == 128)
-      decode_reduce_kernel<128><<<rgrid, dim3(64), 0, s>>>(
-          seq_lens, max_blocks, num_q_heads, partition_size, p_max, ws_o, ws_m, ws_l, oo);
+      decode_reduce_kernel<128><<<rgrid, dim3(256), 0, s>>>(a);
     else
-      decode_reduce_kernel<64><<<rgrid, dim3(64), 0, s>>>(
-          seq_lens, max_blocks, num_q_heads, partition_size, p_max, ws_o, ws_m, ws_l, oo);
+      decode_reduce_kernel<64><<<rgrid, dim3(256), 0, s>>>(a);
   }
   return launch_status();
 }

@@ -42,6 +42,14 @@ __device__ __forceinline__ float wave_sum_xor16_32(float v) {
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Read a wave-uniform int32 through the scalar cache (s_load): it is counted
+// by lgkmcnt, so using it right away does not wait for the wave's in-flight
+// vector loads.  Only for memory no kernel writes while the reader runs.
+__device__ __forceinline__ int32_t scalar_load(const int32_t* p, int64_t i) {
+  typedef const int32_t __attribute__((address_space(4)))* const_i32_ptr;
+  return ((const_i32_ptr)p)[i];
+}
+
 inline pa_status launch_status() {
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }

@@ -38,10 +38,14 @@ class DecodeStepper:
         self.d_slots = [torch.empty(self.B, dtype=torch.int32, device=dev) for _ in range(depth)]
         self.d_tab = torch.empty((self.B, self.max_blocks), dtype=torch.int32, device=dev)
         self.d_len = torch.empty(self.B, dtype=torch.int32, device=dev)
+        p_cap = -(-self.max_len_cap // self.partition)
+        self.h_items = [torch.empty(self.B * p_cap, dtype=torch.int32, pin_memory=True)
+                        for _ in range(depth)]
+        self.d_items = torch.empty(self.B * p_cap, dtype=torch.int32, device=dev)
         self.done = [None] * depth
         self.ws_bytes = L.pa_decode_workspace_bytes(self.B, self.n_q, cache.d, self.max_len_cap,
                                                     self.partition)
-        self.workspace = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev)
+        self.workspace = torch.zeros(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev)
         self.out = torch.empty((self.B, self.n_q, cache.d), dtype=torch.float16, device=dev)
         self.i = 0
         self.last_lens: Optional[np.ndarray] = None
@@ -62,10 +66,12 @@ class DecodeStepper:
         if max_len > self.max_len_cap:
             raise ValueError("a request outgrew the stepper's max_len_cap")
         self.last_lens = len_np.copy()
+        n_items = len(L.pa_decode_work_items(len_np, self.partition, out=self.h_items[r].numpy()))
         with torch.cuda.stream(stream):
             self.d_slots[r].copy_(self.h_slots[r], non_blocking=True)
             self.d_tab.copy_(self.h_tab[r], non_blocking=True)
             self.d_len.copy_(self.h_len[r], non_blocking=True)
+            self.d_items[:n_items].copy_(self.h_items[r][:n_items], non_blocking=True)
             ev = torch.cuda.Event()
             ev.record(stream)
             self.done[r] = ev
@@ -80,7 +86,8 @@ class DecodeStepper:
                 events["decode"][0].record(stream)
             L.pa_paged_attention_decode(self.out, q, self.cache.kv, self.d_tab, self.max_blocks,
                                         self.d_len, self.B, self.n_q, self.scale, self.partition,
-                                        max_len, self.workspace, self.ws_bytes, stream)
+                                        max_len, self.d_items, n_items, self.workspace,
+                                        self.ws_bytes, stream)
             if events is not None:
                 events["decode"][1].record(stream)
         self.i += 1

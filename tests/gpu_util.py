@@ -20,7 +20,8 @@ def log(msg):
     sys.stdout.flush()
 
 
-def gpu_run(w, partition=512, fill=FILL, device="cuda:0", decode=True, prefill=True):
+def gpu_run(w, partition=512, fill=FILL, device="cuda:0", decode=True, prefill=True,
+            worklist=True):
     log(f"[gpu_run] {w.name}: blocks={w.num_blocks} B={w.batch} n_q={w.n_q} n_kv={w.n_kv} "
         f"d={w.d} partition={partition} prefill={w.prefill is not None}")
     cache = PagedKVCache(w.num_blocks, w.n_kv, w.d, w.free_order, device, fill_byte=fill)
@@ -33,7 +34,7 @@ def gpu_run(w, partition=512, fill=FILL, device="cuda:0", decode=True, prefill=T
     slots, copies = cache.append(w.step_ids, w.step_n_new, sk, sv)
     res = {"cache": cache, "step_slots": slots, "step_copies": copies}
     if decode and w.batch:
-        plan = DecodePlan(cache, w.decode_ids, w.n_q, w.scale, partition)
+        plan = DecodePlan(cache, w.decode_ids, w.n_q, w.scale, partition, worklist=worklist)
         q = torch.from_numpy(w.q).to(device)
         res["decode"] = plan.run(q).clone()
         res["plan"], res["q"] = plan, q

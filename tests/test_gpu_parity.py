@@ -44,14 +44,22 @@ def test_config_cache_and_decode(cfg):
 
 
 def test_config3_full_size_decode():
-    """The decode workload the benchmark times (split-K 512 + reduce), every
-    output element against the oracle."""
+    """The decode workload the benchmark times (split-K 512 + reduce, work-list
+    form), every output element against the oracle; the grid form and a
+    second launch must give bitwise the same result."""
     w = make_workload(3)
     st = oracle_run(w)
     res = gpu_run(w, partition=512)
     n = assert_pools_bit_exact(res["cache"], st)
     err = assert_close(res["decode"], decode_reference(w, st), "config 3 decode")
     log(f"config 3: {n} live slots bit-exact, decode max err {err:.2e}")
+    from pagedattention_block_paged_reshape_amd.cache import DecodePlan
+    grid = DecodePlan(res["cache"], w.decode_ids, w.n_q, w.scale, 512, worklist=False)
+    g_out = grid.run(res["q"]).clone()
+    again = res["plan"].run(res["q"]).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(g_out.view(torch.int16), res["decode"].view(torch.int16))
+    assert torch.equal(again.view(torch.int16), res["decode"].view(torch.int16))
 
 
 def test_config5_mixed_step():
@@ -74,11 +82,12 @@ def test_config5_mixed_step():
 RAGGED = [1, 2, 15, 16, 17, 31, 32, 33, 127, 511, 512, 513, 1000, 1537, 2049]
 
 
+@pytest.mark.parametrize("worklist", [True, False])
 @pytest.mark.parametrize("partition", [16, 32, 48, 256, 512, 4096])
-def test_decode_partition_sizes(partition):
+def test_decode_partition_sizes(partition, worklist):
     w = make_tiny_workload(RAGGED, n_q=32, n_kv=8, d=128, seed=21, dist="normal")
     st = oracle_run(w)
-    res = gpu_run(w, partition=partition)
+    res = gpu_run(w, partition=partition, worklist=worklist)
     assert_close(res["decode"], decode_reference(w, st), f"partition {partition}")
 
 
@@ -141,12 +150,17 @@ def test_shared_prefix_equals_private_copies_bitwise():
     assert_close(a["decode"], decode_reference(shared, st), "shared prefix")
 
 
-def test_decode_bad_table_entry_and_empty_request():
+@pytest.mark.parametrize("worklist", [True, False])
+def test_decode_bad_table_entry_and_empty_request(worklist):
     import pagedattention_block_paged_reshape_amd as pa
     w = make_tiny_workload([40, 40, 40], n_q=8, n_kv=2, d=128, seed=8, dist="normal")
     st = oracle_run(w)
-    res = gpu_run(w)
+    res = gpu_run(w, worklist=worklist)
     plan = res["plan"]
+    if worklist:   # the work list must cover the empty request too
+        items = pa.pa_decode_work_items([40, 40, 0], 512)
+        plan.items = torch.from_numpy(items.copy()).to("cuda:0")
+        plan.n_items = len(items)
     good = res["decode"].clone()
     plan.tables[1, 1] = w.num_blocks + 7          # out of range: request 1 must read NaN
     plan.lens[2] = 0                              # empty request: zeros
@@ -157,14 +171,12 @@ def test_decode_bad_table_entry_and_empty_request():
     assert torch.equal(out[0].view(torch.int16), good[0].view(torch.int16))
     assert_close(out[0:1], decode_reference(w, st)[0:1], "request next to a bad one")
     # host-side validation rejects bad geometry before any launch
-    with pytest.raises(pa.PaError):
-        pa.pa_paged_attention_decode(out, res["q"], plan.cache.kv, plan.tables, plan.max_blocks,
-                                     plan.lens, 3, 7, 0.1, 512, plan.max_len, plan.workspace,
-                                     plan.ws_bytes)
-    with pytest.raises(pa.PaError):
-        pa.pa_paged_attention_decode(out, res["q"], plan.cache.kv, plan.tables, plan.max_blocks,
-                                     plan.lens, 3, 8, 0.1, 24, plan.max_len, plan.workspace,
-                                     plan.ws_bytes)
+    for n_q, part in ((7, 512), (8, 24), (8, 8192)):
+        with pytest.raises(pa.PaError):
+            pa.pa_paged_attention_decode(out, res["q"], plan.cache.kv, plan.tables,
+                                         plan.max_blocks, plan.lens, 3, n_q, 0.1, part,
+                                         plan.max_len, plan.items, plan.n_items, plan.workspace,
+                                         plan.ws_bytes)
 
 
 def test_reshape_and_cache_skips_negative_and_out_of_range_slots():

@@ -204,3 +204,34 @@ def test_ragged_workload_tables_match_oracle():
             assert ref.append(op[1], op[2])[0] == s_setup
     assert ref.append(w.step_ids.tolist(), w.step_n_new.tolist())[0] == s_step
     pa.pa_pool_destroy(pool)
+
+
+@pytest.mark.parametrize("partition", [16, 48, 512, 4096])
+def test_decode_work_items_cover_every_unit_largest_first(partition):
+    rng = np.random.default_rng(partition)
+    lens = rng.integers(0, 5000, size=97).tolist() + [0, 1, 16, 17, partition, partition + 1]
+    items = pa.pa_decode_work_items(lens, partition)
+    pb = partition // 16
+    units = []
+    for b, L in enumerate(lens):
+        nb = -(-L // 16)
+        if L == 0:
+            units.append((b, 0, 0))
+        for p in range(-(-nb // pb)):
+            units.append((b, p, min(pb, nb - p * pb)))
+    got = [(int(x) >> 16, int(x) & 0xFFFF) for x in items]
+    assert sorted(got) == sorted((b, p) for b, p, _ in units)
+    size = {(b, p): s for b, p, s in units}
+    sizes = [size[u] for u in got]
+    assert sizes == sorted(sizes, reverse=True)
+    # ties keep (request, partition) order
+    for i in range(1, len(got)):
+        if sizes[i] == sizes[i - 1]:
+            assert got[i] > got[i - 1]
+
+
+def test_decode_work_items_errors():
+    with pytest.raises(pa.PaError):
+        pa.pa_decode_work_items([5, -1], 512)
+    with pytest.raises(pa.PaError):
+        pa.pa_decode_work_items([5], 24)
