@@ -30,8 +30,8 @@
  *     synchronise.  Arguments are validated on the host before any launch
  *     (PA_ERR_INVALID); a failed launch returns PA_ERR_HIP.
  *   - "fp16" means IEEE-754 binary16, passed as pa_half (its bit pattern).
- *   - block_size is fixed at PA_BLOCK_SIZE = 16 tokens ([ngrok] "usually 16
- *     tokens"; [yj] listing example).
+ *   - block_size is fixed at PA_BLOCK_SIZE = 16 tokens (the usual block size
+ *     per [ngrok] "PagedAttention"; [yj] listing example).
  *
  * Device pool layout (one pool per K and per V, one layer):
  *   K pool: [num_blocks][num_kv_heads][16][head_dim] fp16
