@@ -33,15 +33,18 @@
  *   - block_size is fixed at PA_BLOCK_SIZE = 16 tokens (the usual block size
  *     per [ngrok] "PagedAttention"; [yj] listing example).
  *
- * Device pool layout (one pool per K and per V, one layer):
- *   K pool: [num_blocks][num_kv_heads][16][head_dim] fp16
- *           slot s of block b, head h, dim c at ((b*H + h)*16 + s)*D + c
- *   V pool: [num_blocks][num_kv_heads][head_dim][16] fp16
- *           slot s of block b, head h, dim c at ((b*H + h)*D + c)*16 + s
- *   A (block, kv head) tile is 16*D*2 bytes contiguous in each pool (4 KiB at
- *   D = 128).  K keeps a token's row contiguous; V keeps each dimension's 16
- *   slots contiguous, so that both feed the matrix cores' operand registers
- *   directly.  A slot id is block*16 + offset.
+ * Device pool layout (one pool per K and per V, one layer): each pool is
+ * [num_blocks][num_kv_heads][tile], a tile holding the 16 slots x head_dim
+ * fp16 values of one (block, kv head), 16*D*2 bytes contiguous (4 KiB at
+ * D = 128).  Inside a tile the values are ordered the way the matrix cores
+ * consume them, so that every 16-byte-per-lane load of a 64-lane wavefront
+ * reads 1 KiB with lane i at bytes [16i, 16i + 16):
+ *   K tile [D/8][16][8]: slot s, dim c at (c/8)*128 + s*8 + c%8
+ *   V tile [D/32][4][16][2][4]: slot s, dim c at
+ *           (c/32)*512 + (s/4)*128 + (c%16)*8 + ((c/16)%2)*4 + s%4
+ * (offsets in fp16 elements within the tile; tile (b, h) starts at element
+ * (b*H + h)*16*D).  D must be a multiple of 32.  A slot id is block*16 +
+ * offset.
  */
 #ifndef PA_H_
 #define PA_H_

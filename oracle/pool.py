@@ -2,11 +2,13 @@
 
 The pool is preallocated once as fp16 arrays (youngju.dev blog, the
 PagedAttentionManager listing, which allocates K and V pools of the same shape
-up front).  This model stores them in the byte layout the C ABI documents so
-that device pools can be compared bit for bit:
+up front).  This model keeps both in plain logical order,
 
-    K pool: [num_blocks][n_kv][16][d]   (one token row of d values per slot)
-    V pool: [num_blocks][n_kv][d][16]   (one 16-slot column per dimension)
+    K pool, V pool: [num_blocks][n_kv][16][d]   (one token row of d values per slot)
+
+The device orders the values inside each (block, kv head) tile for its matrix
+cores; the tests map device pools back to this order (by the layout rule the
+C ABI header states) before comparing them bit for bit.
 
 Writing a token (the listing's ``append_token`` store into
 ``cache[block, slot]``) and a copy-on-write copy (media.tcdigital.jp, memory
@@ -24,7 +26,7 @@ class PoolModel:
     def __init__(self, num_blocks: int, n_kv: int, d: int, block_size: int = 16):
         self.num_blocks, self.n_kv, self.d, self.bs = num_blocks, n_kv, d, block_size
         self.k = np.zeros((num_blocks, n_kv, block_size, d), dtype=np.float16)
-        self.v = np.zeros((num_blocks, n_kv, d, block_size), dtype=np.float16)
+        self.v = np.zeros((num_blocks, n_kv, block_size, d), dtype=np.float16)
 
     def write(self, k_rows: np.ndarray, v_rows: np.ndarray, slots: Iterable[int]) -> None:
         """Token t goes to slot ``slots[t]`` = block * 16 + offset; a negative
@@ -35,7 +37,7 @@ class PoolModel:
                 continue
             blk, off = divmod(s, self.bs)
             self.k[blk, :, off, :] = k_rows[t]
-            self.v[blk, :, :, off] = v_rows[t]
+            self.v[blk, :, off, :] = v_rows[t]
 
     def write_bulk(self, k_rows: np.ndarray, v_rows: np.ndarray, slots) -> None:
         """Same stores as ``write`` with numpy fancy indexing (large setups)."""
@@ -44,13 +46,13 @@ class PoolModel:
         slots = slots[keep]
         blk, off = slots // self.bs, slots % self.bs
         self.k[blk, :, off, :] = k_rows[keep]
-        self.v[blk, :, :, off] = v_rows[keep]
+        self.v[blk, :, off, :] = v_rows[keep]
 
     def copy(self, copies: Iterable[Tuple[int, int, int]]) -> None:
         """Copy the first ``n`` slots of every KV head from ``src`` to ``dst``."""
         for src, dst, n in copies:
             self.k[dst, :, :n, :] = self.k[src, :, :n, :]
-            self.v[dst, :, :, :n] = self.v[src, :, :, :n]
+            self.v[dst, :, :n, :] = self.v[src, :, :n, :]
 
     def gather(self, table, length: int):
         """Logical K and V of one request, [length][n_kv][d] each, following
@@ -61,5 +63,5 @@ class PoolModel:
             blk = table[pos // self.bs]
             n = min(self.bs, length - pos)
             k[pos:pos + n] = self.k[blk, :, :n, :].transpose(1, 0, 2)
-            v[pos:pos + n] = self.v[blk, :, :, :n].transpose(2, 0, 1)
+            v[pos:pos + n] = self.v[blk, :, :n, :].transpose(1, 0, 2)
         return k, v

@@ -34,10 +34,10 @@ class PagedKVCache:
         self.d = int(head_dim)
         self.device = torch.device(device)
         self.pool = L.pa_pool_create(self.num_blocks, free_order)
-        shape_k = (self.num_blocks, self.n_kv, L.BLOCK_SIZE, self.d)
-        shape_v = (self.num_blocks, self.n_kv, self.d, L.BLOCK_SIZE)
-        self.k_pool = torch.empty(shape_k, dtype=torch.float16, device=self.device)
-        self.v_pool = torch.empty(shape_v, dtype=torch.float16, device=self.device)
+        # [block][kv head][tile of 16 slots x d values, in the library's operand order]
+        shape = (self.num_blocks, self.n_kv, L.BLOCK_SIZE * self.d)
+        self.k_pool = torch.empty(shape, dtype=torch.float16, device=self.device)
+        self.v_pool = torch.empty(shape, dtype=torch.float16, device=self.device)
         if fill_byte is not None:
             self.k_pool.view(torch.uint8).fill_(fill_byte)
             self.v_pool.view(torch.uint8).fill_(fill_byte)

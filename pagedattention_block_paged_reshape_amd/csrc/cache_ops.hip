@@ -7,13 +7,14 @@
 // shared block that diverges (media.tcdigital.jp, "memory sharing for
 // parallel sampling").  Both are bit copies.
 //
-// Pool layout (see include/pa.h): K [N][H][16][D], V [N][H][D][16].
+// Pool layout (see include/pa.h): [N][H][tile], tiles in MFMA operand order
+// (k_tile_off / v_tile_off).
 #include "pa_device.h"
 
 namespace pa {
 
-// One thread per (token, kv head, 8-dim chunk): a 16-byte K row chunk goes to
-// the slot's row; the matching V chunk is scattered into 8 slot columns.
+// One thread per (token, kv head, 8-dim chunk): the 8 K values are contiguous
+// in the tile (one 16-byte store); the 8 V values land 8 elements apart.
 template <int D>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const f16* __restrict__ k, const f16* __restrict__ v, const int32_t* __restrict__ slots,
@@ -34,15 +35,15 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   const int64_t src = (t * n_kv + h) * D + chunk * 8;
   const f16x8 kv = *reinterpret_cast<const f16x8*>(k + src);
   const f16x8 vv = *reinterpret_cast<const f16x8*>(v + src);
-  const int64_t tile = blk * n_kv + h;
-  *reinterpret_cast<f16x8*>(kp + (tile * kBlock + off) * D + chunk * 8) = kv;
-  f16* vcol = vp + (tile * D + chunk * 8) * kBlock + off;
+  const int64_t tile = (blk * n_kv + h) * (kBlock * D);
+  *reinterpret_cast<f16x8*>(kp + tile + k_tile_off(off, chunk * 8)) = kv;
+  f16* vt = vp + tile + v_tile_off(off, chunk * 8);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) vcol[e * kBlock] = vv[e];
+  for (int e = 0; e < 8; ++e) vt[e * 8] = vv[e];  // dims chunk*8 + e: same 16-dim half
 }
 
-// One workgroup per (copy, kv head): slots [0, n) of the K tile are a
-// contiguous prefix; in the V tile each dimension's first n slots are copied.
+// One workgroup per (copy, kv head): slots [0, n) of the K and V tiles, as
+// 16-byte K chunks and single V elements.
 template <int D>
 __global__ __launch_bounds__(256) void copy_blocks_kernel(const pa_copy* __restrict__ copies,
                                                           int32_t n_kv, int32_t num_blocks,
@@ -53,16 +54,15 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(const pa_copy* __restr
   if (c.src < 0 || c.src >= num_blocks || c.dst < 0 || c.dst >= num_blocks) return;
   if (c.n_slots <= 0 || c.n_slots > kBlock || c.src == c.dst) return;
   const int n = c.n_slots;
-  const int64_t st = static_cast<int64_t>(c.src) * n_kv + h;
-  const int64_t dt = static_cast<int64_t>(c.dst) * n_kv + h;
-  const f16x8* ks = reinterpret_cast<const f16x8*>(kp + st * kBlock * D);
-  f16x8* kd = reinterpret_cast<f16x8*>(kp + dt * kBlock * D);
-  for (int i = threadIdx.x; i < n * D / 8; i += blockDim.x) kd[i] = ks[i];
-  const f16* vs = vp + st * D * kBlock;
-  f16* vd = vp + dt * D * kBlock;
-  for (int i = threadIdx.x; i < D * n; i += blockDim.x) {
-    const int dim = i / n, s = i % n;
-    vd[dim * kBlock + s] = vs[dim * kBlock + s];
+  const int64_t st = (static_cast<int64_t>(c.src) * n_kv + h) * (kBlock * D);
+  const int64_t dt = (static_cast<int64_t>(c.dst) * n_kv + h) * (kBlock * D);
+  for (int i = threadIdx.x; i < n * (D / 8); i += blockDim.x) {
+    const int off = k_tile_off(i % n, (i / n) * 8);
+    *reinterpret_cast<f16x8*>(kp + dt + off) = *reinterpret_cast<const f16x8*>(kp + st + off);
+  }
+  for (int i = threadIdx.x; i < n * D; i += blockDim.x) {
+    const int off = v_tile_off(i % n, i / n);
+    vp[dt + off] = vp[st + off];
   }
 }
 

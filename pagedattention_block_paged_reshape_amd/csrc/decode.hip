@@ -56,6 +56,9 @@ namespace pa {
 #ifndef PA_MERGE_SLOTS
 #define PA_MERGE_SLOTS 2
 #endif
+#ifndef PA_WL_WAVES_PER_EU
+#define PA_WL_WAVES_PER_EU 2
+#endif
 constexpr int kDecodeWaves = PA_DECODE_WAVES;  // wavefronts per workgroup
 constexpr int kDecodeThreads = kDecodeWaves * kWave;
 constexpr int kMergeSlots = PA_MERGE_SLOTS;    // LDS merge slots of the work-list form
@@ -149,6 +152,14 @@ __device__ __forceinline__ Unit make_unit(const DecodeArgs& a, int b, int p, int
   const int kb_end = min(u.kb0 + a.part_blocks, (u.L + kBlock - 1) / kBlock);
   const int nb = max(kb_end - u.kb0, 0);
   u.cnt = nb > wave ? (nb - wave + kDecodeWaves - 1) / kDecodeWaves : 0;
+  // All of these are wave-uniform; saying so keeps the block loop's control
+  // flow and block addresses in scalar registers.
+  u.b = uniform(u.b);
+  u.p = uniform(u.p);
+  u.L = uniform(u.L);
+  u.n_parts = uniform(u.n_parts);
+  u.kb0 = uniform(u.kb0);
+  u.cnt = uniform(u.cnt);
   const int32_t* trow = a.tables + static_cast<int64_t>(b) * a.max_blocks;
   u.my_pb = 0;
   u.my_pb2 = 0;
@@ -182,19 +193,25 @@ __device__ __forceinline__ void load_q(const DecodeArgs& a, int g, int b, int la
 }
 
 // K and V tiles of physical block pb, kv head g, straight into MFMA operand
-// registers (K: 16 B per lane per K-step; V^T: 8 B per lane per dim tile).
+// registers.  The tiles are stored in operand order, so each load is 16 B
+// per lane with lane i on bytes [16i, 16i+16) of a 1 KiB span:
+//   K step kk: lane l gets K[slot l%16][dims kk*32 + 8*(l/16) .. +8];
+//   V pair cc: lane l gets V[slots 4*(l/16) .. +4][dim (2cc+h)*16 + l%16] for
+//   h = 0, 1, i.e. the A operands of dim tiles 2cc and 2cc+1.
 template <int D>
 __device__ __forceinline__ void load_block(const DecodeArgs& a, int g, int pb, int lane,
                                            f16x8* kd, f16x4* vd) {
-  const int col = lane & 15;
-  const int lg = lane >> 4;
-  const int64_t tile = static_cast<int64_t>(pb) * a.n_kv + g;
-  const f16* kt = a.kp + tile * (kBlock * D) + col * D + lg * 8;
-  const f16* vt = a.vp + tile * (kBlock * D) + col * kBlock + lg * 4;
+  const int64_t tile = (static_cast<int64_t>(pb) * a.n_kv + g) * (kBlock * D);  // uniform
+  const f16* kt = a.kp + tile + lane * 8;
+  const f16* vt = a.vp + tile + lane * 8;
 #pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk) kd[kk] = *reinterpret_cast<const f16x8*>(kt + kk * 32);
+  for (int kk = 0; kk < D / 32; ++kk) kd[kk] = *reinterpret_cast<const f16x8*>(kt + kk * 512);
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) vd[c] = *reinterpret_cast<const f16x4*>(vt + c * 16 * kBlock);
+  for (int cc = 0; cc < D / 32; ++cc) {
+    const f16x8 pair = *reinterpret_cast<const f16x8*>(vt + cc * 512);
+    vd[2 * cc] = f16x4{pair[0], pair[1], pair[2], pair[3]};
+    vd[2 * cc + 1] = f16x4{pair[4], pair[5], pair[6], pair[7]};
+  }
 }
 
 // Physical block behind the wave's i-th load: unit u's blocks first; past
@@ -206,9 +223,14 @@ __device__ __forceinline__ int unit_block(const Unit& u, int i) {
 }
 
 __device__ __forceinline__ int pick_block(const Unit& u, const Unit& nx, int i) {
-  if (i < u.cnt) return unit_block(u, i);
-  if (nx.cnt > 0) return unit_block(nx, 0);
-  return u.cnt > 0 ? unit_block(u, u.cnt - 1) : 0;
+  int pb;
+  if (i < u.cnt)
+    pb = unit_block(u, i);
+  else if (nx.cnt > 0)
+    pb = unit_block(nx, 0);
+  else
+    pb = u.cnt > 0 ? unit_block(u, u.cnt - 1) : 0;
+  return uniform(pb);
 }
 
 // The wavefront's pass over its blocks of unit u on kv head g.  On entry
@@ -383,6 +405,87 @@ __device__ __forceinline__ void merge_store(const DecodeArgs& a, const MergeSlot
   }
 }
 
+// Merge the partitions of each (request, query head): with M = max_p m_p
+// and w_p = l_p * 2^(m_p - M), out = sum_p w_p o_p / sum_p w_p, summed in
+// partition order.  One workgroup per (kv head, request); 32 lanes per query
+// head, each lane D/32 dims.  The kernel is latency-bound, so after reading
+// the request's length each lane requests the (o, m, l) of up to kChunk
+// partitions at once: a request of up to kChunk partitions costs two memory
+// round trips.  Longer ones take further chunks.  Requests that fit in one
+// partition were written by the partition kernel and are skipped.
+template <int D>
+__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
+  constexpr int PER = D / 32;
+  constexpr int kChunk = 8;
+  typedef _Float16 f16xP __attribute__((ext_vector_type(PER)));
+  const int g = blockIdx.x;
+  const int b = blockIdx.y;
+  const int G = a.G;
+  const int n_q = a.n_kv * G;
+  const int j = threadIdx.x & 31;
+  const int part_tokens = a.part_blocks * kBlock;
+  // partials of (b, g): [p_max][G][D] contiguous, (m, l) as [p_max][G]
+  const int64_t bg = (static_cast<int64_t>(b) * a.n_kv + g) * a.p_max * G;
+  int L = scalar_load(a.seq_lens, b);
+  if (L < 0) return;                                         // written as NaN already
+  if (L > a.max_blocks * kBlock) L = a.max_blocks * kBlock;  // partials are NaN-flagged
+  const int n_parts = min((L + part_tokens - 1) / part_tokens, a.p_max);
+  if (n_parts <= 1) return;
+  for (int h = threadIdx.x >> 5; h < G; h += blockDim.x >> 5) {
+    auto load_o = [&](int p) {
+      return *reinterpret_cast<const f16xP*>(a.ws_o + (bg + static_cast<int64_t>(p) * G + h) * D +
+                                             j * PER);
+    };
+    f16xP v[kChunk];
+    float mm[kChunk], ll[kChunk];
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      if (u < n_parts) {
+        v[u] = load_o(u);
+        mm[u] = a.ws_m[bg + u * G + h];
+        ll[u] = a.ws_l[bg + u * G + h];
+      }
+    }
+
+    float M = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u)
+      if (u < n_parts) M = fmaxf(M, mm[u]);
+    for (int p = kChunk; p < n_parts; ++p) M = fmaxf(M, a.ws_m[bg + p * G + h]);
+    float wsum = 0.0f;
+    float acc[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
+    for (int p0 = 0; p0 < n_parts; p0 += kChunk) {
+      if (p0 > 0) {
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u) {
+          if (p0 + u < n_parts) {
+            v[u] = load_o(p0 + u);
+            mm[u] = a.ws_m[bg + (p0 + u) * G + h];
+            ll[u] = a.ws_l[bg + (p0 + u) * G + h];
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) {
+        if (p0 + u < n_parts) {
+          const float w = ll[u] * exp2f(mm[u] - M);
+          wsum += w;
+#pragma unroll
+          for (int e = 0; e < PER; ++e) acc[e] += w * static_cast<float>(v[u][e]);
+        }
+      }
+    }
+    const float inv = 1.0f / wsum;
+    f16xP rr;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) rr[e] = static_cast<f16>(acc[e] * inv);
+    const int64_t qh = static_cast<int64_t>(b) * n_q + g * G + h;
+    *reinterpret_cast<f16xP*>(a.out + qh * D + j * PER) = rr;
+  }
+}
+
 // Grid form: one workgroup per (kv head, request, partition).
 template <int D>
 __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(DecodeArgs a) {
@@ -425,14 +528,16 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(Decode
 
 // Work-list form: gridDim.y resident workgroups per kv head walk `items`
 // ((request << 16) | partition, largest first) in a snake deal: in round r
-// workgroup y takes item r*wph + y, in reverse order on odd rounds, so every
-// workgroup gets a near-equal share of blocks and the small units come last.
+// workgroup y takes entry r*wph + y, reversed on odd rounds, which gives every
+// workgroup a near-equal share of blocks and leaves the smallest units for
+// last.  (Claiming the last rounds dynamically from a counter was measured
+// and gained nothing: HBM stays saturated while the faster workgroups drain.)
 // While a unit is computed the next unit's block ids are already loaded, and
 // its first block and query rows are in flight during the unit's epilogue.
 // LDS merge slots rotate over consecutive units so that a fast wavefront can
 // post the next unit while the last one of an earlier unit still merges.
 template <int D>
-__global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(PA_WL_WAVES_PER_EU)))
 void decode_worklist_kernel(DecodeArgs a, const int32_t* __restrict__ items, int32_t n_items) {
   constexpr int OROW = D + 4;
   const int g = blockIdx.x;
@@ -500,83 +605,6 @@ void decode_worklist_kernel(DecodeArgs a, const int32_t* __restrict__ items, int
   }
 }
 
-// Merge the partitions of each (request, query head): with M = max_p m_p and
-// w_p = l_p * 2^(m_p - M), out = sum_p w_p o_p / sum_p w_p.  One workgroup per
-// (kv head, request); the 32 lanes of head h load the (m, l) of up to 32
-// partitions at once and reduce them with shuffles, then each lane
-// accumulates D/32 dims over the partitions with 8 loads in flight at a time.
-// Requests that fit in one partition were written by the partition kernel
-// and are skipped.
-template <int D>
-__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
-  constexpr int PER = D / 32;
-  constexpr int UNROLL = 8;
-  typedef _Float16 f16xP __attribute__((ext_vector_type(PER)));
-  const int g = blockIdx.x;
-  const int b = blockIdx.y;
-  int L = a.seq_lens[b];
-  if (L < 0) return;                                         // written as NaN already
-  if (L > a.max_blocks * kBlock) L = a.max_blocks * kBlock;  // partials are NaN-flagged
-  const int part_tokens = a.part_blocks * kBlock;
-  const int n_parts = min((L + part_tokens - 1) / part_tokens, a.p_max);
-  if (n_parts <= 1) return;
-  const int G = a.G;
-  const int n_q = a.n_kv * G;
-  const int j = threadIdx.x & 31;
-  // partials of (b, g): [p_max][G][D] contiguous, (m, l) as [p_max][G]
-  const int64_t bg = (static_cast<int64_t>(b) * a.n_kv + g) * a.p_max * G;
-  for (int h = threadIdx.x >> 5; h < G; h += blockDim.x >> 5) {
-    const int64_t qh = static_cast<int64_t>(b) * n_q + g * G + h;
-    auto load_o = [&](int p) {
-      return *reinterpret_cast<const f16xP*>(a.ws_o + (bg + static_cast<int64_t>(p) * G + h) * D +
-                                             j * PER);
-    };
-    // the first partials' rows are requested together with the (m, l) loads
-    f16xP v[UNROLL];
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u)
-      if (u < n_parts) v[u] = load_o(u);
-    float M = -INFINITY;
-    for (int p0 = 0; p0 < n_parts; p0 += 32)
-      if (p0 + j < n_parts) M = fmaxf(M, a.ws_m[bg + (p0 + j) * G + h]);
-#pragma unroll
-    for (int sh = 1; sh < 32; sh <<= 1) M = fmaxf(M, __shfl_xor(M, sh, 32));
-    float wsum = 0.0f;
-    float acc[PER];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
-    for (int p0 = 0; p0 < n_parts; p0 += 32) {
-      const int np = min(32, n_parts - p0);
-      const int64_t sj = bg + (p0 + j) * G + h;
-      const float wj = j < np ? a.ws_l[sj] * exp2f(a.ws_m[sj] - M) : 0.0f;
-      float ws = wj;
-#pragma unroll
-      for (int sh = 1; sh < 32; sh <<= 1) ws += __shfl_xor(ws, sh, 32);
-      wsum += ws;
-      for (int u0 = 0; u0 < np; u0 += UNROLL) {
-        if (p0 + u0 > 0) {
-#pragma unroll
-          for (int u = 0; u < UNROLL; ++u)
-            if (u0 + u < np) v[u] = load_o(p0 + u0 + u);
-        }
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-          const float w = __shfl(wj, u0 + u, 32);
-          if (u0 + u < np) {
-#pragma unroll
-            for (int e = 0; e < PER; ++e) acc[e] += w * static_cast<float>(v[u][e]);
-          }
-        }
-      }
-    }
-    const float inv = 1.0f / wsum;
-    f16xP rr;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) rr[e] = static_cast<f16>(acc[e] * inv);
-    *reinterpret_cast<f16xP*>(a.out + qh * D + j * PER) = rr;
-  }
-}
-
 // Resident workgroups of the work-list kernel on the current device (cached
 // per head_dim and G; the dynamic LDS depends on G).
 static int worklist_resident_wgs(int D, int G, size_t lds) {
@@ -607,6 +635,7 @@ static int worklist_resident_wgs(int D, int G, size_t lds) {
 
 using namespace pa;
 
+
 extern "C" uint64_t pa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
                                               int32_t head_dim, int32_t max_seq_len,
                                               int32_t partition_size) {
@@ -617,9 +646,7 @@ extern "C" uint64_t pa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads
                              : (static_cast<uint64_t>(max_seq_len) + partition_size - 1) /
                                    partition_size;
   // fp16 normalised partial outputs, then fp32 running max and sum
-  const uint64_t partials =
-      parts > 1 ? static_cast<uint64_t>(batch) * num_q_heads * parts * (head_dim * 2 + 8) : 0;
-  return partials;
+  return parts > 1 ? static_cast<uint64_t>(batch) * num_q_heads * parts * (head_dim * 2 + 8) : 0;
 }
 
 extern "C" pa_status pa_paged_attention_decode(pa_half* out, const pa_half* q, pa_kv_view kv,

@@ -40,6 +40,17 @@ __device__ __forceinline__ float wave_sum_xor16_32(float v) {
   return v;
 }
 
+// Element offsets of (slot s, dim c) inside a (block, kv head) tile of the
+// pools (layout documented in include/pa.h): K as [D/8][16][8], V as
+// [D/32][4][16][2][4], so that 16-byte-per-lane loads of MFMA operands read
+// 1 KiB per wavefront with consecutive lanes on consecutive bytes.
+__host__ __device__ __forceinline__ int k_tile_off(int s, int c) {
+  return (c >> 3) * 128 + s * 8 + (c & 7);
+}
+__host__ __device__ __forceinline__ int v_tile_off(int s, int c) {
+  return (c >> 5) * 512 + (s >> 2) * 128 + (c & 15) * 8 + ((c >> 4) & 1) * 4 + (s & 3);
+}
+
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // Read a wave-uniform int32 through the scalar cache (s_load): it is counted

@@ -17,10 +17,11 @@
 //    16-wide MFMA tiles.  Grid = (kv head, query tile, key split);
 //    blockIdx.x = kv head puts each head on one XCD so that every query tile
 //    and split of that head shares one L2 for the same K/V blocks.
-//  * Keys advance 64 at a time (4 blocks).  The 4 K tiles ([16][D]) and 4 V
-//    tiles ([D][16]) are gathered through the table with 16-byte loads into
-//    registers one step ahead, then stored to LDS (rows padded so the MFMA
-//    operand reads are bank-conflict free) and shared by the 4 wavefronts.
+//  * Keys advance 64 at a time (4 blocks).  The 4 K tiles and 4 V tiles are
+//    gathered through the table with lane-contiguous 16-byte loads into
+//    registers one step ahead, then stored to LDS in logical order (K as
+//    [key][D], V^T as [D][key], rows padded so the MFMA operand reads are
+//    bank-conflict free) and shared by the 4 wavefronts.
 //  * S^T = K . Q^T (keys x M-rows, 16x16x32 f16 MFMA); online softmax in fp32
 //    base 2 per M-row; P^T goes straight from the score accumulators into the
 //    B operand of O^T += V^T . P^T.  Only the steps that cross the causal
@@ -141,13 +142,14 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
       const int64_t tile = (static_cast<int64_t>(pb) * n_kv + g) * (kBlock * D);
       rk[u] = *reinterpret_cast<const f16x8*>(kp + tile + within * 8);
       f16x8 vv = *reinterpret_cast<const f16x8*>(vp + tile + within * 8);
-      // V chunk = dim `within/2`, slots (within%2)*8 .. +8: zero slots past the end
-      const int slot0 = (within & 1) * 8;
-      const int valid = seq_end - (lb * kBlock + slot0);
-      if (valid < 8) {
+      // V chunk `within` = two dims' values for slots 4q .. 4q+3 (tile order
+      // [D/32][4][16][2][4]): zero the slots past the sequence's end
+      const int q4 = ((within >> 4) & 3) * 4;
+      const int valid = seq_end - (lb * kBlock + q4);
+      if (valid < 4) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (e >= valid) vv[e] = static_cast<f16>(0.0f);
+          if ((e & 3) >= valid) vv[e] = static_cast<f16>(0.0f);
       }
       rv[u] = vv;
     }
@@ -158,12 +160,16 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
       const int ci = threadIdx.x + kPfThreads * u;
       const int bi = ci / (kBlock * D / 8);
       const int within = ci % (kBlock * D / 8);
-      const int key = bi * kBlock + within / (D / 8);
-      const int d8 = within % (D / 8);
+      // K chunk `within` = dims (within/16)*8 .. +8 of slot within%16
+      const int key = bi * kBlock + (within & 15);
+      const int d8 = within >> 4;
       *reinterpret_cast<f16x8*>(sk + key * KROW + d8 * 8) = rk[u];
-      const int dim = within / 2;
-      const int kslot = bi * kBlock + (within & 1) * 8;
-      *reinterpret_cast<f16x8*>(sv + dim * VROW + kslot) = rv[u];
+      // V chunk `within` = dims c2*32 + dd and c2*32 + 16 + dd, slots 4q .. +4
+      const int dim = (within >> 6) * 32 + (within & 15);
+      const int kslot = bi * kBlock + ((within >> 4) & 3) * 4;
+      const f16x8 vv = rv[u];
+      *reinterpret_cast<f16x4*>(sv + dim * VROW + kslot) = f16x4{vv[0], vv[1], vv[2], vv[3]};
+      *reinterpret_cast<f16x4*>(sv + (dim + 16) * VROW + kslot) = f16x4{vv[4], vv[5], vv[6], vv[7]};
     }
   };
 

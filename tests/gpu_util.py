@@ -79,11 +79,24 @@ def valid_slots(st):
     return n
 
 
+def pools_to_logical(kd, vd, d):
+    """Device pools ([N][H][tile], any dtype of 2-byte elements) in logical
+    [N][H][16][d] order, by the tile layout include/pa.h states:
+    K tile [d/8][16][8] (dim chunk, slot, dim in chunk);
+    V tile [d/32][4][16][2][4] (32-dim group, slot quad, dim % 16, 16-dim half,
+    slot in quad)."""
+    n, h = kd.shape[0], kd.shape[1]
+    k = kd.reshape(n, h, d // 8, 16, 8).transpose(0, 1, 3, 2, 4).reshape(n, h, 16, d)
+    v = vd.reshape(n, h, d // 32, 4, 16, 2, 4).transpose(0, 1, 3, 6, 2, 5, 4).reshape(n, h, 16, d)
+    return k, v
+
+
 def assert_pools_bit_exact(cache, st, fill=FILL):
     """Valid slots of live blocks equal the oracle pool bit for bit; blocks
     no request holds still carry the fill pattern."""
-    kd = cache.k_pool.cpu().numpy().view(np.uint16)
-    vd = cache.v_pool.cpu().numpy().view(np.uint16)
+    kraw = cache.k_pool.cpu().numpy().view(np.uint16)
+    vraw = cache.v_pool.cpu().numpy().view(np.uint16)
+    kd, vd = pools_to_logical(kraw, vraw, cache.d)
     ko = st.pool.k.view(np.uint16)
     vo = st.pool.v.view(np.uint16)
     nvalid = valid_slots(st)
@@ -91,11 +104,11 @@ def assert_pools_bit_exact(cache, st, fill=FILL):
     k_dev = kd.transpose(0, 2, 1, 3)[mask]
     k_ref = ko.transpose(0, 2, 1, 3)[mask]
     assert np.array_equal(k_dev, k_ref), "K pool differs from the oracle"
-    v_dev = vd.transpose(0, 3, 1, 2)[mask]
-    v_ref = vo.transpose(0, 3, 1, 2)[mask]
+    v_dev = vd.transpose(0, 2, 1, 3)[mask]
+    v_ref = vo.transpose(0, 2, 1, 3)[mask]
     assert np.array_equal(v_dev, v_ref), "V pool differs from the oracle"
     pattern = np.uint16(fill | (fill << 8))
     untouched = nvalid == 0
-    assert (kd[untouched] == pattern).all(), "a block no request holds was written (K)"
-    assert (vd[untouched] == pattern).all(), "a block no request holds was written (V)"
+    assert (kraw[untouched] == pattern).all(), "a block no request holds was written (K)"
+    assert (vraw[untouched] == pattern).all(), "a block no request holds was written (V)"
     return int(mask.sum())

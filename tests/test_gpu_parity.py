@@ -9,6 +9,7 @@ import pytest
 import torch
 
 from gpu_util import (ATOL, FILL, RTOL, assert_close, assert_pools_bit_exact, gpu_run, log,
+                      pools_to_logical,
                       oracle_run)
 from oracle import decode_attention_one, decode_reference, prefill_reference
 from synth import make_mixed_workload, make_tiny_workload, make_workload
@@ -44,7 +45,7 @@ def test_config_cache_and_decode(cfg):
 
 
 def test_config3_full_size_decode():
-    """The decode workload the benchmark times (split-K 512 + reduce, work-list
+    """The decode workload the benchmark times (split-K 512 + merge, work-list
     form), every output element against the oracle; the grid form and a
     second launch must give bitwise the same result."""
     w = make_workload(3)
@@ -188,15 +189,15 @@ def test_reshape_and_cache_skips_negative_and_out_of_range_slots():
     slots = torch.tensor([5, -1, 4 * 16 + 3], dtype=torch.int32, device="cuda:0")
     pa.pa_reshape_and_cache(k, v, slots, 3, cache.kv)
     torch.cuda.synchronize()
-    kp = cache.k_pool.cpu()
-    vp = cache.v_pool.cpu()
-    assert torch.equal(kp[0, :, 5, :], k[0].cpu())
-    assert torch.equal(vp[0, :, :, 5], v[0].cpu())
-    written = torch.zeros(4, 16, dtype=torch.bool)
+    kl, vl = pools_to_logical(cache.k_pool.cpu().numpy(), cache.v_pool.cpu().numpy(), 64)
+    assert np.array_equal(kl[0, :, 5, :], k[0].cpu().numpy())
+    assert np.array_equal(vl[0, :, 5, :], v[0].cpu().numpy())
+    written = np.zeros((4, 16), dtype=bool)
     written[0, 5] = True
-    pattern = FILL | (FILL << 8)
-    kk = kp.view(torch.int16).permute(0, 2, 1, 3)
-    assert (kk[~written] == torch.tensor(pattern).to(torch.int16)).all()
+    pattern = np.uint16(FILL | (FILL << 8))
+    for pool in (kl, vl):
+        rest = pool.view(np.uint16).transpose(0, 2, 1, 3)[~written]
+        assert (rest == pattern).all()
 
 
 # ---------------------------------------------------------------- prefill

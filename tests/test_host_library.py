@@ -235,3 +235,21 @@ def test_decode_work_items_errors():
         pa.pa_decode_work_items([5, -1], 512)
     with pytest.raises(pa.PaError):
         pa.pa_decode_work_items([5], 24)
+
+
+def test_tile_layout_converter_matches_the_header_formulas():
+    """The tests read device pools through gpu_util.pools_to_logical; check it
+    against the per-element offsets include/pa.h states for both tiles."""
+    gpu_util = pytest.importorskip("gpu_util")
+    for d in (64, 128):
+        kraw = np.full((1, 1, 16 * d), -1, dtype=np.int32)
+        vraw = np.full((1, 1, 16 * d), -1, dtype=np.int32)
+        for s in range(16):
+            for c in range(d):
+                kraw[0, 0, (c // 8) * 128 + s * 8 + c % 8] = s * 1000 + c
+                vraw[0, 0, (c // 32) * 512 + (s // 4) * 128 + (c % 16) * 8
+                     + ((c // 16) % 2) * 4 + s % 4] = s * 1000 + c
+        assert (kraw >= 0).all() and (vraw >= 0).all()      # both maps are onto
+        k, v = gpu_util.pools_to_logical(kraw, vraw, d)
+        want = np.arange(16)[:, None] * 1000 + np.arange(d)[None, :]
+        assert np.array_equal(k[0, 0], want) and np.array_equal(v[0, 0], want)
