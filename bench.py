@@ -113,6 +113,123 @@ def cpu_baseline(w, budget_s: float, steps_done: int):
     }
 
 
+def prefill_flops(q_start: int, chunk_len: int, n_q: int, d: int) -> int:
+    """Matrix-core flops of one causal chunk: row r sees q_start + r + 1 keys;
+    per (row, head, key) 2*d for q.k and 2*d for p.v."""
+    pairs = chunk_len * q_start + chunk_len * (chunk_len + 1) // 2
+    return 4 * d * n_q * pairs
+
+
+def cpu_prefill_baseline(w, budget_s: float):
+    """The fp64 oracle's causal chunk attention on a bounded sample of the
+    same chunk: all 512 rows for as many query heads as the budget allows."""
+    from oracle import prefill_reference, run_setup, run_step
+    log("[bench] cpu_baseline: building the oracle's pool model (not timed)")
+    st = run_setup(w)
+    run_step(w, st)
+    pf = w.prefill
+    t0, c0 = time.perf_counter(), time.process_time()
+    heads = 0
+    while True:
+        prefill_reference(w, st, heads=[heads % w.n_q])
+        heads += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    cpu = time.process_time() - c0
+    flops = prefill_flops(pf.q_start, pf.chunk_len, 1, w.d) * heads
+    return {
+        "value": flops / el / 1e12,
+        "unit": "TFLOP/s",
+        "cores": max(1, int(round(cpu / el))),
+        "kind": "oracle",
+        "sample": f"{heads} single-head passes (cycling over the chunk's {w.n_q} query heads; all {pf.chunk_len} rows, "
+                  f"{pf.q_start + pf.chunk_len} keys each) in {el:.1f} s wall, "
+                  f"cpu/wall = {cpu / el:.2f}",
+    }
+
+
+def bench_prefill(args):
+    """Causal chunked prefill over the paged cache: the 512-token chunk at
+    offset 49,488 of a 50,000-token prompt (32/8 heads, head_dim 128)."""
+    import torch
+    from synth import make_workload
+    from pagedattention_block_paged_reshape_amd.cache import (PagedKVCache, PrefillPlan,
+                                                              run_program)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("[bench] generating workload 5")
+    w = make_workload("5")
+    pf = w.prefill
+    cache = PagedKVCache(w.num_blocks, w.n_kv, w.d, w.free_order, dev)
+    dk = torch.from_numpy(w.setup_k).to(dev)
+    dv = torch.from_numpy(w.setup_v).to(dev)
+    run_program(cache, w.setup, dk, dv)
+    del dk, dv
+    cache.append(w.step_ids, w.step_n_new, torch.from_numpy(w.step_k).to(dev),
+                 torch.from_numpy(w.step_v).to(dev))
+    plan = PrefillPlan(cache, pf.seq_id, pf.q_start, pf.chunk_len, w.n_q, w.scale)
+    q = torch.from_numpy(pf.q).to(dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        plan.run(q, stream)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record(stream)
+        plan.run(q, stream)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    flops = prefill_flops(pf.q_start, pf.chunk_len, w.n_q, w.d)
+    achieved = flops / (ms.mean() * 1e-3) / 1e12
+    log(f"[bench] prefill launch mean {ms.mean() * 1e3:.1f} us (p50 {np.median(ms) * 1e3:.1f}); "
+        f"{flops / 1e9:.1f} GFLOP -> {achieved:.1f} TFLOP/s")
+    result = {
+        "metric": "paged prefill chunk attention TFLOP/s (% of fp16 MFMA peak)",
+        "value": round(flops * args.steps / wall / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"config 5 chunk ({w.name}): causal chunk of {pf.chunk_len} query rows "
+                        f"at offset {pf.q_start} of a {pf.q_start + pf.chunk_len}-token prompt, "
+                        f"{w.n_q}/{w.n_kv} heads, head_dim {w.d}, block 16, pool "
+                        f"{w.num_blocks} blocks scattered",
+            "chunk": pf.chunk_len,
+            "q_start": pf.q_start,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": MFMA_F16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "pa_paged_attention_prefill (prefill_chunk_kernel + prefill_reduce_kernel)",
+            "algorithmic_flops_per_launch": flops,
+            "launch_us_mean": round(float(ms.mean()) * 1e3, 2),
+            "launch_us_p50": round(float(np.median(ms)) * 1e3, 2),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        del cache, plan
+        torch.cuda.empty_cache()
+        result["cpu_baseline"] = cpu_prefill_baseline(w, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
 def copy_calibration(nbytes: int, reps: int):
     """A plain device copy of known size (for scaling HBM byte counters)."""
     import torch
@@ -136,6 +253,8 @@ def main():
     ap.add_argument("--flush-mb", type=int, default=0,
                     help="write this many MiB between steps to evict L2/MALL")
     ap.add_argument("--copy-calibration-mb", type=int, default=0)
+    ap.add_argument("--prefill", action="store_true",
+                    help="time the causal prefill chunk of workload 5 instead of decode")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -147,6 +266,9 @@ def main():
     import torch
     if args.copy_calibration_mb:
         copy_calibration(args.copy_calibration_mb << 20, 5)
+        return
+    if args.prefill:
+        bench_prefill(args)
         return
 
     from synth import make_workload

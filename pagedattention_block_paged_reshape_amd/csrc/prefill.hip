@@ -198,39 +198,48 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
       }
     }
 
-    // mask only where the step crosses the diagonal of this tile
-    const bool diag = key0 + kPfKeys - 1 > q_start + r0;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) s[mt][nt] *= scale_log2;
+    if (key0 + kPfKeys - 1 > q_start + r0) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int limit = q_start + min(mrow_r[nt], chunk_len - 1);  // last key allowed
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (key0 + mt * 16 + 4 * lg + j > limit) s[mt][nt][j] = -INFINITY;
+      }
+    }
     f16x8 pb8[2][2];  // [k-step of PV][n-tile]
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      const int limit = q_start + min(mrow_r[nt], chunk_len - 1);  // last key allowed
       float mloc = -INFINITY;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float x = s[mt][nt][j] * scale_log2;
-          if (diag && key0 + mt * 16 + 4 * lg + j > limit) x = -INFINITY;
-          s[mt][nt][j] = x;
-          mloc = fmaxf(mloc, x);
-        }
+        for (int j = 0; j < 4; ++j) mloc = fmaxf(mloc, s[mt][nt][j]);
       mloc = wave_max_xor16_32(mloc);
       const float m_new = fmaxf(m_run[nt], mloc);
       const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-      const float alpha = exp2f(m_run[nt] - m_use);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_use);
       float psum = 0.0f;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const f16 ph = static_cast<f16>(exp2f(s[mt][nt][j] - m_use));
+          const f16 ph = static_cast<f16>(__builtin_amdgcn_exp2f(s[mt][nt][j] - m_use));
           psum += static_cast<float>(ph);
           pb8[mt >> 1][nt][(mt & 1) * 4 + j] = ph;
         }
       l_run[nt] = l_run[nt] * alpha + psum;
       m_run[nt] = m_new;
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt][nt] *= alpha;
+        for (int dt = 0; dt < DT; ++dt) o[dt][nt] *= alpha;
+      }
     }
 
     // O^T[dim][M-row] += V^T[dim][key] . P^T[key][M-row]
