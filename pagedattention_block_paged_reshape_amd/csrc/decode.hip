@@ -273,12 +273,13 @@ __device__ __forceinline__ void run_unit(const DecodeArgs& a, int g, int wave, i
     }
     mloc = wave_max_xor16_32(mloc);
     const float m_new = fmaxf(st.m, mloc);
-    const float alpha = exp2f(st.m - m_new);
+    // hardware 2^x: results below 2^-126 flush to 0, which softmax ignores
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
     f16x4 pf;
     float psum = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const f16 ph = static_cast<f16>(exp2f(sv[j] - m_new));
+      const f16 ph = static_cast<f16>(__builtin_amdgcn_exp2f(sv[j] - m_new));
       pf[j] = ph;
       psum += static_cast<float>(ph);
     }
