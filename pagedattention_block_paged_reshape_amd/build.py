@@ -31,9 +31,11 @@ HIPCC_FLAGS = [
     "-munsafe-fp-atomics",
 ]
 GXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
-# Per-file extras: the decode kernel keeps its MFMA accumulators in VGPRs,
-# which it rescales with ordinary VALU ops every block (no AGPR round trips).
-EXTRA_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-file extras: the attention kernels keep their MFMA accumulators in
+# VGPRs, which they rescale with ordinary VALU ops (no AGPR round trips); for
+# the prefill kernel this also fits two wavefronts per SIMD.
+EXTRA_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc() -> str:

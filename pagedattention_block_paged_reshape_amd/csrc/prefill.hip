@@ -198,10 +198,8 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
       }
     }
 
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) s[mt][nt] *= scale_log2;
+    // causal mask, on the raw scores, only where the step crosses the
+    // diagonal of this tile (a uniform branch: most steps skip it)
     if (key0 + kPfKeys - 1 > q_start + r0) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
@@ -222,17 +220,19 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) mloc = fmaxf(mloc, s[mt][nt][j]);
       mloc = wave_max_xor16_32(mloc);
-      const float m_new = fmaxf(m_run[nt], mloc);
+      // running max in base-2 units (scale_log2 > 0, so max(s) * c = max(s * c))
+      const float m_new = fmaxf(m_run[nt], mloc * scale_log2);
       const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+      // hardware 2^x: results below 2^-126 flush to 0, which softmax ignores
       const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_use);
       float psum = 0.0f;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const f16 ph = static_cast<f16>(__builtin_amdgcn_exp2f(s[mt][nt][j] - m_use));
-          psum += static_cast<float>(ph);
-          pb8[mt >> 1][nt][(mt & 1) * 4 + j] = ph;
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[mt][nt][j], scale_log2, -m_use));
+          psum += p;
+          pb8[mt >> 1][nt][(mt & 1) * 4 + j] = static_cast<f16>(p);
         }
       l_run[nt] = l_run[nt] * alpha + psum;
       m_run[nt] = m_new;
