@@ -236,3 +236,42 @@ def test_prefill_last_row_matches_decode_kernel():
     a = res["prefill"][-1].float().cpu().numpy()
     b = dec[0].float().cpu().numpy()
     assert np.allclose(a, b, rtol=RTOL, atol=ATOL)
+
+
+@pytest.mark.parametrize("q_start,chunk", [(0, 40), (4093, 512)])   # one split / several
+def test_prefill_bad_table_entry_reads_nan_and_empty_chunk_is_a_noop(q_start, chunk):
+    """A table entry outside the pool makes the chunk's output NaN (no
+    out-of-bounds read); a chunk of length 0 launches nothing and leaves the
+    output untouched; bad geometry is rejected on the host."""
+    import pagedattention_block_paged_reshape_amd as pa
+    w = make_mixed_workload([], q_start, chunk, n_q=32, n_kv=8, d=128, seed=21)
+    res = gpu_run(w, decode=False)
+    pp, qc = res["pplan"], res["qc"]
+    pp.table[0] = w.num_blocks + 3            # logical block 0: every row attends key 0
+    out = pp.run(qc).clone()
+    torch.cuda.synchronize()
+    assert torch.isnan(out.float()).all()
+    sentinel = torch.full_like(out, 7.0)
+    pa.pa_paged_attention_prefill(sentinel, qc, pp.cache.kv, pp.table, pp.table_len, pp.q_start,
+                                  0, pp.n_q, pp.scale, pp.workspace, pp.ws_bytes)
+    torch.cuda.synchronize()
+    assert (sentinel.float() == 7.0).all()
+    for n_q, q0, c in ((30, pp.q_start, pp.chunk_len),                 # 30 % 8 != 0
+                       (pp.n_q, pp.q_start, pp.table_len * 16 + 1),    # past the table
+                       (pp.n_q, -1, pp.chunk_len)):
+        with pytest.raises(pa.PaError):
+            pa.pa_paged_attention_prefill(out, qc, pp.cache.kv, pp.table, pp.table_len, q0, c,
+                                          n_q, pp.scale, pp.workspace, pp.ws_bytes)
+
+
+def test_decode_empty_batch_is_a_noop():
+    import pagedattention_block_paged_reshape_amd as pa
+    w = make_tiny_workload([20], n_q=8, n_kv=2, d=128, seed=5, dist="normal")
+    res = gpu_run(w)
+    plan = res["plan"]
+    sentinel = torch.full_like(res["decode"], 3.0)
+    pa.pa_paged_attention_decode(sentinel, res["q"], plan.cache.kv, plan.tables, plan.max_blocks,
+                                 plan.lens, 0, w.n_q, plan.scale, 512, plan.max_len, None, 0,
+                                 plan.workspace, plan.ws_bytes)
+    torch.cuda.synchronize()
+    assert (sentinel.float() == 3.0).all()
