@@ -251,7 +251,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush-mb", type=int, default=0,
-                    help="write this many MiB between steps to evict L2/MALL")
+                    help="read this many MiB between steps to evict L2/MALL (a read leaves "
+                         "no dirty lines behind to be written back during the next step)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0)
     ap.add_argument("--prefill", action="store_true",
                     help="time the causal prefill chunk of workload 5 instead of decode")
@@ -280,7 +281,13 @@ def main():
     log(f"[bench] generating workload {args.config}")
     w = make_workload(args.config)
     total_steps = args.warmup + args.steps
-    cache = PagedKVCache(w.num_blocks, w.n_kv, w.d, w.free_order, dev)
+    # room for the timed steps' appends (one token per request per step, plus
+    # a copy-on-write per request): extra blocks go to the bottom of the free
+    # stack, so the workload's own allocations are unchanged
+    extra = w.batch * (total_steps // 16 + 2)
+    free_order = np.concatenate([np.arange(w.num_blocks, w.num_blocks + extra, dtype=np.int32),
+                                 np.asarray(w.free_order, dtype=np.int32)])
+    cache = PagedKVCache(w.num_blocks + extra, w.n_kv, w.d, free_order, dev)
     log("[bench] uploading and storing the cached K/V through reshape_and_cache")
     dk = torch.from_numpy(w.setup_k).to(dev)
     dv = torch.from_numpy(w.setup_v).to(dev)
@@ -295,7 +302,7 @@ def main():
     stream = torch.cuda.current_stream(dev)
     flush = None
     if args.flush_mb:
-        flush = torch.empty(args.flush_mb << 20, dtype=torch.uint8, device=dev)
+        flush = torch.ones((args.flush_mb << 20) // 4, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
     log(f"[bench] warmup {args.warmup} steps")
@@ -312,7 +319,7 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         if flush is not None:
-            flush.fill_(i & 0xFF)
+            flush_sink = flush.sum()
         stepper.step(q, step_k, step_v, stream, events=ev[i])
         bytes_per_step.append(algorithmic_decode_bytes(stepper.last_lens, w.n_q, w.n_kv, w.d))
     torch.cuda.synchronize()
@@ -343,7 +350,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"config {args.config} ({w.name}): B={w.batch}, {w.n_q}/{w.n_kv} heads, "
-                        f"head_dim {w.d}, block 16, pool {w.num_blocks} blocks scattered, "
+                        f"head_dim {w.d}, block 16, pool {w.num_blocks} blocks scattered (+{extra} spare), "
                         f"split-K partition {args.partition} + reduce",
             "batch": w.batch,
             "mean_context": round(float(np.mean(stepper.last_lens)), 1),
