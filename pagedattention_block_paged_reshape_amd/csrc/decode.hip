@@ -46,6 +46,8 @@
 //    partial plus fp32 (max, sum), merged by the reduce kernel.
 #include <math.h>
 
+#include <algorithm>
+
 #include "pa_device.h"
 
 namespace pa {
@@ -64,6 +66,7 @@ constexpr int kDecodeThreads = kDecodeWaves * kWave;
 constexpr int kMergeSlots = PA_MERGE_SLOTS;    // LDS merge slots of the work-list form
 constexpr int kMaxWaveBlocks = 128;            // block ids a wavefront holds (2 per lane)
 constexpr int kSpinLimit = 1 << 22;  // safety bound on the LDS slot wait
+constexpr size_t kResultRingBytes = 16384;  // LDS for buffered unit results (work-list form)
 
 struct DecodeArgs {
   const f16* q;
@@ -355,14 +358,14 @@ __device__ __forceinline__ bool post_state(const MergeSlot<D>& ms, const WaveSta
   return arrived == kDecodeWaves - 1;
 }
 
-// Merge the 4 posted states of unit (g, b, p) in fixed wave order and store:
-// each lane produces 8 consecutive dims of one head (one 16-byte store).
-template <int D>
-__device__ __forceinline__ void merge_store(const DecodeArgs& a, const MergeSlot<D>& ms, int g,
-                                            int b, int p, int L, int n_parts, int lane) {
+// Merge the posted states of a unit in fixed wave order: each lane produces
+// 8 consecutive dims of one head and hands them, with the head's running max
+// and sum, to emit(h, d0, r, m, l).  An empty request reads as zeros, a
+// flagged one as NaN.
+template <int D, typename Emit>
+__device__ __forceinline__ void merge_unit(const MergeSlot<D>& ms, int G, int L, int lane,
+                                           Emit emit) {
   constexpr int OROW = D + 4;
-  const int G = a.G;
-  const int n_q = a.n_kv * G;
   const bool any_bad =
       __hip_atomic_load(ms.bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
   for (int idx = lane; idx < G * (D / 8); idx += kWave) {
@@ -383,7 +386,6 @@ __device__ __forceinline__ void merge_store(const DecodeArgs& a, const MergeSlot
         a1 += e * *reinterpret_cast<const f32x4*>(row + 4);
       }
     }
-    // an empty request reads as zeros; a flagged one as NaN
     const float inv = any_bad ? __builtin_nanf("") : (L > 0 ? 1.0f / wsum : 0.0f);
     f16x8 r;
 #pragma unroll
@@ -391,19 +393,37 @@ __device__ __forceinline__ void merge_store(const DecodeArgs& a, const MergeSlot
       r[k] = static_cast<f16>(a0[k] * inv);
       r[k + 4] = static_cast<f16>(a1[k] * inv);
     }
-    const int64_t qh = static_cast<int64_t>(b) * n_q + g * G + h;
-    if (n_parts <= 1) {
-      *reinterpret_cast<f16x8*>(a.out + qh * D + d0) = r;
-    } else {
-      // partials of one unit are contiguous: [B][n_kv][p_max][G][D]
-      const int64_t slot = ((static_cast<int64_t>(b) * a.n_kv + g) * a.p_max + p) * G + h;
-      *reinterpret_cast<f16x8*>(a.ws_o + slot * D + d0) = r;
-      if (d0 == 0) {
-        a.ws_m[slot] = any_bad ? __builtin_nanf("") : M;
-        a.ws_l[slot] = wsum;
-      }
+    emit(h, d0, r, any_bad ? __builtin_nanf("") : M, wsum);
+  }
+}
+
+// Global destination of a unit's merged rows: the request's output rows if
+// it has one partition, else its partial slot ([B][n_kv][p_max][G][D] fp16,
+// (m, l) as [B][n_kv][p_max][G] fp32).
+template <int D>
+__device__ __forceinline__ void store_rows(const DecodeArgs& a, int g, int b, int p,
+                                           int n_parts, int h, int d0, f16x8 r, float m,
+                                           float l) {
+  const int G = a.G;
+  if (n_parts <= 1) {
+    const int64_t qh = static_cast<int64_t>(b) * a.n_kv * G + g * G + h;
+    *reinterpret_cast<f16x8*>(a.out + qh * D + d0) = r;
+  } else {
+    const int64_t slot = ((static_cast<int64_t>(b) * a.n_kv + g) * a.p_max + p) * G + h;
+    *reinterpret_cast<f16x8*>(a.ws_o + slot * D + d0) = r;
+    if (d0 == 0) {
+      a.ws_m[slot] = m;
+      a.ws_l[slot] = l;
     }
   }
+}
+
+template <int D>
+__device__ __forceinline__ void merge_store(const DecodeArgs& a, const MergeSlot<D>& ms, int g,
+                                            int b, int p, int L, int n_parts, int lane) {
+  merge_unit<D>(ms, a.G, L, lane, [&](int h, int d0, f16x8 r, float m, float l) {
+    store_rows<D>(a, g, b, p, n_parts, h, d0, r, m, l);
+  });
 }
 
 // Merge the partitions of each (request, query head): with M = max_p m_p
@@ -531,19 +551,27 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(Decode
 // ((request << 16) | partition, largest first) in a snake deal: in round r
 // workgroup y takes entry r*wph + y, reversed on odd rounds, which gives every
 // workgroup a near-equal share of blocks and leaves the smallest units for
-// last.  (Claiming the last rounds dynamically from a counter was measured
-// and gained nothing: HBM stays saturated while the faster workgroups drain.)
-// While a unit is computed the next unit's block ids are already loaded, and
-// its first block and query rows are in flight during the unit's epilogue.
-// LDS merge slots rotate over consecutive units so that a fast wavefront can
-// post the next unit while the last one of an earlier unit still merges.
+// last.  While a unit is computed the next unit's block ids are already
+// loaded, and its first block and query rows are in flight during the unit's
+// epilogue.  LDS merge slots rotate over consecutive units so that a fast
+// wavefront can post the next unit while the last one of an earlier unit
+// still merges.
+//
+// Merged results are not stored when a unit ends: they go to an LDS ring of
+// `ring` unit slots, written to HBM when the ring is full and when the
+// workgroup's work is done.  On this GPU a wavefront's stores and loads
+// retire in order, so a store issued at a unit's end would make the next
+// unit's first wait also wait for the store's acknowledgement; measured on
+// the Llama-3-70B-shaped layer that cost ~8 % of the launch.
 template <int D>
 __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(PA_WL_WAVES_PER_EU)))
-void decode_worklist_kernel(DecodeArgs a, const int32_t* __restrict__ items, int32_t n_items) {
+void decode_worklist_kernel(DecodeArgs a, const int32_t* __restrict__ items, int32_t n_items,
+                            int32_t ring) {
   constexpr int OROW = D + 4;
   const int g = blockIdx.x;
   const int wph = gridDim.y;
   const int y = blockIdx.y;
+  const int G = a.G;
   const int wave = uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
 
@@ -552,20 +580,42 @@ void decode_worklist_kernel(DecodeArgs a, const int32_t* __restrict__ items, int
   __shared__ int sm_arrive[kMergeSlots];
   __shared__ int sm_bad[kMergeSlots];
   __shared__ int sm_merged[kMergeSlots];
-  extern __shared__ f32x4 sm_o4[];  // [kMergeSlots][kDecodeWaves][G][D + 4] floats
+  // dynamic LDS: [kMergeSlots][kDecodeWaves][G][D + 4] floats (merge states),
+  // then the result ring: [ring] (request, partition, partitions, valid),
+  // [ring][G][D] fp16 rows, [ring][G] max, [ring][G] sum
+  extern __shared__ f32x4 sm_o4[];
   if (threadIdx.x < kMergeSlots) {
     sm_arrive[threadIdx.x] = 0;
     sm_bad[threadIdx.x] = 0;
     sm_merged[threadIdx.x] = 0;
   }
   __syncthreads();
-  const int slot_floats = kDecodeWaves * a.G * OROW;
+  const int slot_floats = kDecodeWaves * G * OROW;
+  int4* ring_info = reinterpret_cast<int4*>(reinterpret_cast<float*>(sm_o4) +
+                                           kMergeSlots * slot_floats);  // 16-byte aligned
+  f16* ring_o = reinterpret_cast<f16*>(ring_info + ring);
+  float* ring_m = reinterpret_cast<float*>(ring_o + ring * G * D);
+  float* ring_l = ring_m + ring * G;
 
   auto item = [&](int k) { return (k & 1) ? (k + 1) * wph - 1 - y : k * wph + y; };
   auto unit_at = [&](int t) {
     const uint32_t packed = static_cast<uint32_t>(scalar_load(items, t));
     return make_unit(a, static_cast<int>(packed >> 16), static_cast<int>(packed & 0xFFFFu), wave,
                      lane);
+  };
+  // both wavefronts: write ring slots 0 .. count-1 to their global rows
+  auto flush = [&](int count) {
+    for (int j = wave; j < count; j += kDecodeWaves) {
+      const int4 info = ring_info[j];  // request, partition, partitions, valid
+      if (info.w == 0) continue;
+      for (int idx = lane; idx < G * (D / 8); idx += kWave) {
+        const int h = idx / (D / 8);
+        const int d0 = (idx % (D / 8)) * 8;
+        const f16x8 r = *reinterpret_cast<const f16x8*>(ring_o + (j * G + h) * D + d0);
+        store_rows<D>(a, g, info.x, info.y, info.z, h, d0, r, ring_m[j * G + h],
+                      ring_l[j * G + h]);
+      }
+    }
   };
 
   if (item(0) >= n_items) return;
@@ -593,15 +643,31 @@ void decode_worklist_kernel(DecodeArgs a, const int32_t* __restrict__ items, int
     const MergeSlot<D> ms{sm_m[buf], sm_l[buf],
                           reinterpret_cast<float*>(sm_o4) + buf * slot_floats, &sm_arrive[buf],
                           &sm_bad[buf]};
-    if (post_state<D>(ms, st, a.G, wave, lane, u.bad)) {
-      if (u.ok) merge_store<D>(a, ms, g, u.b, u.p, u.L, u.n_parts, lane);
+    const int rs = k % ring;  // this unit's result slot
+    if (post_state<D>(ms, st, G, wave, lane, u.bad)) {
+      if (u.ok) {
+        merge_unit<D>(ms, G, u.L, lane, [&](int h, int d0, f16x8 r, float m, float l) {
+          *reinterpret_cast<f16x8*>(ring_o + (rs * G + h) * D + d0) = r;
+          if (d0 == 0) {
+            ring_m[rs * G + h] = m;
+            ring_l[rs * G + h] = l;
+          }
+        });
+      }
       if (lane == 0) {
+        ring_info[rs] = int4{u.b, u.p, u.n_parts, u.ok ? 1 : 0};
         sm_arrive[buf] = 0;
         sm_bad[buf] = 0;
         __hip_atomic_fetch_add(&sm_merged[buf], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
     }
-    if (!more) return;
+    if (!more || rs == ring - 1) {
+      // every unit in the ring has been merged once both wavefronts get here
+      __syncthreads();
+      flush(rs + 1);
+      if (!more) return;
+      __syncthreads();  // the ring is read out before the next unit reuses slot 0
+    }
     u = nx;
   }
 }
@@ -714,16 +780,22 @@ extern "C" pa_status pa_paged_attention_decode(pa_half* out, const pa_half* q, p
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (worklist) {
     if (n_items > 0) {
-      const size_t lds = static_cast<size_t>(kMergeSlots) * kDecodeWaves * G * (D + 4) * sizeof(float);
+      // result ring: as many unit slots as fit in ~16 KiB (at least 2)
+      const size_t ring_slot = static_cast<size_t>(G) * D * 2 + 2 * G * sizeof(float) + 16;
+      const int ring = static_cast<int>(std::max<size_t>(2, kResultRingBytes / ring_slot));
+      const size_t lds = static_cast<size_t>(kMergeSlots) * kDecodeWaves * G * (D + 4) * sizeof(float) +
+                         static_cast<size_t>(ring) * ring_slot;
       int wph = worklist_resident_wgs(D, G, lds) / kv.num_kv_heads;
       if (wph < 1) wph = 1;
       if (wph > n_items) wph = n_items;
       if (wph > 65535) wph = 65535;
       const dim3 grid(static_cast<uint32_t>(kv.num_kv_heads), static_cast<uint32_t>(wph));
       if (D == 128)
-        decode_worklist_kernel<128><<<grid, dim3(kDecodeThreads), lds, s>>>(a, work_items, n_items);
+        decode_worklist_kernel<128><<<grid, dim3(kDecodeThreads), lds, s>>>(a, work_items, n_items,
+                                                                             ring);
       else
-        decode_worklist_kernel<64><<<grid, dim3(kDecodeThreads), lds, s>>>(a, work_items, n_items);
+        decode_worklist_kernel<64><<<grid, dim3(kDecodeThreads), lds, s>>>(a, work_items, n_items,
+                                                                            ring);
     }
   } else {
     const size_t lds = static_cast<size_t>(kDecodeWaves) * G * (D + 4) * sizeof(float);
