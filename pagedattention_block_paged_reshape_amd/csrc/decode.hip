@@ -404,16 +404,18 @@ template <int D>
 __device__ __forceinline__ void store_rows(const DecodeArgs& a, int g, int b, int p,
                                            int n_parts, int h, int d0, f16x8 r, float m,
                                            float l) {
+  // Streaming (non-temporal) stores: nothing in this launch reads the rows
+  // back, so they should not take cache lines from the K/V gather.
   const int G = a.G;
   if (n_parts <= 1) {
     const int64_t qh = static_cast<int64_t>(b) * a.n_kv * G + g * G + h;
-    *reinterpret_cast<f16x8*>(a.out + qh * D + d0) = r;
+    __builtin_nontemporal_store(r, reinterpret_cast<f16x8*>(a.out + qh * D + d0));
   } else {
     const int64_t slot = ((static_cast<int64_t>(b) * a.n_kv + g) * a.p_max + p) * G + h;
-    *reinterpret_cast<f16x8*>(a.ws_o + slot * D + d0) = r;
+    __builtin_nontemporal_store(r, reinterpret_cast<f16x8*>(a.ws_o + slot * D + d0));
     if (d0 == 0) {
-      a.ws_m[slot] = m;
-      a.ws_l[slot] = l;
+      __builtin_nontemporal_store(m, a.ws_m + slot);
+      __builtin_nontemporal_store(l, a.ws_l + slot);
     }
   }
 }
