@@ -82,9 +82,9 @@ struct DecodeArgs {
   int32_t part_blocks;
   int32_t p_max;
   f16* out;
-  f16* ws_o;    // [B][n_q][p_max][D] fp16
-  float* ws_m;  // [B][n_q][p_max]
-  float* ws_l;  // [B][n_q][p_max]
+  f16* ws_o;    // [B][n_kv][p_max][G][D] fp16
+  float* ws_m;  // [B][n_kv][p_max][G]
+  float* ws_l;  // [B][n_kv][p_max][G]
 };
 
 // One wavefront's share of a unit: running max and sum per query head and
@@ -428,84 +428,92 @@ __device__ __forceinline__ void merge_store(const DecodeArgs& a, const MergeSlot
   });
 }
 
-// Merge the partitions of each (request, query head): with M = max_p m_p
-// and w_p = l_p * 2^(m_p - M), out = sum_p w_p o_p / sum_p w_p, summed in
-// partition order.  One workgroup per (kv head, request); 32 lanes per query
-// head, each lane D/32 dims.  The kernel is latency-bound, so after reading
-// the request's length each lane requests the (o, m, l) of up to kChunk
-// partitions at once: a request of up to kChunk partitions costs two memory
-// round trips.  Longer ones take further chunks.  Requests that fit in one
-// partition were written by the partition kernel and are skipped.
-template <int D>
-__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
-  constexpr int PER = D / 32;
+// Merge the partial states of one (request, query head) over the 8 * NV
+// dims from d0: with M = max_p m_p and w_p = l_p * 2^(m_p - M),
+// out = sum_p w_p o_p / sum_p w_p, the sums taken in partition order (each
+// partition's exp sum rescaled to the common max, which gives exactly the
+// softmax over the whole sequence).  `bg` is the (request, kv head)'s first
+// partial slot.  The partials of up to kChunk partitions are requested at
+// once, so a request of up to kChunk partitions costs one memory round trip.
+template <int D, int NV>
+__device__ __forceinline__ void merge_partials(const DecodeArgs& a, int64_t bg, int h, int d0,
+                                               int n_parts, f16x8 (&res)[NV]) {
   constexpr int kChunk = 8;
-  typedef _Float16 f16xP __attribute__((ext_vector_type(PER)));
+  const int G = a.G;
+  f16x8 v[kChunk][NV];
+  float mm[kChunk], ll[kChunk];
+  auto load = [&](int p0) {
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      if (p0 + u < n_parts) {
+        const int64_t slot = bg + static_cast<int64_t>(p0 + u) * G + h;
+#pragma unroll
+        for (int c = 0; c < NV; ++c)
+          v[u][c] = *reinterpret_cast<const f16x8*>(a.ws_o + slot * D + d0 + 8 * c);
+        mm[u] = a.ws_m[slot];
+        ll[u] = a.ws_l[slot];
+      }
+    }
+  };
+  load(0);
+  float M = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < kChunk; ++u)
+    if (u < n_parts) M = fmaxf(M, mm[u]);
+  for (int p = kChunk; p < n_parts; ++p) M = fmaxf(M, a.ws_m[bg + static_cast<int64_t>(p) * G + h]);
+  float wsum = 0.0f;
+  float acc[NV][8];
+#pragma unroll
+  for (int c = 0; c < NV; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[c][e] = 0.0f;
+  for (int p0 = 0; p0 < n_parts; p0 += kChunk) {
+    if (p0 > 0) load(p0);
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      if (p0 + u < n_parts) {
+        const float w = ll[u] * exp2f(mm[u] - M);
+        wsum += w;
+#pragma unroll
+        for (int c = 0; c < NV; ++c)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[c][e] += w * static_cast<float>(v[u][c][e]);
+      }
+    }
+  }
+  const float inv = 1.0f / wsum;
+#pragma unroll
+  for (int c = 0; c < NV; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) res[c][e] = static_cast<f16>(acc[c][e] * inv);
+}
+
+// Second kernel of both launch forms: one wavefront per (kv head, request)
+// merges the request's partitions, D/16 lanes per query head and 16 dims
+// per lane.  The kernel is bound by memory latency: it reads the request's
+// length, then all partials in one round trip.  Requests that fit in one
+// partition were written by the first kernel and are skipped.
+template <int D>
+__global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeArgs a) {
+  constexpr int LPH = D / 16;  // lanes per query head
   const int g = blockIdx.x;
   const int b = blockIdx.y;
   const int G = a.G;
-  const int n_q = a.n_kv * G;
-  const int j = threadIdx.x & 31;
   const int part_tokens = a.part_blocks * kBlock;
-  // partials of (b, g): [p_max][G][D] contiguous, (m, l) as [p_max][G]
-  const int64_t bg = (static_cast<int64_t>(b) * a.n_kv + g) * a.p_max * G;
   int L = scalar_load(a.seq_lens, b);
   if (L < 0) return;                                         // written as NaN already
   if (L > a.max_blocks * kBlock) L = a.max_blocks * kBlock;  // partials are NaN-flagged
   const int n_parts = min((L + part_tokens - 1) / part_tokens, a.p_max);
   if (n_parts <= 1) return;
-  for (int h = threadIdx.x >> 5; h < G; h += blockDim.x >> 5) {
-    auto load_o = [&](int p) {
-      return *reinterpret_cast<const f16xP*>(a.ws_o + (bg + static_cast<int64_t>(p) * G + h) * D +
-                                             j * PER);
-    };
-    f16xP v[kChunk];
-    float mm[kChunk], ll[kChunk];
-#pragma unroll
-    for (int u = 0; u < kChunk; ++u) {
-      if (u < n_parts) {
-        v[u] = load_o(u);
-        mm[u] = a.ws_m[bg + u * G + h];
-        ll[u] = a.ws_l[bg + u * G + h];
-      }
-    }
-
-    float M = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < kChunk; ++u)
-      if (u < n_parts) M = fmaxf(M, mm[u]);
-    for (int p = kChunk; p < n_parts; ++p) M = fmaxf(M, a.ws_m[bg + p * G + h]);
-    float wsum = 0.0f;
-    float acc[PER];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
-    for (int p0 = 0; p0 < n_parts; p0 += kChunk) {
-      if (p0 > 0) {
-#pragma unroll
-        for (int u = 0; u < kChunk; ++u) {
-          if (p0 + u < n_parts) {
-            v[u] = load_o(p0 + u);
-            mm[u] = a.ws_m[bg + (p0 + u) * G + h];
-            ll[u] = a.ws_l[bg + (p0 + u) * G + h];
-          }
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kChunk; ++u) {
-        if (p0 + u < n_parts) {
-          const float w = ll[u] * exp2f(mm[u] - M);
-          wsum += w;
-#pragma unroll
-          for (int e = 0; e < PER; ++e) acc[e] += w * static_cast<float>(v[u][e]);
-        }
-      }
-    }
-    const float inv = 1.0f / wsum;
-    f16xP rr;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) rr[e] = static_cast<f16>(acc[e] * inv);
-    const int64_t qh = static_cast<int64_t>(b) * n_q + g * G + h;
-    *reinterpret_cast<f16xP*>(a.out + qh * D + j * PER) = rr;
+  const int64_t bg = (static_cast<int64_t>(b) * a.n_kv + g) * a.p_max * G;
+  for (int idx = threadIdx.x; idx < G * LPH; idx += kWave) {
+    const int h = idx / LPH;
+    const int d0 = (idx % LPH) * 16;
+    f16x8 r[2];
+    merge_partials<D, 2>(a, bg, h, d0, n_parts, r);
+    f16* dst = a.out + ((static_cast<int64_t>(b) * a.n_kv + g) * G + h) * D + d0;
+    *reinterpret_cast<f16x8*>(dst) = r[0];
+    *reinterpret_cast<f16x8*>(dst + 8) = r[1];
   }
 }
 
@@ -812,9 +820,9 @@ extern "C" pa_status pa_paged_attention_decode(pa_half* out, const pa_half* q, p
   if (p_max > 1) {
     const dim3 rgrid(static_cast<uint32_t>(kv.num_kv_heads), static_cast<uint32_t>(batch));
     if (D == 128)
-      decode_reduce_kernel<128><<<rgrid, dim3(256), 0, s>>>(a);
+      decode_reduce_kernel<128><<<rgrid, dim3(kWave), 0, s>>>(a);
     else
-      decode_reduce_kernel<64><<<rgrid, dim3(256), 0, s>>>(a);
+      decode_reduce_kernel<64><<<rgrid, dim3(kWave), 0, s>>>(a);
   }
   return launch_status();
 }
