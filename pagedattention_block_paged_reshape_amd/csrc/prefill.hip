@@ -20,7 +20,8 @@
 //  * Keys advance 64 at a time (4 blocks).  The 4 K tiles and 4 V tiles are
 //    gathered through the table with lane-contiguous 16-byte loads into
 //    registers one step ahead, then stored to LDS in logical order (K as
-//    [key][D], V^T as [D][key], rows padded so the MFMA operand reads are
+//    [key][D], V^T as [D][key] with each 32-key half in the score
+//    accumulators' key order, rows padded so the MFMA operand reads are
 //    bank-conflict free) and shared by the 4 wavefronts.
 //  * S^T = K . Q^T (keys x M-rows, 16x16x32 f16 MFMA); online softmax in fp32
 //    base 2 per M-row; P^T goes straight from the score accumulators into the
@@ -64,8 +65,8 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
   constexpr int KROW = D + 8;      // padded K row (halves)
   constexpr int VROW = kPfKeys + 8;  // padded V^T row (halves)
   constexpr int KCH = kPfKeys * D / 8 / kPfThreads;  // 16-B chunks per thread per tile set
-  __shared__ f16 sk[kPfKeys * KROW];
-  __shared__ f16 sv[D * VROW];
+  __shared__ __attribute__((aligned(16))) f16 sk[kPfKeys * KROW];
+  __shared__ __attribute__((aligned(16))) f16 sv[D * VROW];
   __shared__ int sbad;
 
   const int g = blockIdx.x;
@@ -120,21 +121,32 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
 
   // Register staging of one step's 4 K tiles and 4 V tiles.
   f16x8 rk[KCH], rv[KCH];
-  auto fetch = [&](int step) {
+  // Physical ids of a step's 4 blocks, read (clamped into the table; entries
+  // past the sequence are never used) a step before their fetch.
+  constexpr int kStepBlocks = kPfKeys / kBlock;
+  auto read_ids = [&](int step, int (&ids)[kStepBlocks]) {
+#pragma unroll
+    for (int i = 0; i < kStepBlocks; ++i)
+      ids[i] = scalar_load(table, min(step * kStepBlocks + i, table_len - 1));
+  };
+  // Chunk u of every thread lies in one block of the step, the same for the
+  // whole wavefront (a block is kBlock * D / 8 >= 64 chunks), so the bounds
+  // checks and the tail test are scalar.
+  auto fetch = [&](int step, const int (&ids)[kStepBlocks]) {
     const int key0 = step * kPfKeys;
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
-      const int ci = threadIdx.x + kPfThreads * u;   // 16-byte chunk of the 4-tile set
-      const int bi = ci / (kBlock * D / 8);          // which of the 4 blocks
+      const int ci = threadIdx.x + kPfThreads * u;         // 16-byte chunk of the 4-tile set
+      const int bi = uniform(ci / (kBlock * D / 8));       // which of the 4 blocks
       const int within = ci % (kBlock * D / 8);
-      const int lb = key0 / kBlock + bi;             // logical block
+      const int lb = key0 / kBlock + bi;                   // logical block
       const f16x8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
       if (lb * kBlock >= seq_end || lb >= table_len) {
         rk[u] = zero;
         rv[u] = zero;
         continue;
       }
-      int pb = table[lb];
+      int pb = ids[bi];
       if (static_cast<uint32_t>(pb) >= static_cast<uint32_t>(num_blocks)) {
         bad = true;
         pb = 0;
@@ -142,11 +154,12 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
       const int64_t tile = (static_cast<int64_t>(pb) * n_kv + g) * (kBlock * D);
       rk[u] = *reinterpret_cast<const f16x8*>(kp + tile + within * 8);
       f16x8 vv = *reinterpret_cast<const f16x8*>(vp + tile + within * 8);
-      // V chunk `within` = two dims' values for slots 4q .. 4q+3 (tile order
-      // [D/32][4][16][2][4]): zero the slots past the sequence's end
-      const int q4 = ((within >> 4) & 3) * 4;
-      const int valid = seq_end - (lb * kBlock + q4);
-      if (valid < 4) {
+      if (lb * kBlock + kBlock > seq_end) {
+        // the sequence's last block: V chunk `within` holds two dims' values
+        // for slots 4q .. 4q+3 (tile order [D/32][4][16][2][4]); zero the
+        // slots past the end
+        const int q4 = ((within >> 4) & 3) * 4;
+        const int valid = seq_end - (lb * kBlock + q4);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           if ((e & 3) >= valid) vv[e] = static_cast<f16>(0.0f);
@@ -164,21 +177,30 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
       const int key = bi * kBlock + (within & 15);
       const int d8 = within >> 4;
       *reinterpret_cast<f16x8*>(sk + key * KROW + d8 * 8) = rk[u];
-      // V chunk `within` = dims c2*32 + dd and c2*32 + 16 + dd, slots 4q .. +4
+      // V chunk `within` = dims c2*32 + dd and c2*32 + 16 + dd, slots 4q .. +4.
+      // V^T rows keep each 32-key half in the order the score accumulators
+      // hold P^T: key 16h + 4q + j of the half sits at 8q + 4h + j, so one
+      // 16-byte read gives a lane its 8 keys of the PV operand.
       const int dim = (within >> 6) * 32 + (within & 15);
-      const int kslot = bi * kBlock + ((within >> 4) & 3) * 4;
+      const int q4 = (within >> 4) & 3;
+      const int kpos = (bi >> 1) * 32 + q4 * 8 + (bi & 1) * 4;
       const f16x8 vv = rv[u];
-      *reinterpret_cast<f16x4*>(sv + dim * VROW + kslot) = f16x4{vv[0], vv[1], vv[2], vv[3]};
-      *reinterpret_cast<f16x4*>(sv + (dim + 16) * VROW + kslot) = f16x4{vv[4], vv[5], vv[6], vv[7]};
+      *reinterpret_cast<f16x4*>(sv + dim * VROW + kpos) = f16x4{vv[0], vv[1], vv[2], vv[3]};
+      *reinterpret_cast<f16x4*>(sv + (dim + 16) * VROW + kpos) = f16x4{vv[4], vv[5], vv[6], vv[7]};
     }
   };
 
-  if (st0 < st1) fetch(st0);
+  int ids[kStepBlocks];
+  if (st0 < st1) {
+    read_ids(st0, ids);
+    fetch(st0, ids);
+  }
+  if (st0 + 1 < st1) read_ids(st0 + 1, ids);
   for (int step = st0; step < st1; ++step) {
     __syncthreads();  // previous step's LDS reads are done
     stash();
     __syncthreads();
-    if (step + 1 < st1) fetch(step + 1);
+    if (step + 1 < st1) fetch(step + 1, ids);
 
     const int key0 = step * kPfKeys;
     // scores S^T[key][M-row]: 4 key tiles x 2 M-row tiles
@@ -197,6 +219,8 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
         s[mt][nt] = acc;
       }
     }
+
+    if (step + 2 < st1) read_ids(step + 2, ids);
 
     // causal mask, on the raw scores, only where the step crosses the
     // diagonal of this tile (a uniform branch: most steps skip it)
@@ -247,10 +271,8 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const f16* vrow = sv + (dt * 16 + col) * VROW + ks * 32 + 4 * lg;
-        const f16x4 lo = *reinterpret_cast<const f16x4*>(vrow);
-        const f16x4 hi = *reinterpret_cast<const f16x4*>(vrow + 16);
-        const f16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const f16x8 va =
+            *reinterpret_cast<const f16x8*>(sv + (dt * 16 + col) * VROW + ks * 32 + 8 * lg);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) o[dt][nt] = mfma16x16x32(va, pb8[ks][nt], o[dt][nt]);
       }
