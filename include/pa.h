@@ -57,6 +57,9 @@ extern "C" {
 
 #define PA_BLOCK_SIZE 16
 
+/* pa_paged_attention_decode flags. */
+#define PA_DECODE_KEEP_KV 1u /* K/V tiles are shared between requests: cache them */
+
 typedef uint16_t pa_half; /* IEEE binary16 bit pattern */
 
 typedef enum pa_status {
@@ -99,7 +102,7 @@ typedef struct pa_pool_stats {
   int32_t num_blocks;
   int32_t num_free;
   int32_t num_seqs;
-  int32_t reserved;
+  int32_t num_shared;  /* blocks referenced by more than one sequence       */
   int64_t allocs;   /* blocks taken off the free list (including CoW targets) */
   int64_t frees;    /* blocks returned to the free list                       */
   int64_t cows;     /* copy-on-write copies planned                          */
@@ -246,13 +249,21 @@ uint64_t pa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t h
  *   workspace: device, 16-byte aligned, >= pa_decode_workspace_bytes(...);
  *   may be NULL when that is 0.  Calls sharing a workspace must not overlap.
  *   A table entry outside [0, num_blocks) or a length above max_blocks*16
- *   makes that request's output NaN (no out-of-bounds access). */
+ *   makes that request's output NaN (no out-of-bounds access).
+ *   flags: 0 or PA_DECODE_KEEP_KV (anything else: PA_ERR_INVALID).  By
+ *   default every K/V tile is loaded non-temporally, since without sharing
+ *   each is read once per call; pass PA_DECODE_KEEP_KV when requests share
+ *   blocks ([tcd] "memory sharing for parallel sampling"; [yj]
+ *   "copy-on-write prefix sharing"), e.g. whenever pa_pool_get_stats reports
+ *   num_shared > 0, so that a shared tile stays cached for the other
+ *   requests.  Results are bitwise the same either way. */
 pa_status pa_paged_attention_decode(pa_half* out, const pa_half* q, pa_kv_view kv,
                                     const int32_t* tables, int32_t max_blocks,
                                     const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
                                     float scale, int32_t partition_size, int32_t max_seq_len,
                                     const int32_t* work_items, int32_t n_items,
-                                    void* workspace, uint64_t workspace_bytes, void* stream);
+                                    void* workspace, uint64_t workspace_bytes, uint32_t flags,
+                                    void* stream);
 
 /* Workspace bytes pa_paged_attention_prefill needs for a chunk of chunk_len
  * query rows ending at key position q_start + chunk_len. */

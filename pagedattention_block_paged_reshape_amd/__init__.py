@@ -8,6 +8,7 @@ from ._lib import (  # noqa: F401
     BLOCK_SIZE,
     EXPORTED,
     LIB_PATH,
+    PA_DECODE_KEEP_KV,
     OutOfBlocksError,
     PaError,
     kv_view,

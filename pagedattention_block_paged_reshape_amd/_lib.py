@@ -15,6 +15,7 @@ from typing import Optional, Sequence
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
+PA_DECODE_KEEP_KV = 1  # pa_paged_attention_decode flag: K/V tiles shared between requests
 LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
 
 PA_OK = 0
@@ -49,7 +50,7 @@ class pa_copy(C.Structure):
 
 class pa_pool_stats(C.Structure):
     _fields_ = [("num_blocks", C.c_int32), ("num_free", C.c_int32), ("num_seqs", C.c_int32),
-                ("reserved", C.c_int32), ("allocs", C.c_int64), ("frees", C.c_int64),
+                ("num_shared", C.c_int32), ("allocs", C.c_int64), ("frees", C.c_int64),
                 ("cows", C.c_int64)]
 
 
@@ -85,7 +86,8 @@ _SIGS = {
     "pa_decode_workspace_bytes": (_U64, [_I32, _I32, _I32, _I32, _I32]),
     "pa_decode_work_items": (_I32, [_P, _I32, _I32, _P, _I32]),
     "pa_paged_attention_decode": (C.c_int, [_P, _P, pa_kv_view, _P, _I32, _P, _I32, _I32,
-                                            C.c_float, _I32, _I32, _P, _I32, _P, _U64, _P]),
+                                            C.c_float, _I32, _I32, _P, _I32, _P, _U64, C.c_uint32,
+                                            _P]),
     "pa_prefill_workspace_bytes": (_U64, [_I32, _I32, _I32, _I32]),
     "pa_paged_attention_prefill": (C.c_int, [_P, _P, pa_kv_view, _P, _I32, _I32, _I32, _I32,
                                              C.c_float, _P, _U64, _P]),
@@ -307,12 +309,12 @@ def pa_decode_work_items(seq_lens, partition_size: int, out: Optional[np.ndarray
 def pa_paged_attention_decode(out, q, kv: pa_kv_view, tables, max_blocks: int, seq_lens,
                               batch: int, num_q_heads: int, scale: float, partition_size: int,
                               max_seq_len: int, work_items, n_items: int, workspace,
-                              workspace_bytes: int, stream=None) -> None:
+                              workspace_bytes: int, stream=None, flags: int = 0) -> None:
     _check(LIB.pa_paged_attention_decode(_dptr(out), _dptr(q), kv, _dptr(tables), int(max_blocks),
                                          _dptr(seq_lens), int(batch), int(num_q_heads),
                                          float(scale), int(partition_size), int(max_seq_len),
                                          _dptr(work_items), int(n_items), _dptr(workspace),
-                                         int(workspace_bytes), _stream(stream)),
+                                         int(workspace_bytes), int(flags), _stream(stream)),
            "pa_paged_attention_decode")
 
 

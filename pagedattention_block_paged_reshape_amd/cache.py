@@ -54,6 +54,12 @@ class PagedKVCache:
         except Exception:
             pass
 
+    def shares_blocks(self) -> bool:
+        """True while some block is referenced by more than one sequence:
+        decode then keeps K/V tiles in cache (PA_DECODE_KEEP_KV) so that a
+        shared prefix is read from HBM once per kv head."""
+        return L.pa_pool_get_stats(self.pool)["num_shared"] > 0
+
     # -- host-side request bookkeeping -------------------------------------
     def add(self, seq_id: int):
         L.pa_seq_add(self.pool, seq_id)
@@ -112,8 +118,10 @@ class DecodePlan:
 
     def __init__(self, cache: PagedKVCache, seq_ids, num_q_heads: int, scale: float,
                  partition: int = DEFAULT_PARTITION, out: Optional[torch.Tensor] = None,
-                 worklist: bool = True):
+                 worklist: bool = True, keep_kv: Optional[bool] = None):
         self.cache = cache
+        keep = cache.shares_blocks() if keep_kv is None else bool(keep_kv)
+        self.flags = L.PA_DECODE_KEEP_KV if keep else 0
         tab, ln, self.max_blocks = cache.host_tables(seq_ids)
         self.tables = torch.from_numpy(tab).to(cache.device)
         self.lens = torch.from_numpy(ln).to(cache.device)
@@ -140,7 +148,8 @@ class DecodePlan:
                                     self.lens, self.batch, self.n_q, self.scale, self.partition,
                                     self.max_len, self.items, self.n_items, self.workspace,
                                     self.ws_bytes,
-                                    stream or torch.cuda.current_stream(self.cache.device))
+                                    stream or torch.cuda.current_stream(self.cache.device),
+                                    flags=self.flags)
         return self.out
 
 

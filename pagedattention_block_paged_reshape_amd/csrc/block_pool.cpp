@@ -40,6 +40,17 @@ struct pa_pool {
   std::vector<int32_t> ref;
   std::unordered_map<int64_t, Seq> seqs;
   int64_t allocs = 0, frees = 0, cows = 0;
+  int32_t shared = 0;  // blocks with ref > 1
+
+  void ref_up(int32_t b) {
+    if (++ref[b] == 2) ++shared;
+  }
+  // Drops one reference; true when the block became free.
+  bool ref_down(int32_t b) {
+    const int32_t r = --ref[b];
+    if (r == 1) --shared;
+    return r == 0;
+  }
 
   int32_t pop() {
     int32_t b = free_stack.back();
@@ -155,7 +166,7 @@ pa_status pa_seq_fork(pa_pool* pool, int64_t parent, int64_t child) {
   if (it == pool->seqs.end()) return PA_ERR_UNKNOWN_SEQ;
   if (pool->seqs.count(child)) return PA_ERR_EXISTS;
   Seq c = it->second;
-  for (int32_t b : c.table) ++pool->ref[b];
+  for (int32_t b : c.table) pool->ref_up(b);
   pool->seqs.emplace(child, std::move(c));
   return PA_OK;
 }
@@ -165,7 +176,7 @@ pa_status pa_seq_free(pa_pool* pool, int64_t seq_id) {
   auto it = pool->seqs.find(seq_id);
   if (it == pool->seqs.end()) return PA_ERR_UNKNOWN_SEQ;
   for (int32_t b : it->second.table) {
-    if (--pool->ref[b] == 0) {
+    if (pool->ref_down(b)) {
       pool->free_stack.push_back(b);
       ++pool->frees;
     }
@@ -214,7 +225,7 @@ pa_status pa_append_slots(pa_pool* pool, int32_t n, const int64_t* seq_ids,
         blk = s.table[logical];
         if (pool->ref[blk] > 1) {
           const int32_t fresh = pool->pop();
-          --pool->ref[blk];
+          pool->ref_down(blk);
           copies[c++] = pa_copy{blk, fresh, off};
           ++pool->cows;
           s.table[logical] = fresh;
@@ -282,7 +293,7 @@ pa_status pa_pool_get_stats(const pa_pool* pool, pa_pool_stats* stats) {
   stats->num_blocks = pool->num_blocks;
   stats->num_free = static_cast<int32_t>(pool->free_stack.size());
   stats->num_seqs = static_cast<int32_t>(pool->seqs.size());
-  stats->reserved = 0;
+  stats->num_shared = pool->shared;
   stats->allocs = pool->allocs;
   stats->frees = pool->frees;
   stats->cows = pool->cows;
@@ -313,11 +324,13 @@ pa_status pa_pool_check(const pa_pool* pool) {
       ++held[b];
     }
   }
-  int64_t referenced = 0;
+  int64_t referenced = 0, shared = 0;
   for (int32_t b = 0; b < N; ++b) {
     if (held[b] != pool->ref[b]) return PA_ERR_INTERNAL;
     if (pool->ref[b] > 0) ++referenced;
+    if (pool->ref[b] > 1) ++shared;
   }
+  if (shared != pool->shared) return PA_ERR_INTERNAL;
   std::vector<char> in_free(N, 0);
   for (int32_t b : pool->free_stack) {
     if (b < 0 || b >= N || in_free[b] || pool->ref[b] != 0) return PA_ERR_INTERNAL;

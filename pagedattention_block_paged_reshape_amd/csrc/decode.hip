@@ -201,17 +201,30 @@ __device__ __forceinline__ void load_q(const DecodeArgs& a, int g, int b, int la
 //   K step kk: lane l gets K[slot l%16][dims kk*32 + 8*(l/16) .. +8];
 //   V pair cc: lane l gets V[slots 4*(l/16) .. +4][dim (2cc+h)*16 + l%16] for
 //   h = 0, 1, i.e. the A operands of dim tiles 2cc and 2cc+1.
-template <int D>
+// Unless KEEP, the loads are non-temporal: a tile is read once per launch
+// when no two requests share it, and streaming it keeps it from competing
+// for cache lines with the tables, queries and partials (on the
+// Llama-3-70B-shaped layer this alone took the launch from ~262 us to
+// ~233 us, 5.4 -> 6.0 TB/s).  When requests share blocks (a common prefix),
+// KEEP loads them normally so that the shared tiles stay in L2.
+template <int D, bool KEEP>
+__device__ __forceinline__ f16x8 load_tile16(const f16* p) {
+  const f16x8* q = reinterpret_cast<const f16x8*>(p);
+  return KEEP ? *q : __builtin_nontemporal_load(q);
+}
+
+template <int D, bool KEEP>
 __device__ __forceinline__ void load_block(const DecodeArgs& a, int g, int pb, int lane,
                                            f16x8* kd, f16x4* vd) {
   const int64_t tile = (static_cast<int64_t>(pb) * a.n_kv + g) * (kBlock * D);  // uniform
   const f16* kt = a.kp + tile + lane * 8;
   const f16* vt = a.vp + tile + lane * 8;
 #pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk) kd[kk] = *reinterpret_cast<const f16x8*>(kt + kk * 512);
+  for (int kk = 0; kk < D / 32; ++kk)
+    kd[kk] = load_tile16<D, KEEP>(kt + kk * 512);
 #pragma unroll
   for (int cc = 0; cc < D / 32; ++cc) {
-    const f16x8 pair = *reinterpret_cast<const f16x8*>(vt + cc * 512);
+    const f16x8 pair = load_tile16<D, KEEP>(vt + cc * 512);
     vd[2 * cc] = f16x4{pair[0], pair[1], pair[2], pair[3]};
     vd[2 * cc + 1] = f16x4{pair[4], pair[5], pair[6], pair[7]};
   }
@@ -219,7 +232,9 @@ __device__ __forceinline__ void load_block(const DecodeArgs& a, int g, int pb, i
 
 // Physical block behind the wave's i-th load: unit u's blocks first; past
 // them the next unit's first block (so that it is in flight during u's
-// epilogue), or u's last block again (an L2 hit) when there is none.
+// epilogue), or, when there is none, block 0: one tile that every such
+// stand-in load shares, so it stays cached (the loads are non-temporal, so
+// re-reading u's last block would go to HBM again).
 __device__ __forceinline__ int unit_block(const Unit& u, int i) {
   return i < kWave ? __builtin_amdgcn_readlane(u.my_pb, i)
                    : __builtin_amdgcn_readlane(u.my_pb2, i - kWave);
@@ -232,14 +247,14 @@ __device__ __forceinline__ int pick_block(const Unit& u, const Unit& nx, int i) 
   else if (nx.cnt > 0)
     pb = unit_block(nx, 0);
   else
-    pb = u.cnt > 0 ? unit_block(u, u.cnt - 1) : 0;
+    pb = 0;
   return uniform(pb);
 }
 
 // The wavefront's pass over its blocks of unit u on kv head g.  On entry
 // kA/vA hold u's first block (when u.cnt > 0); on exit they hold nx's first
 // block (when nx.cnt > 0).
-template <int D>
+template <int D, bool KEEP>
 __device__ __forceinline__ void run_unit(const DecodeArgs& a, int g, int wave, int lane,
                                          const Unit& u, const Unit& nx, const f16x8* qf,
                                          f16x8* kA, f16x4* vA, f16x8* kB, f16x4* vB,
@@ -253,7 +268,7 @@ __device__ __forceinline__ void run_unit(const DecodeArgs& a, int g, int wave, i
 #pragma unroll
   for (int c = 0; c < DT; ++c) st.o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (u.cnt == 0) {
-    if (nx.cnt > 0) load_block<D>(a, g, pick_block(u, nx, 0), lane, kA, vA);
+    if (nx.cnt > 0) load_block<D, KEEP>(a, g, pick_block(u, nx, 0), lane, kA, vA);
     return;
   }
   const int L = u.L;
@@ -315,9 +330,9 @@ __device__ __forceinline__ void run_unit(const DecodeArgs& a, int g, int wave, i
   // counts only cover the block being consumed.  Every load is
   // unconditional (pick_block), the last one into kA/vA being nx's first.
   for (int i = 0; i < u.cnt; i += 2) {
-    load_block<D>(a, g, pick_block(u, nx, i + 1), lane, kB, vB);
+    load_block<D, KEEP>(a, g, pick_block(u, nx, i + 1), lane, kB, vB);
     compute(i, kA, vA);
-    load_block<D>(a, g, pick_block(u, nx, i + 2), lane, kA, vA);
+    load_block<D, KEEP>(a, g, pick_block(u, nx, i + 2), lane, kA, vA);
     if (i + 1 < u.cnt) compute(i + 1, kB, vB);
   }
 }
@@ -518,7 +533,7 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeArgs a) {
 }
 
 // Grid form: one workgroup per (kv head, request, partition).
-template <int D>
+template <int D, bool KEEP>
 __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(DecodeArgs a) {
   const int g = blockIdx.x;
   const int b = blockIdx.y;
@@ -548,10 +563,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(Decode
   f16x4 vA[D / 16], vB[D / 16];
   if (u.cnt > 0) {
     load_q<D>(a, g, b, lane, qf);
-    load_block<D>(a, g, pick_block(u, nx, 0), lane, kA, vA);
+    load_block<D, KEEP>(a, g, pick_block(u, nx, 0), lane, kA, vA);
   }
   WaveState<D> st;
-  run_unit<D>(a, g, wave, lane, u, nx, qf, kA, vA, kB, vB, st);
+  run_unit<D, KEEP>(a, g, wave, lane, u, nx, qf, kA, vA, kB, vB, st);
   const MergeSlot<D> ms{sm_m, sm_l, reinterpret_cast<float*>(sm_o4), &sm_arrive, &sm_bad};
   if (post_state<D>(ms, st, a.G, wave, lane, u.bad))
     merge_store<D>(a, ms, g, b, p, u.L, n_parts, lane);
@@ -573,7 +588,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(Decode
 // retire in order, so a store issued at a unit's end would make the next
 // unit's first wait also wait for the store's acknowledgement; measured on
 // the Llama-3-70B-shaped layer that cost ~8 % of the launch.
-template <int D>
+template <int D, bool KEEP>
 __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(PA_WL_WAVES_PER_EU)))
 void decode_worklist_kernel(DecodeArgs a, const int32_t* __restrict__ items, int32_t n_items,
                             int32_t ring) {
@@ -633,13 +648,13 @@ void decode_worklist_kernel(DecodeArgs a, const int32_t* __restrict__ items, int
   f16x8 qf[D / 32], kA[D / 32], kB[D / 32];
   f16x4 vA[D / 16], vB[D / 16];
   load_q<D>(a, g, u.b, lane, qf);
-  if (u.cnt > 0) load_block<D>(a, g, pick_block(u, no_unit(), 0), lane, kA, vA);
+  if (u.cnt > 0) load_block<D, KEEP>(a, g, pick_block(u, no_unit(), 0), lane, kA, vA);
 
   for (int k = 0;; ++k) {
     const bool more = item(k + 1) < n_items;
     const Unit nx = more ? unit_at(item(k + 1)) : no_unit();
     WaveState<D> st;
-    run_unit<D>(a, g, wave, lane, u, nx, qf, kA, vA, kB, vB, st);
+    run_unit<D, KEEP>(a, g, wave, lane, u, nx, qf, kA, vA, kB, vB, st);
     if (more) load_q<D>(a, g, nx.b, lane, qf);  // in flight during the epilogue
 
     const int buf = k % kMergeSlots;
@@ -684,14 +699,17 @@ void decode_worklist_kernel(DecodeArgs a, const int32_t* __restrict__ items, int
 
 // Resident workgroups of the work-list kernel on the current device (cached
 // per head_dim and G; the dynamic LDS depends on G).
-static int worklist_resident_wgs(int D, int G, size_t lds) {
-  static int per_cu[2][17];
+static int worklist_resident_wgs(int D, bool keep, int G, size_t lds) {
+  static int per_cu[2][2][17];
   static int cus = 0;
-  int& slot = per_cu[D == 128 ? 1 : 0][G];
+  int& slot = per_cu[D == 128 ? 1 : 0][keep ? 1 : 0][G];
   if (slot == 0) {
     int n = 0;
-    const void* fn = D == 128 ? reinterpret_cast<const void*>(&decode_worklist_kernel<128>)
-                              : reinterpret_cast<const void*>(&decode_worklist_kernel<64>);
+    const void* fn =
+        D == 128 ? (keep ? reinterpret_cast<const void*>(&decode_worklist_kernel<128, true>)
+                         : reinterpret_cast<const void*>(&decode_worklist_kernel<128, false>))
+                 : (keep ? reinterpret_cast<const void*>(&decode_worklist_kernel<64, true>)
+                         : reinterpret_cast<const void*>(&decode_worklist_kernel<64, false>));
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kDecodeThreads, lds) != hipSuccess || n < 1)
       n = 1;
     slot = n;
@@ -733,7 +751,7 @@ extern "C" pa_status pa_paged_attention_decode(pa_half* out, const pa_half* q, p
                                                int32_t partition_size, int32_t max_seq_len,
                                                const int32_t* work_items, int32_t n_items,
                                                void* workspace, uint64_t workspace_bytes,
-                                               void* stream) {
+                                               uint32_t flags, void* stream) {
   if (kv.k_pool == nullptr || kv.v_pool == nullptr || kv.block_size != kBlock ||
       kv.num_blocks <= 0 || kv.num_kv_heads <= 0 || kv.num_kv_heads > 65535)
     return PA_ERR_INVALID;
@@ -746,6 +764,8 @@ extern "C" pa_status pa_paged_attention_decode(pa_half* out, const pa_half* q, p
       partition_size > kDecodeWaves * kMaxWaveBlocks * kBlock)
     return PA_ERR_INVALID;
   if (!(scale == scale)) return PA_ERR_INVALID;
+  if ((flags & ~static_cast<uint32_t>(PA_DECODE_KEEP_KV)) != 0) return PA_ERR_INVALID;
+  const bool keep = (flags & PA_DECODE_KEEP_KV) != 0;
   if (n_items < 0 || n_items > (1 << 30) || (n_items > 0 && work_items == nullptr))
     return PA_ERR_INVALID;
   if (batch == 0) return PA_OK;
@@ -795,26 +815,22 @@ extern "C" pa_status pa_paged_attention_decode(pa_half* out, const pa_half* q, p
       const int ring = static_cast<int>(std::max<size_t>(2, kResultRingBytes / ring_slot));
       const size_t lds = static_cast<size_t>(kMergeSlots) * kDecodeWaves * G * (D + 4) * sizeof(float) +
                          static_cast<size_t>(ring) * ring_slot;
-      int wph = worklist_resident_wgs(D, G, lds) / kv.num_kv_heads;
+      int wph = worklist_resident_wgs(D, keep, G, lds) / kv.num_kv_heads;
       if (wph < 1) wph = 1;
       if (wph > n_items) wph = n_items;
       if (wph > 65535) wph = 65535;
       const dim3 grid(static_cast<uint32_t>(kv.num_kv_heads), static_cast<uint32_t>(wph));
-      if (D == 128)
-        decode_worklist_kernel<128><<<grid, dim3(kDecodeThreads), lds, s>>>(a, work_items, n_items,
-                                                                             ring);
-      else
-        decode_worklist_kernel<64><<<grid, dim3(kDecodeThreads), lds, s>>>(a, work_items, n_items,
-                                                                            ring);
+      auto fn = D == 128 ? (keep ? decode_worklist_kernel<128, true> : decode_worklist_kernel<128, false>)
+                         : (keep ? decode_worklist_kernel<64, true> : decode_worklist_kernel<64, false>);
+      fn<<<grid, dim3(kDecodeThreads), lds, s>>>(a, work_items, n_items, ring);
     }
   } else {
     const size_t lds = static_cast<size_t>(kDecodeWaves) * G * (D + 4) * sizeof(float);
     const dim3 grid(static_cast<uint32_t>(kv.num_kv_heads), static_cast<uint32_t>(batch),
                     static_cast<uint32_t>(p_max));
-    if (D == 128)
-      decode_partition_kernel<128><<<grid, dim3(kDecodeThreads), lds, s>>>(a);
-    else
-      decode_partition_kernel<64><<<grid, dim3(kDecodeThreads), lds, s>>>(a);
+    auto fn = D == 128 ? (keep ? decode_partition_kernel<128, true> : decode_partition_kernel<128, false>)
+                       : (keep ? decode_partition_kernel<64, true> : decode_partition_kernel<64, false>);
+    fn<<<grid, dim3(kDecodeThreads), lds, s>>>(a);
   }
   if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   if (p_max > 1) {

@@ -84,10 +84,11 @@ class DecodeStepper:
             if events is not None:
                 events["cache"][1].record(stream)
                 events["decode"][0].record(stream)
+            flags = L.PA_DECODE_KEEP_KV if self.cache.shares_blocks() else 0
             L.pa_paged_attention_decode(self.out, q, self.cache.kv, self.d_tab, self.max_blocks,
                                         self.d_len, self.B, self.n_q, self.scale, self.partition,
                                         max_len, self.d_items, n_items, self.workspace,
-                                        self.ws_bytes, stream)
+                                        self.ws_bytes, stream, flags=flags)
             if events is not None:
                 events["decode"][1].record(stream)
         self.i += 1

@@ -125,6 +125,7 @@ def test_decode_deterministic_and_placement_invariant():
 
 
 def test_shared_prefix_equals_private_copies_bitwise():
+    import pagedattention_block_paged_reshape_amd as pa
     shared = make_workload("4b")
     B = 16
     shared.decode_ids = shared.decode_ids[:B]
@@ -146,6 +147,13 @@ def test_shared_prefix_equals_private_copies_bitwise():
     b = gpu_run(private)
     assert len(a["step_copies"]) == B - 1 and len(b["step_copies"]) == 0
     assert torch.equal(a["decode"].view(torch.int16), b["decode"].view(torch.int16))
+    # the shared pool decodes with cached K/V loads, the private one streams
+    # them; the load policy must not change a bit
+    assert a["plan"].flags == pa.PA_DECODE_KEEP_KV and b["plan"].flags == 0
+    a["plan"].flags = 0
+    streamed = a["plan"].run(a["q"]).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(streamed.view(torch.int16), a["decode"].view(torch.int16))
     st = oracle_run(shared)
     assert_pools_bit_exact(a["cache"], st)
     assert_close(a["decode"], decode_reference(shared, st), "shared prefix")

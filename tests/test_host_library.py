@@ -115,6 +115,8 @@ def test_random_programs_match_oracle_exactly(seed):
                     assert slots.tolist() == exp[0]
                     assert [tuple(c) for c in copies.tolist()] == exp[1]
             tw.compare()
+            st = pa.pa_pool_get_stats(tw.lib)
+            assert st["num_shared"] == sum(1 for r in tw.ref.ref if r > 1)
         st = pa.pa_pool_get_stats(tw.lib)
         assert st["num_free"] == len(tw.ref.free) and st["num_seqs"] == len(live)
     finally:
@@ -253,3 +255,38 @@ def test_tile_layout_converter_matches_the_header_formulas():
         k, v = gpu_util.pools_to_logical(kraw, vraw, d)
         want = np.arange(16)[:, None] * 1000 + np.arange(d)[None, :]
         assert np.array_equal(k[0, 0], want) and np.array_equal(v[0, 0], want)
+
+
+def test_decode_rejects_unknown_flags_before_any_launch():
+    # argument checks run on the host before anything touches the GPU: the
+    # dummy addresses below are never dereferenced
+    kv = pa.kv_view(None, None, 4, 2, 64)
+    kv.k_pool = kv.v_pool = 1 << 20
+    args = dict(out=1 << 21, q=1 << 22, kv=kv, tables=1 << 23, max_blocks=4,
+                seq_lens=1 << 24, batch=0, num_q_heads=4, scale=0.125, partition_size=512,
+                max_seq_len=64, work_items=None, n_items=0, workspace=None, workspace_bytes=0)
+    with pytest.raises(pa.PaError):
+        pa.pa_paged_attention_decode(**args, flags=2)
+    pa.pa_paged_attention_decode(**args, flags=pa.PA_DECODE_KEEP_KV)   # batch 0: nothing to do
+    pa.pa_paged_attention_decode(**args, flags=0)
+
+
+def test_pool_counts_shared_blocks():
+    lib = pa.pa_pool_create(8)
+    try:
+        pa.pa_seq_add(lib, 0)
+        pa.pa_append_slots(lib, [0], [20])                 # 2 blocks
+        assert pa.pa_pool_get_stats(lib)["num_shared"] == 0
+        pa.pa_seq_fork(lib, 0, 1)
+        assert pa.pa_pool_get_stats(lib)["num_shared"] == 2
+        pa.pa_seq_fork(lib, 0, 2)                          # ref 3: still 2 shared blocks
+        assert pa.pa_pool_get_stats(lib)["num_shared"] == 2
+        _, copies = pa.pa_append_slots(lib, [1], [1])      # copy-on-write of the partial block
+        assert len(copies) == 1 and pa.pa_pool_get_stats(lib)["num_shared"] == 2
+        pa.pa_seq_free(lib, 2)                             # the partial block is now private
+        assert pa.pa_pool_get_stats(lib)["num_shared"] == 1
+        pa.pa_seq_free(lib, 1)
+        assert pa.pa_pool_get_stats(lib)["num_shared"] == 0
+        pa.pa_pool_check(lib)
+    finally:
+        pa.pa_pool_destroy(lib)
