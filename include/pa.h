@@ -106,6 +106,8 @@ typedef struct pa_pool_stats {
   int64_t allocs;   /* blocks taken off the free list (including CoW targets) */
   int64_t frees;    /* blocks returned to the free list                       */
   int64_t cows;     /* copy-on-write copies planned                          */
+  int32_t num_evictable; /* unreferenced cached blocks (reusable, see below)  */
+  int32_t num_cached;    /* blocks holding a registered prefix                */
 } pa_pool_stats;
 
 /* Create a pool's host metadata ([yj] listing: the whole pool is known up
@@ -126,11 +128,39 @@ pa_status pa_seq_fork(pa_pool* pool, int64_t parent, int64_t child);
 
 /* Drop the request: each block's count - 1 in logical order; a block reaching
  * zero is pushed on the free stack (request finished or preempted: [ngrok]
- * scheduler; [lens] scheduler skeleton). */
+ * scheduler; [lens] scheduler skeleton), or, if it is cached (see
+ * pa_seq_register), appended to the evictable list instead. */
 pa_status pa_seq_free(pa_pool* pool, int64_t seq_id);
 
 /* Blocks pa_append_slots would take off the free list for the same arguments
  * (new blocks + copy-on-write targets).  Pure. */
+
+/* Prefix caching ([ngrok] "prefix caching": requests that begin with the same
+ * tokens share the KV blocks of that prefix; only the same tokens at the same
+ * positions count, one differing token ends the sharing, and a block is known
+ * by a hash of the previous block's hash and its own tokens).  Only full
+ * 16-token blocks are cached.
+ *
+ * pa_seq_add_cached: register a new request (PA_ERR_EXISTS if live) whose
+ *   table starts with the cached blocks matching tokens[0..n_tokens) block by
+ *   block from the first token, stopping at the first block that is not
+ *   cached.  Each hit takes one more reference (sharing as pa_seq_fork does;
+ *   an evictable block is revived).  *n_cached = 16 * hits = the request's
+ *   length; the caller appends and computes the remaining tokens.  A hash hit
+ *   counts only if the block's parent hash and tokens match exactly.
+ * pa_seq_register: make the request's full blocks within its first n_tokens
+ *   tokens (tokens = those token ids, n_tokens <= its length) findable, in
+ *   order: block i gets key hash(key of block i-1, its 16 tokens).  A block
+ *   that already has a key keeps it, and a key already held by another block
+ *   stays there.  *n_registered = blocks newly cached.
+ * A cached block whose last reference is dropped is kept as evictable.
+ * Allocation (pa_append_slots) takes the free stack first; when it is empty
+ * it evicts the block that became evictable longest ago (dropping its key).
+ * pa_num_free_blocks and the capacity checks count free + evictable blocks. */
+pa_status pa_seq_add_cached(pa_pool* pool, int64_t seq_id, const int32_t* tokens,
+                            int32_t n_tokens, int32_t* n_cached);
+pa_status pa_seq_register(pa_pool* pool, int64_t seq_id, const int32_t* tokens,
+                          int32_t n_tokens, int32_t* n_registered);
 pa_status pa_can_append(const pa_pool* pool, int32_t n, const int64_t* seq_ids,
                         const int32_t* n_new, int32_t* blocks_needed);
 
@@ -170,9 +200,14 @@ pa_status pa_pool_get_stats(const pa_pool* pool, pa_pool_stats* stats);
 /* Free stack contents from bottom to top (capacity cap, count in *n). */
 pa_status pa_free_list(const pa_pool* pool, int32_t* out, int32_t cap, int32_t* n);
 
-/* Invariants: free + referenced = num_blocks; each block's count equals the
- * number of tables holding it; each table has ceil(len/16) entries; the free
- * stack holds distinct unreferenced blocks.  PA_ERR_INTERNAL if violated. */
+/* Evictable blocks, the next to be evicted first (capacity cap, count in *n). */
+pa_status pa_evictable_list(const pa_pool* pool, int32_t* out, int32_t cap, int32_t* n);
+
+/* Invariants: free + evictable + referenced = num_blocks; each block's count
+ * equals the number of tables holding it; each table has ceil(len/16)
+ * entries; the free stack holds distinct unreferenced uncached blocks, the
+ * evictable list distinct unreferenced cached ones; the cache map and the
+ * blocks' keys agree.  PA_ERR_INTERNAL if violated. */
 pa_status pa_pool_check(const pa_pool* pool);
 
 /* Bytes one token's K and V occupy: 2 * layers * kv_heads * head_dim *

@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     pa_copy_blocks,
     pa_decode_work_items,
     pa_decode_workspace_bytes,
+    pa_evictable_list,
     pa_free_list,
     pa_kv_bytes_per_token,
     pa_num_free_blocks,
@@ -31,8 +32,10 @@ from ._lib import (  # noqa: F401
     pa_ref_count,
     pa_reshape_and_cache,
     pa_seq_add,
+    pa_seq_add_cached,
     pa_seq_fork,
     pa_seq_free,
+    pa_seq_register,
     pa_seq_table,
     status_string,
 )

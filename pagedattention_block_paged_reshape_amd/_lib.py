@@ -51,7 +51,7 @@ class pa_copy(C.Structure):
 class pa_pool_stats(C.Structure):
     _fields_ = [("num_blocks", C.c_int32), ("num_free", C.c_int32), ("num_seqs", C.c_int32),
                 ("num_shared", C.c_int32), ("allocs", C.c_int64), ("frees", C.c_int64),
-                ("cows", C.c_int64)]
+                ("cows", C.c_int64), ("num_evictable", C.c_int32), ("num_cached", C.c_int32)]
 
 
 class pa_kv_view(C.Structure):
@@ -79,6 +79,9 @@ _SIGS = {
     "pa_ref_count": (C.c_int, [_P, _I32, C.POINTER(_I32)]),
     "pa_pool_get_stats": (C.c_int, [_P, C.POINTER(pa_pool_stats)]),
     "pa_free_list": (C.c_int, [_P, _P, _I32, C.POINTER(_I32)]),
+    "pa_evictable_list": (C.c_int, [_P, _P, _I32, C.POINTER(_I32)]),
+    "pa_seq_add_cached": (C.c_int, [_P, _I64, _P, _I32, C.POINTER(_I32)]),
+    "pa_seq_register": (C.c_int, [_P, _I64, _P, _I32, C.POINTER(_I32)]),
     "pa_pool_check": (C.c_int, [_P]),
     "pa_kv_bytes_per_token": (_U64, [_I32, _I32, _I32, _I32]),
     "pa_reshape_and_cache": (C.c_int, [_P, _P, _P, _I32, pa_kv_view, _P]),
@@ -172,6 +175,26 @@ def pa_seq_fork(pool: int, parent: int, child: int) -> None:
     _check(LIB.pa_seq_fork(pool, int(parent), int(child)), "pa_seq_fork")
 
 
+def pa_seq_add_cached(pool: int, seq_id: int, tokens) -> int:
+    """New request starting with the cached blocks of ``tokens``; returns the
+    number of cached tokens (its length)."""
+    t = _host(tokens, np.int32)
+    out = _I32()
+    _check(LIB.pa_seq_add_cached(pool, int(seq_id), t.ctypes.data if len(t) else None, len(t),
+                                 C.byref(out)), "pa_seq_add_cached")
+    return out.value
+
+
+def pa_seq_register(pool: int, seq_id: int, tokens) -> int:
+    """Cache the request's full blocks within its first len(tokens) tokens;
+    returns how many blocks were newly cached."""
+    t = _host(tokens, np.int32)
+    out = _I32()
+    _check(LIB.pa_seq_register(pool, int(seq_id), t.ctypes.data if len(t) else None, len(t),
+                               C.byref(out)), "pa_seq_register")
+    return out.value
+
+
 def pa_seq_free(pool: int, seq_id: int) -> None:
     _check(LIB.pa_seq_free(pool, int(seq_id)), "pa_seq_free")
 
@@ -248,6 +271,14 @@ def pa_pool_get_stats(pool: int) -> dict:
     s = pa_pool_stats()
     _check(LIB.pa_pool_get_stats(pool, C.byref(s)), "pa_pool_get_stats")
     return {k: getattr(s, k) for k, _ in pa_pool_stats._fields_ if k != "reserved"}
+
+
+def pa_evictable_list(pool: int) -> np.ndarray:
+    n = _I32()
+    LIB.pa_evictable_list(pool, None, 0, C.byref(n))
+    buf = np.empty(max(n.value, 1), dtype=np.int32)
+    _check(LIB.pa_evictable_list(pool, buf.ctypes.data, n.value, C.byref(n)), "pa_evictable_list")
+    return buf[:n.value]
 
 
 def pa_free_list(pool: int) -> np.ndarray:

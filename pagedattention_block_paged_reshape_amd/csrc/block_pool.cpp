@@ -12,7 +12,12 @@
 //   - media.tcdigital.jp, "memory sharing for parallel sampling": shared
 //     blocks are referenced, and a new block is taken only when outputs
 //     diverge (copy-on-write).
+//   - techfeed.io ngrok summary, "prefix caching": requests starting with
+//     the same tokens share the KV blocks of that prefix; a block is
+//     identified by a hash of the previous block's hash and its own tokens,
+//     so one differing token ends the sharing from its block on.
 #include <algorithm>
+#include <array>
 #include <cstdint>
 #include <cstring>
 #include <new>
@@ -38,6 +43,17 @@ struct pa_pool {
   int32_t num_blocks = 0;
   std::vector<int32_t> free_stack;  // bottom -> top; pop from the back
   std::vector<int32_t> ref;
+  // Prefix cache (sized on first use).  A cached block is a full block whose
+  // key is the hash chain of the token prefix it ends; it keeps the parent
+  // hash and its tokens so that a hash hit is confirmed exactly.  A cached
+  // block whose last reference goes away becomes evictable (kept, oldest
+  // first in an intrusive list) instead of free.
+  std::vector<uint64_t> hash_of;    // 0 = not cached
+  std::vector<uint64_t> parent_of;
+  std::vector<std::array<int32_t, PA_BLOCK_SIZE>> tokens_of;
+  std::unordered_map<uint64_t, int32_t> cache;
+  std::vector<int32_t> ev_prev, ev_next;
+  int32_t ev_head = -1, ev_tail = -1, n_evictable = 0;
   std::unordered_map<int64_t, Seq> seqs;
   int64_t allocs = 0, frees = 0, cows = 0;
   int32_t shared = 0;  // blocks with ref > 1
@@ -52,14 +68,91 @@ struct pa_pool {
     return r == 0;
   }
 
+  bool cached(int32_t b) const { return !hash_of.empty() && hash_of[b] != 0; }
+  int32_t available() const { return static_cast<int32_t>(free_stack.size()) + n_evictable; }
+
+  void ensure_cache() {
+    if (hash_of.empty()) {
+      hash_of.assign(num_blocks, 0);
+      parent_of.assign(num_blocks, 0);
+      tokens_of.resize(num_blocks);
+      ev_prev.assign(num_blocks, -1);
+      ev_next.assign(num_blocks, -1);
+    }
+  }
+  void ev_push_back(int32_t b) {
+    ev_prev[b] = ev_tail;
+    ev_next[b] = -1;
+    if (ev_tail >= 0) ev_next[ev_tail] = b; else ev_head = b;
+    ev_tail = b;
+    ++n_evictable;
+  }
+  void ev_remove(int32_t b) {
+    if (ev_prev[b] >= 0) ev_next[ev_prev[b]] = ev_next[b]; else ev_head = ev_next[b];
+    if (ev_next[b] >= 0) ev_prev[ev_next[b]] = ev_prev[b]; else ev_tail = ev_prev[b];
+    ev_prev[b] = ev_next[b] = -1;
+    --n_evictable;
+  }
+
+  // A free block: the top of the free stack, or, when the stack is empty,
+  // the block that became evictable longest ago (its cache entry dropped).
   int32_t pop() {
-    int32_t b = free_stack.back();
-    free_stack.pop_back();
+    int32_t b;
+    if (!free_stack.empty()) {
+      b = free_stack.back();
+      free_stack.pop_back();
+    } else {
+      b = ev_head;
+      ev_remove(b);
+      cache.erase(hash_of[b]);
+      hash_of[b] = 0;
+    }
     ref[b] = 1;
     ++allocs;
     return b;
   }
+  // Drops one reference (a sequence freed); a block left unreferenced goes
+  // back to the free stack, or to the evictable list if it is cached.
+  void release(int32_t b) {
+    if (ref_down(b)) {
+      if (cached(b)) ev_push_back(b); else free_stack.push_back(b);
+      ++frees;
+    }
+  }
 };
+
+namespace {
+
+// Hash of a full block given its parent's hash (0 for the first block):
+// splitmix64 finaliser steps over the parent and each token with its slot.
+inline uint64_t mix64(uint64_t x) {
+  x ^= x >> 30;
+  x *= 0xbf58476d1ce4e5b9ULL;
+  x ^= x >> 27;
+  x *= 0x94d049bb133111ebULL;
+  x ^= x >> 31;
+  return x;
+}
+
+uint64_t block_hash(uint64_t parent, const int32_t* t) {
+  uint64_t h = mix64(parent ^ 0x9e3779b97f4a7c15ULL);
+  for (int i = 0; i < PA_BLOCK_SIZE; ++i)
+    h = mix64(h ^ static_cast<uint32_t>(t[i]) ^ (static_cast<uint64_t>(i + 1) << 32));
+  return h == 0 ? 1 : h;
+}
+
+// Cached block holding exactly (parent, tokens), or -1.
+int32_t cache_find(const pa_pool* p, uint64_t h, uint64_t parent, const int32_t* t) {
+  auto it = p->cache.find(h);
+  if (it == p->cache.end()) return -1;
+  const int32_t b = it->second;
+  if (p->parent_of[b] != parent) return -1;
+  for (int i = 0; i < PA_BLOCK_SIZE; ++i)
+    if (p->tokens_of[b][i] != t[i]) return -1;
+  return b;
+}
+
+}  // namespace
 
 namespace {
 
@@ -175,12 +268,7 @@ pa_status pa_seq_free(pa_pool* pool, int64_t seq_id) {
   if (pool == nullptr) return PA_ERR_INVALID;
   auto it = pool->seqs.find(seq_id);
   if (it == pool->seqs.end()) return PA_ERR_UNKNOWN_SEQ;
-  for (int32_t b : it->second.table) {
-    if (pool->ref_down(b)) {
-      pool->free_stack.push_back(b);
-      ++pool->frees;
-    }
-  }
+  for (int32_t b : it->second.table) pool->release(b);
   pool->seqs.erase(it);
   return PA_OK;
 }
@@ -207,7 +295,7 @@ pa_status pa_append_slots(pa_pool* pool, int32_t n, const int64_t* seq_ids,
   if (tokens > 0 && slot_mapping == nullptr) return PA_ERR_INVALID;
   if (tokens > slot_cap || ncopy > copy_cap) return PA_ERR_CAPACITY;
   if (ncopy > 0 && copies == nullptr) return PA_ERR_INVALID;
-  if (need > static_cast<int32_t>(pool->free_stack.size())) return PA_ERR_OUT_OF_BLOCKS;
+  if (need > pool->available()) return PA_ERR_OUT_OF_BLOCKS;
 
   int64_t t = 0;
   int32_t c = 0;
@@ -278,7 +366,71 @@ pa_status pa_seq_table(const pa_pool* pool, int64_t seq_id, int32_t* table, int3
 }
 
 int32_t pa_num_free_blocks(const pa_pool* pool) {
-  return pool == nullptr ? -1 : static_cast<int32_t>(pool->free_stack.size());
+  return pool == nullptr ? -1 : pool->available();
+}
+
+pa_status pa_seq_add_cached(pa_pool* pool, int64_t seq_id, const int32_t* tokens,
+                            int32_t n_tokens, int32_t* n_cached) {
+  if (pool == nullptr || n_cached == nullptr || n_tokens < 0 ||
+      (n_tokens > 0 && tokens == nullptr))
+    return PA_ERR_INVALID;
+  if (pool->seqs.count(seq_id)) return PA_ERR_EXISTS;
+  Seq s;
+  if (!pool->cache.empty()) {
+    uint64_t parent = 0;
+    for (int32_t i = 0; i + kBS <= n_tokens; i += kBS) {
+      const uint64_t h = block_hash(parent, tokens + i);
+      const int32_t b = cache_find(pool, h, parent, tokens + i);
+      if (b < 0) break;
+      if (pool->ref[b] == 0) pool->ev_remove(b);
+      pool->ref_up(b);
+      s.table.push_back(b);
+      parent = h;
+    }
+  }
+  s.len = kBS * static_cast<int32_t>(s.table.size());
+  *n_cached = s.len;
+  pool->seqs.emplace(seq_id, std::move(s));
+  return PA_OK;
+}
+
+pa_status pa_seq_register(pa_pool* pool, int64_t seq_id, const int32_t* tokens,
+                          int32_t n_tokens, int32_t* n_registered) {
+  if (pool == nullptr || n_registered == nullptr || n_tokens < 0 ||
+      (n_tokens > 0 && tokens == nullptr))
+    return PA_ERR_INVALID;
+  auto it = pool->seqs.find(seq_id);
+  if (it == pool->seqs.end()) return PA_ERR_UNKNOWN_SEQ;
+  const Seq& s = it->second;
+  if (n_tokens > s.len) return PA_ERR_INVALID;
+  pool->ensure_cache();
+  int32_t added = 0;
+  uint64_t parent = 0;
+  for (int32_t i = 0; i + kBS <= n_tokens; i += kBS) {
+    const uint64_t h = block_hash(parent, tokens + i);
+    const int32_t b = s.table[i / kBS];
+    // a block keeps the key it has; a key stays with the block that has it
+    if (!pool->cached(b) && pool->cache.find(h) == pool->cache.end()) {
+      pool->cache.emplace(h, b);
+      pool->hash_of[b] = h;
+      pool->parent_of[b] = parent;
+      std::copy(tokens + i, tokens + i + kBS, pool->tokens_of[b].begin());
+      ++added;
+    }
+    parent = h;
+  }
+  *n_registered = added;
+  return PA_OK;
+}
+
+pa_status pa_evictable_list(const pa_pool* pool, int32_t* out, int32_t cap, int32_t* n) {
+  if (pool == nullptr || n == nullptr) return PA_ERR_INVALID;
+  *n = pool->n_evictable;
+  if (pool->n_evictable > cap) return PA_ERR_CAPACITY;
+  if (pool->n_evictable > 0 && out == nullptr) return PA_ERR_INVALID;
+  int32_t k = 0;
+  for (int32_t b = pool->ev_head; b >= 0; b = pool->ev_next[b]) out[k++] = b;
+  return PA_OK;
 }
 
 pa_status pa_ref_count(const pa_pool* pool, int32_t block, int32_t* ref) {
@@ -294,6 +446,8 @@ pa_status pa_pool_get_stats(const pa_pool* pool, pa_pool_stats* stats) {
   stats->num_free = static_cast<int32_t>(pool->free_stack.size());
   stats->num_seqs = static_cast<int32_t>(pool->seqs.size());
   stats->num_shared = pool->shared;
+  stats->num_evictable = pool->n_evictable;
+  stats->num_cached = static_cast<int32_t>(pool->cache.size());
   stats->allocs = pool->allocs;
   stats->frees = pool->frees;
   stats->cows = pool->cows;
@@ -333,10 +487,31 @@ pa_status pa_pool_check(const pa_pool* pool) {
   if (shared != pool->shared) return PA_ERR_INTERNAL;
   std::vector<char> in_free(N, 0);
   for (int32_t b : pool->free_stack) {
-    if (b < 0 || b >= N || in_free[b] || pool->ref[b] != 0) return PA_ERR_INTERNAL;
+    if (b < 0 || b >= N || in_free[b] || pool->ref[b] != 0 || pool->cached(b))
+      return PA_ERR_INTERNAL;
     in_free[b] = 1;
   }
-  if (static_cast<int64_t>(pool->free_stack.size()) + referenced != N) return PA_ERR_INTERNAL;
+  // evictable: unreferenced cached blocks, each once, links consistent
+  int64_t evictable = 0;
+  for (int32_t b = pool->ev_head, prev = -1; b >= 0; prev = b, b = pool->ev_next[b]) {
+    if (b >= N || in_free[b] || pool->ref[b] != 0 || !pool->cached(b) || pool->ev_prev[b] != prev)
+      return PA_ERR_INTERNAL;
+    in_free[b] = 1;
+    if (++evictable > N) return PA_ERR_INTERNAL;
+    if (pool->ev_next[b] < 0 && pool->ev_tail != b) return PA_ERR_INTERNAL;
+  }
+  if (evictable != pool->n_evictable) return PA_ERR_INTERNAL;
+  if (static_cast<int64_t>(pool->free_stack.size()) + evictable + referenced != N)
+    return PA_ERR_INTERNAL;
+  // the cache map and the per-block keys agree
+  int64_t keyed = 0;
+  for (int32_t b = 0; b < N; ++b) {
+    if (!pool->cached(b)) continue;
+    ++keyed;
+    auto it = pool->cache.find(pool->hash_of[b]);
+    if (it == pool->cache.end() || it->second != b) return PA_ERR_INTERNAL;
+  }
+  if (keyed != static_cast<int64_t>(pool->cache.size())) return PA_ERR_INTERNAL;
   return PA_OK;
 }
 

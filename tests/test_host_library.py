@@ -290,3 +290,111 @@ def test_pool_counts_shared_blocks():
         pa.pa_pool_check(lib)
     finally:
         pa.pa_pool_destroy(lib)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_prefix_cache_programs_match_oracle_exactly(seed):
+    """add_cached / append / register / fork / free on a small pool and a
+    small token alphabet (many shared prefixes, evictions), compared with the
+    oracle model after every operation."""
+    from oracle.allocator import OutOfBlocks as ModelOut
+    from oracle.prefix_cache import PrefixCachingPoolModel
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(10, 30))
+    order = rng.permutation(n)
+    lib = pa.pa_pool_create(n, order)
+    ref = PrefixCachingPoolModel(n, 16, order)
+    stems = [[int(t) for t in rng.integers(0, 3, size=64)] for _ in range(3)]
+    toks = {}
+    nid = 0
+
+    def compare():
+        pa.pa_pool_check(lib)
+        ref.check()
+        assert pa.pa_free_list(lib).tolist() == ref.free
+        assert pa.pa_evictable_list(lib).tolist() == ref.evictable
+        st = pa.pa_pool_get_stats(lib)
+        assert st["num_evictable"] == len(ref.evictable)
+        assert st["num_cached"] == len(ref.cache)
+        assert st["num_shared"] == sum(1 for r in ref.ref if r > 1)
+        assert pa.pa_num_free_blocks(lib) == ref.num_free()
+        for s in ref.tables:
+            tab, ln = pa.pa_seq_table(lib, s)
+            assert tab.tolist() == ref.tables[s] and ln == ref.lens[s]
+
+    def append(s, k):
+        new = [int(t) for t in rng.integers(0, 3, size=k)]
+        try:
+            exp = ref.append([s], [k])
+        except ModelOut:
+            with pytest.raises(pa.OutOfBlocksError):
+                pa.pa_append_slots(lib, [s], [k])
+            return False
+        slots, copies = pa.pa_append_slots(lib, [s], [k])
+        assert slots.tolist() == exp[0]
+        assert [tuple(c) for c in copies.tolist()] == exp[1]
+        toks[s] += new
+        return True
+
+    try:
+        for _ in range(200):
+            op = int(rng.integers(0, 6))
+            live = list(ref.tables)
+            if op <= 1 or not live:                       # a request arrives
+                stem = stems[int(rng.integers(0, 3))]
+                prompt = stem[:int(rng.integers(0, 65))] + \
+                    [int(t) for t in rng.integers(0, 3, size=int(rng.integers(0, 24)))]
+                hit = ref.add_cached(nid, prompt)
+                assert pa.pa_seq_add_cached(lib, nid, prompt) == hit
+                toks[nid] = prompt[:hit]
+                rest = prompt[hit:]
+                if rest:
+                    try:
+                        exp = ref.append([nid], [len(rest)])
+                    except ModelOut:
+                        with pytest.raises(pa.OutOfBlocksError):
+                            pa.pa_append_slots(lib, [nid], [len(rest)])
+                    else:
+                        slots, copies = pa.pa_append_slots(lib, [nid], [len(rest)])
+                        assert slots.tolist() == exp[0]
+                        assert [tuple(c) for c in copies.tolist()] == exp[1]
+                        toks[nid] += rest
+                if int(rng.integers(0, 4)):
+                    assert pa.pa_seq_register(lib, nid, toks[nid]) == ref.register(nid, toks[nid])
+                nid += 1
+            elif op == 2:
+                s = int(rng.choice(live))
+                append(s, int(rng.integers(1, 20)))
+            elif op == 3:
+                s = int(rng.choice(live))
+                k = int(rng.integers(0, len(toks[s]) + 1))
+                assert pa.pa_seq_register(lib, s, toks[s][:k]) == ref.register(s, toks[s][:k])
+            elif op == 4:
+                p = int(rng.choice(live))
+                pa.pa_seq_fork(lib, p, nid)
+                ref.fork(p, nid)
+                toks[nid] = list(toks[p])
+                nid += 1
+            else:
+                s = int(rng.choice(live))
+                pa.pa_seq_free(lib, s)
+                ref.free_seq(s)
+                del toks[s]
+            compare()
+    finally:
+        pa.pa_pool_destroy(lib)
+
+
+def test_prefix_cache_register_rejects_more_tokens_than_held():
+    lib = pa.pa_pool_create(4)
+    try:
+        pa.pa_seq_add(lib, 0)
+        pa.pa_append_slots(lib, [0], [20])
+        with pytest.raises(pa.PaError):
+            pa.pa_seq_register(lib, 0, list(range(21)))
+        with pytest.raises(pa.PaError):
+            pa.pa_seq_add_cached(lib, 0, list(range(16)))     # live id
+        assert pa.pa_seq_register(lib, 0, list(range(20))) == 1
+        assert pa.pa_seq_add_cached(lib, 1, list(range(20))) == 16
+    finally:
+        pa.pa_pool_destroy(lib)
