@@ -19,7 +19,9 @@ Sources (web pages on vLLM / PagedAttention; cited by page title and section):
     contiguous-waste example, PagedAttention manager, copy-on-write prefix
     sharing.
   * ngrok summary, "prefix caching" section: blocks shared by hash chain of
-    the token prefix (oracle/prefix_cache.py).
+    the token prefix (oracle/prefix_cache.py); scheduler section and
+    ta-paperlens "scheduler skeleton": continuous batching with decode
+    first, chunked prefill and preemption (oracle/scheduler.py).
 
 Every function is pinned by tests/test_oracle_*.py against values the pages
 print, closed forms, library routines (torch CPU fp64 SDPA) and brute force.
@@ -27,6 +29,7 @@ No part of it is "parity unpinned".
 """
 from .allocator import BlockPoolModel, OutOfBlocks  # noqa: F401
 from .prefix_cache import PrefixCachingPoolModel  # noqa: F401
+from .scheduler import SchedulerModel  # noqa: F401
 from .pool import PoolModel  # noqa: F401
 from .attention import (  # noqa: F401
     decode_attention,

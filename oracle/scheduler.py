@@ -1,0 +1,169 @@
+"""Oracle model of the continuous-batching scheduler around the paged cache.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``).
+
+What it follows:
+  * ngrok summary, scheduler section: every forward pass the scheduler picks
+    the tokens of the batch within a token budget, requests that are already
+    running (decoding) first, then waiting requests' prefill while budget is
+    left; a very long prompt is split into chunks that fit the budget
+    (chunked prefill); when KV blocks run out, the request added most
+    recently is preempted: its blocks are freed, it goes back to the head of
+    the waiting queue and its tokens are computed again later.
+  * ta-paperlens, "scheduler skeleton": admit from the waiting queue while the
+    head can be allocated; step every running request; drop finished ones and
+    free their blocks; while out of blocks, preempt running[-1].
+
+Readings (the pages leave these open):
+  * A request is (prompt length, output length).  Its input is the prompt
+    followed by its generated tokens; one step processes a chunk of its
+    not-yet-computed input.  When a step computes the last input token, the
+    request produces one new token (counted in ``generated``); it is done
+    when generated == output length, and is then freed at the end of the
+    step.
+  * Order inside a step: running requests in admission order, those whose
+    whole input but the newest token is computed (decode: 1 token) before
+    those still in prefill (a chunk of min(remaining, budget left)); then
+    waiting requests in queue order, each admitted only if the pool can hold
+    the blocks of its first chunk and fewer than ``max_running`` run.  A
+    running request that gets no budget simply waits (it keeps its blocks).
+  * Block reservation is one append of all the step's chunks in that order.
+    If it does not fit, the most recently admitted running request is
+    preempted (freed, its computed count reset to 0, put at the head of the
+    waiting queue, removed from this step) and the reservation retried;
+    requests admitted in this very step count as running for this.
+  * A preempted request recomputes prompt + generated tokens from position 0
+    (recompute mode).
+"""
+from __future__ import annotations
+
+from collections import deque
+from dataclasses import dataclass, field
+from typing import Deque, Dict, List, Tuple
+
+from .allocator import BlockPoolModel, OutOfBlocks
+
+
+@dataclass
+class Req:
+    rid: int
+    prompt: int
+    out: int
+    computed: int = 0
+    generated: int = 0
+    preemptions: int = 0
+
+    @property
+    def total(self) -> int:
+        return self.prompt + self.generated
+
+
+@dataclass
+class StepPlan:
+    items: List[Tuple[int, int, int, int]] = field(default_factory=list)  # rid, start, n, decode
+    slots: List[int] = field(default_factory=list)
+    copies: List[Tuple[int, int, int]] = field(default_factory=list)
+    preempted: List[int] = field(default_factory=list)
+    admitted: List[int] = field(default_factory=list)
+
+
+class SchedulerModel:
+    def __init__(self, pool: BlockPoolModel, token_budget: int, max_running: int):
+        if token_budget < 1 or max_running < 1:
+            raise ValueError("budget and max_running must be positive")
+        self.pool = pool
+        self.budget = int(token_budget)
+        self.max_running = int(max_running)
+        self.reqs: Dict[int, Req] = {}
+        self.waiting: Deque[int] = deque()
+        self.running: List[int] = []
+        self.finished: List[int] = []
+        self.last: StepPlan = StepPlan()
+
+    def add_request(self, rid: int, prompt: int, out: int) -> None:
+        """A request that could not fit the pool even alone (its prompt and
+        all but its last output token) is refused: it would be preempted
+        forever."""
+        if rid in self.reqs or prompt < 1 or out < 1:
+            raise ValueError("bad request")
+        if self._blocks_for_new(prompt + out - 1) > self.pool.num_blocks:
+            raise ValueError("request larger than the pool")
+        self.reqs[rid] = Req(rid, int(prompt), int(out))
+        self.waiting.append(rid)
+
+    def _blocks_for_new(self, n: int) -> int:
+        return -(-n // self.pool.block_size)
+
+    def schedule(self) -> StepPlan:
+        """Plan one step: which chunks run, their slots, copies, preemptions."""
+        plan = StepPlan()
+        budget = self.budget
+        chunks: List[Tuple[int, int]] = []      # (rid, n) in reservation order
+        for rid in self.running:                 # decode first
+            r = self.reqs[rid]
+            if r.total - r.computed == 1 and r.computed >= r.prompt and budget > 0:
+                chunks.append((rid, 1))
+                budget -= 1
+        for rid in self.running:                 # then prefill chunks of running requests
+            r = self.reqs[rid]
+            if not (r.total - r.computed == 1 and r.computed >= r.prompt) and budget > 0:
+                n = min(r.total - r.computed, budget)
+                chunks.append((rid, n))
+                budget -= n
+        free = self.pool.num_free()
+        need_running = self.pool.blocks_needed([c[0] for c in chunks], [c[1] for c in chunks]) \
+            if chunks else 0
+        spare = free - need_running
+        while self.waiting and budget > 0 and len(self.running) < self.max_running:
+            r = self.reqs[self.waiting[0]]
+            n = min(r.total - r.computed, budget)
+            blocks = self._blocks_for_new(n)
+            if blocks > spare:
+                break
+            self.waiting.popleft()
+            self.pool.add(r.rid)
+            self.running.append(r.rid)
+            plan.admitted.append(r.rid)
+            chunks.append((r.rid, n))
+            budget -= n
+            spare -= blocks
+        while True:
+            try:
+                slots, copies = self.pool.append([c[0] for c in chunks], [c[1] for c in chunks])
+                break
+            except OutOfBlocks:
+                victim = self.running.pop()
+                v = self.reqs[victim]
+                self.pool.free_seq(victim)
+                v.computed = 0
+                v.preemptions += 1
+                self.waiting.appendleft(victim)
+                plan.preempted.append(victim)
+                chunks = [c for c in chunks if c[0] != victim]
+                if victim in plan.admitted:
+                    plan.admitted.remove(victim)
+        for rid, n in chunks:
+            r = self.reqs[rid]
+            decode = int(r.computed >= r.prompt)
+            plan.items.append((rid, r.computed, n, decode))
+        plan.slots, plan.copies = slots, copies
+        self.last = plan
+        return plan
+
+    def commit(self) -> List[int]:
+        """The planned chunks were computed: advance, emit tokens, retire
+        finished requests (their blocks are freed).  Returns the finished ids."""
+        done = []
+        for rid, start, n, _ in self.last.items:
+            r = self.reqs[rid]
+            r.computed = start + n
+            if r.computed == r.total:
+                r.generated += 1
+                if r.generated == r.out:
+                    done.append(rid)
+        for rid in done:
+            self.running.remove(rid)
+            self.pool.free_seq(rid)
+            self.finished.append(rid)
+        self.last = StepPlan()
+        return done
