@@ -210,6 +210,72 @@ pa_status pa_evictable_list(const pa_pool* pool, int32_t* out, int32_t cap, int3
  * blocks' keys agree.  PA_ERR_INTERNAL if violated. */
 pa_status pa_pool_check(const pa_pool* pool);
 
+/* Continuous-batching scheduler over a pool ([ngrok] scheduler section;
+ * [lens] "scheduler skeleton").  Host only; it drives the pool through the
+ * calls above and the caller runs the kernels for each planned step.
+ *
+ * A request is (prompt_len, output_len).  Its input is the prompt followed by
+ * its generated tokens; each step computes a chunk of its not-yet-computed
+ * input, and a step that computes its last input token yields one new token.
+ * It finishes when output_len tokens are out; its blocks are freed then.
+ *
+ * pa_sched_schedule plans one step within token_budget tokens:
+ *   1. running requests (admission order) with exactly their newest token
+ *      left (decode, 1 token) first;
+ *   2. then running requests still in prefill: a chunk of
+ *      min(remaining input, budget left) (chunked prefill);
+ *   3. then waiting requests in queue order while budget is left, fewer than
+ *      max_running run and the pool can hold the blocks of their first
+ *      chunk (admission);
+ *   4. all chunks are reserved with one pa_append_slots in that order; while
+ *      it reports PA_ERR_OUT_OF_BLOCKS, the most recently admitted running
+ *      request is preempted: its blocks are freed, it returns to the head of
+ *      the waiting queue with nothing computed (it recomputes prompt and
+ *      generated tokens later) and leaves this step.
+ * items[i] = {request, first position, token count, decode?} in reservation
+ * order; slot_mapping / copies are pa_append_slots' outputs for them;
+ * preempted lists the preempted requests.  Capacities must be at least
+ * max_running (items, copies, preempted) and token_budget (slots), else
+ * PA_ERR_CAPACITY with nothing changed.  One plan at a time: the next
+ * schedule needs a pa_sched_commit.
+ * pa_sched_commit: the planned chunks were computed; advance the requests,
+ * free the finished ones and list them in finished (capacity >= items).
+ * A request whose prompt and output (but the last token) exceed the pool is
+ * refused by pa_sched_add_request (PA_ERR_INVALID): it could never finish. */
+typedef struct pa_sched pa_sched;
+
+typedef struct pa_sched_item {
+  int64_t req_id;
+  int32_t start;     /* first input position of the chunk                 */
+  int32_t n_tokens;  /* chunk length                                       */
+  int32_t decode;    /* 1: the request's single newest token after its prompt */
+  int32_t reserved;
+} pa_sched_item;
+
+typedef struct pa_sched_stats {
+  int32_t n_waiting;
+  int32_t n_running;
+  int64_t steps;
+  int64_t preemptions;
+  int64_t finished;
+} pa_sched_stats;
+
+pa_status pa_sched_create(pa_pool* pool, int32_t token_budget, int32_t max_running,
+                          pa_sched** out);
+void pa_sched_destroy(pa_sched* sched);
+pa_status pa_sched_add_request(pa_sched* sched, int64_t req_id, int32_t prompt_len,
+                               int32_t output_len);
+pa_status pa_sched_schedule(pa_sched* sched, pa_sched_item* items, int32_t item_cap,
+                            int32_t* n_items, int32_t* slot_mapping, int64_t slot_cap,
+                            pa_copy* copies, int32_t copy_cap, int32_t* n_copies,
+                            int64_t* preempted, int32_t preempt_cap, int32_t* n_preempted);
+pa_status pa_sched_commit(pa_sched* sched, int64_t* finished, int32_t cap,
+                          int32_t* n_finished);
+pa_status pa_sched_get_stats(const pa_sched* sched, pa_sched_stats* stats);
+/* One request's progress: input tokens computed, outputs so far, preemptions. */
+pa_status pa_sched_request(const pa_sched* sched, int64_t req_id, int32_t* computed,
+                           int32_t* generated, int32_t* preemptions);
+
 /* Bytes one token's K and V occupy: 2 * layers * kv_heads * head_dim *
  * dtype_bytes ([lens] KV-size example: 131,072 for 32/8/128/fp16). */
 uint64_t pa_kv_bytes_per_token(int32_t layers, int32_t num_kv_heads, int32_t head_dim,

@@ -144,7 +144,7 @@ class SchedulerModel:
                     plan.admitted.remove(victim)
         for rid, n in chunks:
             r = self.reqs[rid]
-            decode = int(r.computed >= r.prompt)
+            decode = int(n == 1 and r.computed >= r.prompt)   # the newest token only
             plan.items.append((rid, r.computed, n, decode))
         plan.slots, plan.copies = slots, copies
         self.last = plan

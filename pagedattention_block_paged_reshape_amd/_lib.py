@@ -48,6 +48,16 @@ class pa_copy(C.Structure):
     _fields_ = [("src", C.c_int32), ("dst", C.c_int32), ("n_slots", C.c_int32)]
 
 
+class pa_sched_item(C.Structure):
+    _fields_ = [("req_id", C.c_int64), ("start", C.c_int32), ("n_tokens", C.c_int32),
+                ("decode", C.c_int32), ("reserved", C.c_int32)]
+
+
+class pa_sched_stats(C.Structure):
+    _fields_ = [("n_waiting", C.c_int32), ("n_running", C.c_int32), ("steps", C.c_int64),
+                ("preemptions", C.c_int64), ("finished", C.c_int64)]
+
+
 class pa_pool_stats(C.Structure):
     _fields_ = [("num_blocks", C.c_int32), ("num_free", C.c_int32), ("num_seqs", C.c_int32),
                 ("num_shared", C.c_int32), ("allocs", C.c_int64), ("frees", C.c_int64),
@@ -82,6 +92,14 @@ _SIGS = {
     "pa_evictable_list": (C.c_int, [_P, _P, _I32, C.POINTER(_I32)]),
     "pa_seq_add_cached": (C.c_int, [_P, _I64, _P, _I32, C.POINTER(_I32)]),
     "pa_seq_register": (C.c_int, [_P, _I64, _P, _I32, C.POINTER(_I32)]),
+    "pa_sched_create": (C.c_int, [_P, _I32, _I32, C.POINTER(_P)]),
+    "pa_sched_destroy": (None, [_P]),
+    "pa_sched_add_request": (C.c_int, [_P, _I64, _I32, _I32]),
+    "pa_sched_schedule": (C.c_int, [_P, _P, _I32, C.POINTER(_I32), _P, C.c_int64, _P, _I32,
+                                    C.POINTER(_I32), _P, _I32, C.POINTER(_I32)]),
+    "pa_sched_commit": (C.c_int, [_P, _P, _I32, C.POINTER(_I32)]),
+    "pa_sched_get_stats": (C.c_int, [_P, C.POINTER(pa_sched_stats)]),
+    "pa_sched_request": (C.c_int, [_P, _I64, C.POINTER(_I32), C.POINTER(_I32), C.POINTER(_I32)]),
     "pa_pool_check": (C.c_int, [_P]),
     "pa_kv_bytes_per_token": (_U64, [_I32, _I32, _I32, _I32]),
     "pa_reshape_and_cache": (C.c_int, [_P, _P, _P, _I32, pa_kv_view, _P]),
@@ -271,6 +289,60 @@ def pa_pool_get_stats(pool: int) -> dict:
     s = pa_pool_stats()
     _check(LIB.pa_pool_get_stats(pool, C.byref(s)), "pa_pool_get_stats")
     return {k: getattr(s, k) for k, _ in pa_pool_stats._fields_ if k != "reserved"}
+
+
+def pa_sched_create(pool: int, token_budget: int, max_running: int) -> int:
+    out = _P()
+    _check(LIB.pa_sched_create(pool, int(token_budget), int(max_running), C.byref(out)),
+           "pa_sched_create")
+    return out.value
+
+
+def pa_sched_destroy(sched: int) -> None:
+    LIB.pa_sched_destroy(sched)
+
+
+def pa_sched_add_request(sched: int, req_id: int, prompt_len: int, output_len: int) -> None:
+    _check(LIB.pa_sched_add_request(sched, int(req_id), int(prompt_len), int(output_len)),
+           "pa_sched_add_request")
+
+
+def pa_sched_schedule(sched: int, token_budget: int, max_running: int) -> dict:
+    """Plan one step; buffers are sized from the scheduler's own limits."""
+    items = (pa_sched_item * max_running)()
+    slots = np.empty(max(token_budget, 1), dtype=np.int32)
+    copies = np.empty((max(max_running, 1), 3), dtype=np.int32)
+    pre = np.empty(max(max_running, 1), dtype=np.int64)
+    ni, nc, npre = _I32(), _I32(), _I32()
+    _check(LIB.pa_sched_schedule(sched, items, max_running, C.byref(ni), slots.ctypes.data,
+                                 token_budget, copies.ctypes.data, max_running, C.byref(nc),
+                                 pre.ctypes.data, max_running, C.byref(npre)),
+           "pa_sched_schedule")
+    its = [(items[i].req_id, items[i].start, items[i].n_tokens, items[i].decode)
+           for i in range(ni.value)]
+    n_slots = sum(it[2] for it in its)
+    return {"items": its, "slots": slots[:n_slots].copy(), "copies": copies[:nc.value].copy(),
+            "preempted": pre[:npre.value].tolist()}
+
+
+def pa_sched_commit(sched: int, cap: int) -> list:
+    out = np.empty(max(cap, 1), dtype=np.int64)
+    n = _I32()
+    _check(LIB.pa_sched_commit(sched, out.ctypes.data, int(cap), C.byref(n)), "pa_sched_commit")
+    return out[:n.value].tolist()
+
+
+def pa_sched_get_stats(sched: int) -> dict:
+    st = pa_sched_stats()
+    _check(LIB.pa_sched_get_stats(sched, C.byref(st)), "pa_sched_get_stats")
+    return {k: getattr(st, k) for k, _ in pa_sched_stats._fields_}
+
+
+def pa_sched_request(sched: int, req_id: int):
+    c, g, p = _I32(), _I32(), _I32()
+    _check(LIB.pa_sched_request(sched, int(req_id), C.byref(c), C.byref(g), C.byref(p)),
+           "pa_sched_request")
+    return c.value, g.value, p.value
 
 
 def pa_evictable_list(pool: int) -> np.ndarray:

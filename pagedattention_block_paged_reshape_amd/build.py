@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libpagedattn.so")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["cache_ops.hip", "decode.hip", "prefill.hip"]
-HOST_SOURCES = ["block_pool.cpp", "decode_plan.cpp"]
+HOST_SOURCES = ["block_pool.cpp", "decode_plan.cpp", "scheduler.cpp"]
 
 # Packed-FP32 VALU ops are kept out of the generated code.
 HIPCC_FLAGS = [

@@ -398,3 +398,70 @@ def test_prefix_cache_register_rejects_more_tokens_than_held():
         assert pa.pa_seq_add_cached(lib, 1, list(range(20))) == 16
     finally:
         pa.pa_pool_destroy(lib)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_scheduler_matches_oracle_exactly(seed):
+    """Random arrivals on a small pool (preemptions happen): every step's
+    chunks, slots, preemptions and finished requests equal the model's."""
+    from oracle.scheduler import SchedulerModel
+    rng = np.random.default_rng(200 + seed)
+    n = int(rng.integers(16, 80))
+    order = rng.permutation(n)
+    budget = int(rng.integers(4, 300))
+    max_running = int(rng.integers(1, 16))
+    pool = pa.pa_pool_create(n, order)
+    sched = pa.pa_sched_create(pool, budget, max_running)
+    model = SchedulerModel(BlockPoolModel(n, 16, order), budget, max_running)
+    rid = 0
+    preemptions = 0
+    try:
+        for step in range(100000):
+            if step < 150:
+                for _ in range(int(rng.integers(0, 3))):
+                    prompt = int(rng.integers(1, 16 * max(1, n // 3)))
+                    out = int(rng.integers(1, 40))
+                    model.add_request(rid, prompt, out)
+                    pa.pa_sched_add_request(sched, rid, prompt, out)
+                    rid += 1
+            exp = model.schedule()
+            got = pa.pa_sched_schedule(sched, budget, max_running)
+            assert got["items"] == [tuple(i) for i in exp.items], step
+            assert got["slots"].tolist() == exp.slots
+            assert [tuple(c) for c in got["copies"].tolist()] == exp.copies
+            assert got["preempted"] == exp.preempted
+            preemptions += len(exp.preempted)
+            assert pa.pa_sched_commit(sched, max_running) == model.commit()
+            pa.pa_pool_check(pool)
+            assert pa.pa_free_list(pool).tolist() == model.pool.free
+            st = pa.pa_sched_get_stats(sched)
+            assert st["n_waiting"] == len(model.waiting) and st["n_running"] == len(model.running)
+            if step >= 150 and not model.waiting and not model.running:
+                break
+        assert st["finished"] == rid == len(model.finished)
+        for r in range(rid):
+            m = model.reqs[r]
+            assert pa.pa_sched_request(sched, r) == (m.computed, m.generated, m.preemptions)
+    finally:
+        pa.pa_sched_destroy(sched)
+        pa.pa_pool_destroy(pool)
+
+
+def test_scheduler_argument_checks():
+    pool = pa.pa_pool_create(4)
+    sched = pa.pa_sched_create(pool, 16, 2)
+    try:
+        with pytest.raises(pa.PaError):
+            pa.pa_sched_add_request(sched, 0, 60, 6)          # 65 tokens > 4 blocks
+        pa.pa_sched_add_request(sched, 0, 60, 5)
+        with pytest.raises(pa.PaError):
+            pa.pa_sched_add_request(sched, 0, 1, 1)           # duplicate id
+        with pytest.raises(pa.PaError):
+            pa.pa_sched_schedule(sched, 8, 2)                 # slot buffer below the budget
+        pa.pa_sched_schedule(sched, 16, 2)
+        with pytest.raises(pa.PaError):
+            pa.pa_sched_schedule(sched, 16, 2)                # previous plan not committed
+        pa.pa_sched_commit(sched, 2)
+    finally:
+        pa.pa_sched_destroy(sched)
+        pa.pa_pool_destroy(pool)
