@@ -1,0 +1,150 @@
+"""Multi-step serving loop: the C++ scheduler (pa_sched_*) plans each step,
+and this loop runs the step's kernels on the GPU.
+
+Per step ([lens] "scheduler skeleton": admit, step all running requests,
+retire finished ones, preempt when out of blocks; [ngrok] scheduler section):
+  1. pa_sched_schedule: chunks (request, first position, length) within the
+     token budget, decode first, their KV slots, and any preemptions;
+  2. the step's new K/V rows (a synthetic model: rows are a fixed function of
+     request and position, see synth.serving) go to their slots with
+     pa_reshape_and_cache;
+  3. decode chunks (one new token each) attend their requests' whole
+     sequences in one pa_paged_attention_decode launch; prefill chunks each
+     get a pa_paged_attention_prefill launch (causal over the cache);
+  4. pa_sched_commit retires finished requests and frees their blocks.
+This module only marshals arguments and launches; every step of the path
+runs in the library.
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Optional, Tuple
+
+import numpy as np
+import torch
+
+from . import _lib as L
+from .cache import PagedKVCache
+
+
+class ServingLoop:
+    def __init__(self, cache: PagedKVCache, num_q_heads: int, scale: float, token_budget: int,
+                 max_running: int, partition: int = 512, row_fn=None,
+                 keep_outputs: bool = False):
+        """row_fn(req, pos, tag, width) -> fp16 rows on the cache's device
+        (int64 device tensors in); keep_outputs stores every attention
+        output row by (request, position) for checking."""
+        self.cache = cache
+        self.n_q = int(num_q_heads)
+        self.scale = float(scale)
+        self.budget = int(token_budget)
+        self.max_running = int(max_running)
+        self.partition = int(partition)
+        self.row_fn = row_fn
+        self.keep = keep_outputs
+        # (request, position) -> (output row [n_q][d], "decode" | "prefill")
+        self.outputs: Dict[Tuple[int, int], Tuple[torch.Tensor, str]] = {}
+        self.sched = L.pa_sched_create(cache.pool, self.budget, self.max_running)
+        dev = cache.device
+        self.d = cache.d
+        self.stats = {"steps": 0, "decode_tokens": 0, "prefill_tokens": 0, "preempted": 0,
+                      "finished": 0}
+        self._ws = torch.zeros(16, dtype=torch.uint8, device=dev)
+        self._pws = torch.zeros(16, dtype=torch.uint8, device=dev)
+        self.dev = dev
+
+    def close(self):
+        if self.sched:
+            L.pa_sched_destroy(self.sched)
+            self.sched = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add(self, req_id: int, prompt_len: int, output_len: int):
+        L.pa_sched_add_request(self.sched, req_id, prompt_len, output_len)
+
+    def _workspace(self, attr: str, nbytes: int) -> torch.Tensor:
+        ws = getattr(self, attr)
+        if ws.numel() < nbytes:
+            ws = torch.zeros(nbytes, dtype=torch.uint8, device=self.dev)
+            setattr(self, attr, ws)
+        return ws
+
+    def step(self, stream=None) -> List[int]:
+        """Plan and run one step; returns the requests that finished."""
+        stream = stream or torch.cuda.current_stream(self.dev)
+        plan = L.pa_sched_schedule(self.sched, self.budget, self.max_running)
+        items = plan["items"]
+        self.stats["preempted"] += len(plan["preempted"])
+        if items:
+            req = np.concatenate([np.full(n, r, dtype=np.int64) for r, _, n, _ in items])
+            pos = np.concatenate([np.arange(s, s + n, dtype=np.int64) for _, s, n, _ in items])
+            d_req = torch.from_numpy(req).to(self.dev, non_blocking=True)
+            d_pos = torch.from_numpy(pos).to(self.dev, non_blocking=True)
+            width = self.cache.n_kv * self.d
+            k = self.row_fn(d_req, d_pos, 0, width).view(-1, self.cache.n_kv, self.d)
+            v = self.row_fn(d_req, d_pos, 1, width).view(-1, self.cache.n_kv, self.d)
+            q = self.row_fn(d_req, d_pos, 2, self.n_q * self.d).view(-1, self.n_q, self.d)
+            slots = torch.from_numpy(plan["slots"]).to(self.dev, non_blocking=True)
+            if len(plan["copies"]):
+                d_copies = torch.from_numpy(np.ascontiguousarray(plan["copies"])).to(self.dev)
+                L.pa_copy_blocks(d_copies, len(plan["copies"]), self.cache.kv, stream)
+            L.pa_reshape_and_cache(k, v, slots, len(req), self.cache.kv, stream)
+            offs = np.cumsum([0] + [n for _, _, n, _ in items])
+            dec = [i for i, it in enumerate(items) if it[3]]
+            pre = [i for i, it in enumerate(items) if not it[3]]
+            if dec:
+                self._decode([items[i] for i in dec], q[torch.tensor([offs[i] for i in dec],
+                                                                      device=self.dev)], stream)
+            for i in pre:
+                r, s, n, _ = items[i]
+                self._prefill(r, s, n, q[offs[i]:offs[i] + n], stream)
+            self.stats["decode_tokens"] += len(dec)
+            self.stats["prefill_tokens"] += int(sum(items[i][2] for i in pre))
+        done = L.pa_sched_commit(self.sched, self.max_running)
+        self.stats["steps"] += 1
+        self.stats["finished"] += len(done)
+        return done
+
+    def _decode(self, items, q: torch.Tensor, stream):
+        ids = [r for r, _, _, _ in items]
+        tab, ln, max_blocks = self.cache.host_tables(ids)
+        assert [int(x) for x in ln] == [s + 1 for _, s, _, _ in items]
+        max_len = int(ln.max())
+        work = L.pa_decode_work_items(ln, self.partition)
+        ws_bytes = L.pa_decode_workspace_bytes(len(ids), self.n_q, self.d, max_len, self.partition)
+        ws = self._workspace("_ws", max(ws_bytes, 16))
+        out = torch.empty((len(ids), self.n_q, self.d), dtype=torch.float16, device=self.dev)
+        d_tab = torch.from_numpy(tab).to(self.dev, non_blocking=True)
+        d_len = torch.from_numpy(ln).to(self.dev, non_blocking=True)
+        d_work = torch.from_numpy(np.ascontiguousarray(work)).to(self.dev, non_blocking=True)
+        flags = L.PA_DECODE_KEEP_KV if self.cache.shares_blocks() else 0
+        L.pa_paged_attention_decode(out, q.contiguous(), self.cache.kv, d_tab, max_blocks, d_len,
+                                    len(ids), self.n_q, self.scale, self.partition, max_len,
+                                    d_work, len(work), ws, ws_bytes, stream, flags=flags)
+        if self.keep:
+            for j, (r, s, _, _) in enumerate(items):
+                self.outputs[(r, s)] = (out[j], "decode")
+
+    def _prefill(self, r: int, s: int, n: int, q: torch.Tensor, stream):
+        tab, ln, max_blocks = self.cache.host_tables([r])
+        assert int(ln[0]) == s + n
+        ws_bytes = L.pa_prefill_workspace_bytes(n, self.n_q, self.d, s)
+        ws = self._workspace("_pws", max(ws_bytes, 16))
+        out = torch.empty((n, self.n_q, self.d), dtype=torch.float16, device=self.dev)
+        d_tab = torch.from_numpy(np.ascontiguousarray(tab[0])).to(self.dev, non_blocking=True)
+        L.pa_paged_attention_prefill(out, q.contiguous(), self.cache.kv, d_tab, max_blocks, s, n,
+                                     self.n_q, self.scale, ws, ws_bytes, stream)
+        if self.keep:
+            for j in range(n):
+                self.outputs[(r, s + j)] = (out[j], "prefill")
+
+    def request(self, req_id: int):
+        """(computed input tokens, generated tokens, preemptions)."""
+        return L.pa_sched_request(self.sched, req_id)
+
+    def sched_stats(self) -> dict:
+        return L.pa_sched_get_stats(self.sched)
