@@ -22,6 +22,8 @@ Sources (web pages on vLLM / PagedAttention; cited by page title and section):
     the token prefix (oracle/prefix_cache.py); scheduler section and
     ta-paperlens "scheduler skeleton": continuous batching with decode
     first, chunked prefill and preemption (oracle/scheduler.py).
+  * ta-paperlens "in practice" (KV-cache dtype as a setting): the FP8 E4M3
+    codec of the FP8 KV-cache variant (oracle/fp8.py).
 
 Every function is pinned by tests/test_oracle_*.py against values the pages
 print, closed forms, library routines (torch CPU fp64 SDPA) and brute force.
@@ -30,7 +32,8 @@ No part of it is "parity unpinned".
 from .allocator import BlockPoolModel, OutOfBlocks  # noqa: F401
 from .prefix_cache import PrefixCachingPoolModel  # noqa: F401
 from .scheduler import SchedulerModel  # noqa: F401
-from .pool import PoolModel  # noqa: F401
+from . import fp8  # noqa: F401
+from .pool import Fp8PoolModel, PoolModel  # noqa: F401
 from .attention import (  # noqa: F401
     decode_attention,
     decode_attention_one,

@@ -21,6 +21,8 @@ from typing import Iterable, Tuple
 
 import numpy as np
 
+from . import fp8
+
 
 class PoolModel:
     def __init__(self, num_blocks: int, n_kv: int, d: int, block_size: int = 16):
@@ -65,3 +67,40 @@ class PoolModel:
             k[pos:pos + n] = self.k[blk, :, :n, :].transpose(1, 0, 2)
             v[pos:pos + n] = self.v[blk, :, :n, :].transpose(1, 0, 2)
         return k, v
+
+
+class Fp8PoolModel(PoolModel):
+    """The same pool holding one E4M3 code per value (the FP8 KV-cache
+    variant): a stored row is ``fp8.quantize(row, scale)`` with one scale for
+    the K pool and one for the V pool; copies and gathers move codes."""
+
+    def __init__(self, num_blocks: int, n_kv: int, d: int, k_scale: float, v_scale: float,
+                 block_size: int = 16):
+        super().__init__(num_blocks, n_kv, d, block_size)
+        self.k_scale, self.v_scale = float(k_scale), float(v_scale)
+        self.k = np.zeros((num_blocks, n_kv, block_size, d), dtype=np.uint8)
+        self.v = np.zeros((num_blocks, n_kv, block_size, d), dtype=np.uint8)
+
+    def write(self, k_rows, v_rows, slots) -> None:
+        super().write(fp8.quantize(k_rows, self.k_scale), fp8.quantize(v_rows, self.v_scale),
+                      slots)
+
+    def write_bulk(self, k_rows, v_rows, slots) -> None:
+        super().write_bulk(fp8.quantize(k_rows, self.k_scale), fp8.quantize(v_rows, self.v_scale),
+                           slots)
+
+    def gather(self, table, length: int):
+        """Codes of one request's logical K and V, [length][n_kv][d] uint8."""
+        k = np.empty((length, self.n_kv, self.d), dtype=np.uint8)
+        v = np.empty((length, self.n_kv, self.d), dtype=np.uint8)
+        for pos in range(0, length, self.bs):
+            blk = table[pos // self.bs]
+            n = min(self.bs, length - pos)
+            k[pos:pos + n] = self.k[blk, :, :n, :].transpose(1, 0, 2)
+            v[pos:pos + n] = self.v[blk, :, :n, :].transpose(1, 0, 2)
+        return k, v
+
+    def gather_values(self, table, length: int):
+        """The fp64 values the codes stand for (code value times scale)."""
+        k, v = self.gather(table, length)
+        return fp8.dequantize(k, self.k_scale), fp8.dequantize(v, self.v_scale)
