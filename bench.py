@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark: paged decode attention on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--kv-dtype fp8]
 
 A step is one pass of the whole decode hot path for the batch: reserve one
 slot per request on the host block manager, store the step's new K/V into the
@@ -17,7 +17,9 @@ Prints one JSON line.  ``value`` is decode tokens/s per layer (requests
 advanced per second).  ``roofline`` reports the decode launch (work-list +
 reduce kernels, timed with HIP events on the stream they run on) against the
 8 TB/s HBM peak using algorithmic bytes: every K and V byte of every attended
-token once per KV head, plus Q, O, block tables and lengths.
+token once per KV head, plus Q, O, block tables and lengths.  With
+``--kv-dtype fp8`` the pools hold E4M3 codes (one byte per value, one scale
+per pool) and the same step runs the FP8 store and decode entry points.
 """
 from __future__ import annotations
 
@@ -40,7 +42,10 @@ MFMA_F16_PEAK_TFLOPS = 2500.0
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["pagedattention_block_paged_reshape_amd/csrc/decode.hip",
                   "pagedattention_block_paged_reshape_amd/csrc/pa_device.h"]
-TRAFFIC_FILE = os.path.join(PROFILES, "decode_llama3-70b_traffic.md")
+TRAFFIC_FILES = {"fp16": os.path.join(PROFILES, "decode_llama3-70b_traffic.md"),
+                 "fp8": os.path.join(PROFILES, "decode_llama3-70b_fp8_traffic.md")}
+# FP8 pools: one scale per pool, about max |x| / 448 for the N(0, 1) rows
+FP8_K_SCALE, FP8_V_SCALE = 5.5 / 448, 4.75 / 448
 
 
 def log(msg):
@@ -55,12 +60,13 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic():
+def recorded_traffic(kv_dtype: str = "fp16"):
     """HBM bytes per decode launch from the committed rocprofv3 counter
     summary, if it was taken on the current kernel sources."""
-    if not os.path.exists(TRAFFIC_FILE):
+    path = TRAFFIC_FILES[kv_dtype]
+    if not os.path.exists(path):
         return None
-    text = open(TRAFFIC_FILE).read()
+    text = open(path).read()
     m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
     m_bytes = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
@@ -68,20 +74,20 @@ def recorded_traffic():
     return float(m_bytes.group(1))
 
 
-def algorithmic_decode_bytes(lens, n_q, n_kv, d) -> int:
+def algorithmic_decode_bytes(lens, n_q, n_kv, d, kv_bytes: int = 2) -> int:
     lens = np.asarray(lens, dtype=np.int64)
-    kv = int(lens.sum()) * 2 * n_kv * d * 2              # K and V once per KV head
+    kv = int(lens.sum()) * 2 * n_kv * d * kv_bytes       # K and V once per KV head
     qo = 2 * len(lens) * n_q * d * 2                     # Q in, O out (fp16)
     tables = 4 * int(((lens + 15) // 16).sum())          # block ids read
     return kv + qo + tables + 4 * len(lens)              # + lengths
 
 
-def cpu_baseline(w, budget_s: float, steps_done: int):
+def cpu_baseline(w, budget_s: float, steps_done: int, kv_dtype: str = "fp16"):
     """The fp64 oracle (as written, untuned) doing the same decode step:
     append one token per request, store its K/V, attend over every request."""
     from oracle import decode_reference, run_setup
     log("[bench] cpu_baseline: building the oracle's pool model (not timed)")
-    st = run_setup(w)
+    st = run_setup(w, kv_dtype=kv_dtype, k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE)
     ids, ones = w.step_ids.tolist(), [1] * w.batch
     for _ in range(steps_done):                  # reach the GPU's final lengths
         st.alloc.append(ids, ones)
@@ -108,7 +114,8 @@ def cpu_baseline(w, budget_s: float, steps_done: int):
         "cores": max(1, int(round(cpu / el))),
         "kind": "oracle",
         "sample": f"{reps} full decode steps of the same workload ({w.batch} requests each: "
-                  f"append + store + fp64 attention) in {el:.1f} s wall; BLAS pool "
+                  f"append + store{' (E4M3 encode)' if kv_dtype == 'fp8' else ''} + fp64 "
+                  f"attention) in {el:.1f} s wall; BLAS pool "
                   f"{blas} threads, cpu/wall = {cpu / el:.2f}",
     }
 
@@ -348,6 +355,9 @@ def main():
                          "runs at its sustained clocks")
     ap.add_argument("--config", default="3", help="decode workload (2, 3, 4 or 5)")
     ap.add_argument("--partition", type=int, default=512)
+    ap.add_argument("--kv-dtype", choices=["fp16", "fp8"], default="fp16",
+                    help="KV pool type of the decode step: fp16, or FP8 E4M3 codes with one "
+                         "scale per pool")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush-mb", type=int, default=0,
@@ -393,7 +403,9 @@ def main():
     extra = w.batch * (total_steps // 16 + 2)
     free_order = np.concatenate([np.arange(w.num_blocks, w.num_blocks + extra, dtype=np.int32),
                                  np.asarray(w.free_order, dtype=np.int32)])
-    cache = PagedKVCache(w.num_blocks + extra, w.n_kv, w.d, free_order, dev)
+    fp8 = args.kv_dtype == "fp8"
+    cache = PagedKVCache(w.num_blocks + extra, w.n_kv, w.d, free_order, dev,
+                         kv_dtype=args.kv_dtype, k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE)
     log("[bench] uploading and storing the cached K/V through reshape_and_cache")
     dk = torch.from_numpy(w.setup_k).to(dev)
     dv = torch.from_numpy(w.setup_v).to(dev)
@@ -434,7 +446,8 @@ def main():
         if flush is not None:
             flush_sink = flush.sum()
         stepper.step(q, step_k, step_v, stream, events=ev[i])
-        bytes_per_step.append(algorithmic_decode_bytes(stepper.last_lens, w.n_q, w.n_kv, w.d))
+        bytes_per_step.append(algorithmic_decode_bytes(stepper.last_lens, w.n_q, w.n_kv, w.d,
+                                                       1 if fp8 else 2))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
@@ -459,12 +472,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp16",
+        "dtype": "fp8-e4m3 kv, fp16 q/o, fp32 accumulate" if fp8 else "fp16",
         "data": "synthetic",
         "config": {
             "workload": f"config {args.config} ({w.name}): B={w.batch}, {w.n_q}/{w.n_kv} heads, "
                         f"head_dim {w.d}, block 16, pool {w.num_blocks} blocks scattered (+{extra} spare), "
-                        f"split-K partition {args.partition} + reduce",
+                        f"split-K partition {args.partition} + reduce"
+                        + (f", FP8 E4M3 KV pools (scales {FP8_K_SCALE:.6g}, {FP8_V_SCALE:.6g})"
+                           if fp8 else ""),
+            "kv_dtype": args.kv_dtype,
             "batch": w.batch,
             "mean_context": round(float(np.mean(stepper.last_lens)), 1),
             "partition": args.partition,
@@ -477,8 +493,9 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": recorded_traffic(),
-            "kernel": "pa_paged_attention_decode (decode_worklist_kernel + decode_reduce_kernel)",
+            "traffic": recorded_traffic(args.kv_dtype),
+            "kernel": ("pa_paged_attention_decode_fp8" if fp8 else "pa_paged_attention_decode")
+                      + " (decode_worklist_kernel + decode_reduce_kernel)",
             "algorithmic_bytes_per_launch": int(dec_bytes),
             "launch_us_mean": round(float(dec_ms.mean()) * 1e3, 2),
             "launch_us_p50": round(float(np.median(dec_ms)) * 1e3, 2),
@@ -491,7 +508,7 @@ def main():
     if not args.no_cpu_baseline:
         del cache, stepper
         torch.cuda.empty_cache()
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, total_steps)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, total_steps, args.kv_dtype)
     print(json.dumps(result), flush=True)
 
 

@@ -13,7 +13,8 @@
  *             block mapping", "memory sharing for parallel sampling".
  *   [lens]    ta-paperlens "LLM serving from scratch", "prefill and decode",
  *             eq. (1) and the KV-size example, "fragmentation and
- *             PagedAttention", FIG 1, "scheduler skeleton".
+ *             PagedAttention", FIG 1, "scheduler skeleton", "in practice".
+ *   [sns]     sns.style vLLM overview article, "deep dive".
  *   [yj]      youngju.dev "vLLM inference optimization", "KV Cache problem",
  *             "PagedAttention" (block diagram, PagedAttentionManager listing),
  *             "copy-on-write prefix sharing".
@@ -365,6 +366,61 @@ pa_status pa_paged_attention_decode(pa_half* out, const pa_half* q, pa_kv_view k
                                     const int32_t* work_items, int32_t n_items,
                                     void* workspace, uint64_t workspace_bytes, uint32_t flags,
                                     void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* FP8 KV cache                                                              */
+/* ------------------------------------------------------------------------ */
+/* A smaller KV data type as a serving setting ([lens] "in practice": it
+ * shrinks K/V, so the same memory holds more tokens and more requests; [sns]
+ * "deep dive": FP8 among the supported formats).  The pages fix neither the
+ * format nor the scale; this library reads them as:
+ *   - each value is one OCP FP8 E4M3 byte (sign, 4 exponent bits with bias 7,
+ *     3 mantissa bits; exponent 0 subnormal; 0x7F/0xFF NaN; largest 448);
+ *   - one fp32 scale per pool: an fp16 value x is stored as
+ *     e4m3(clamp(fp32(x) * fp32(1/k_scale), -448, 448)), the product rounded
+ *     to fp32 and then to E4M3 by round-to-nearest-even (NaN stays NaN,
+ *     +-inf saturate to +-448); code c stands for value(c) * k_scale (V alike).
+ * FP8 pools have the fp16 pools' [num_blocks][num_kv_heads][tile] shape with
+ * 16*D one-byte values per tile (tile (b, h) at byte (b*H + h)*16*D), ordered
+ * so that each 16-byte-per-lane load brings two MFMA operands:
+ *   K tile [D/64][4][16][2][8]: slot s, dim c at byte
+ *           (c/64)*1024 + ((c/8)%4)*256 + s*16 + ((c/32)%2)*8 + c%8
+ *   V tile [D/64][4][16][2][2][4]: slot s, dim c at byte
+ *           (c/64)*1024 + (s/4)*256 + (c%16)*16 + ((c/32)%2)*8 + ((c/16)%2)*4 + s%4
+ * (D = 64 or 128). */
+typedef struct pa_kv_view_fp8 {
+  uint8_t* k_pool;       /* device, E4M3 codes, layout above */
+  uint8_t* v_pool;       /* device, E4M3 codes, layout above */
+  int32_t num_blocks;
+  int32_t block_size;    /* must be PA_BLOCK_SIZE */
+  int32_t num_kv_heads;  /* >= 1 */
+  int32_t head_dim;      /* 64 or 128 */
+  float k_scale;         /* > 0, finite */
+  float v_scale;         /* > 0, finite */
+} pa_kv_view_fp8;
+
+/* pa_reshape_and_cache into FP8 pools: the same slots and arguments, each
+ * value quantised as above (k with k_scale, v with v_scale); the host computes
+ * 1/scale in fp32 once per call. */
+pa_status pa_reshape_and_cache_fp8(const pa_half* k, const pa_half* v,
+                                   const int32_t* slot_mapping, int32_t num_tokens,
+                                   pa_kv_view_fp8 kv, void* stream);
+
+/* pa_copy_blocks for FP8 pools (bit copy of slots [0, n_slots) of K and V). */
+pa_status pa_copy_blocks_fp8(const pa_copy* copies, int32_t n, pa_kv_view_fp8 kv, void* stream);
+
+/* pa_paged_attention_decode over FP8 pools: the same arguments, work list,
+ * workspace (pa_decode_workspace_bytes) and flags; K_j and V_j are the values
+ * the codes stand for.  The codes are widened to fp16 exactly, k_scale joins
+ * the softmax exponent's factor (scale * k_scale) and v_scale multiplies each
+ * partition's normalised output; everything else is the fp16 kernels' math. */
+pa_status pa_paged_attention_decode_fp8(pa_half* out, const pa_half* q, pa_kv_view_fp8 kv,
+                                        const int32_t* tables, int32_t max_blocks,
+                                        const int32_t* seq_lens, int32_t batch,
+                                        int32_t num_q_heads, float scale, int32_t partition_size,
+                                        int32_t max_seq_len, const int32_t* work_items,
+                                        int32_t n_items, void* workspace,
+                                        uint64_t workspace_bytes, uint32_t flags, void* stream);
 
 /* Workspace bytes pa_paged_attention_prefill needs for a chunk of chunk_len
  * query rows ending at key position q_start + chunk_len. */

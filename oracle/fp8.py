@@ -59,12 +59,22 @@ def encode_e4m3(x) -> np.ndarray:
     return np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
 
 
-def quantize(x16, scale: float) -> np.ndarray:
-    """Codes of fp16 values x16 under a per-pool scale: f32(x) * f32(1/scale)
-    (both fp32 roundings), then ``encode_e4m3``."""
+def quantize_table(scale: float) -> np.ndarray:
+    """Code of every fp16 bit pattern under a per-pool scale: f32(x) *
+    f32(1/scale) (both fp32 roundings), then ``encode_e4m3``; entry i is the
+    code of the fp16 value whose bits are i."""
     inv = np.float32(1.0) / np.float32(scale)
-    y = np.asarray(x16, dtype=np.float16).astype(np.float32) * inv
+    x = np.arange(65536, dtype=np.uint16).view(np.float16).astype(np.float32)
+    with np.errstate(invalid="ignore", over="ignore"):   # NaN and inf patterns
+        y = x * inv
     return encode_e4m3(y.astype(np.float64))
+
+
+def quantize(x16, scale: float) -> np.ndarray:
+    """Codes of fp16 values x16: the code depends only on the value's bits and
+    the scale, so it is looked up in ``quantize_table(scale)``."""
+    bits = np.ascontiguousarray(np.asarray(x16, dtype=np.float16)).view(np.uint16)
+    return quantize_table(scale)[bits]
 
 
 def dequantize(codes, scale: float) -> np.ndarray:

@@ -68,6 +68,11 @@ class PoolModel:
             v[pos:pos + n] = self.v[blk, :, :n, :].transpose(1, 0, 2)
         return k, v
 
+    def gather_values(self, table, length: int):
+        """The logical K and V as fp64 values."""
+        k, v = self.gather(table, length)
+        return k.astype(np.float64), v.astype(np.float64)
+
 
 class Fp8PoolModel(PoolModel):
     """The same pool holding one E4M3 code per value (the FP8 KV-cache

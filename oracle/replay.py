@@ -18,7 +18,7 @@ import numpy as np
 
 from .allocator import BlockPoolModel
 from .attention import decode_attention_one, prefill_chunk_attention
-from .pool import PoolModel
+from .pool import Fp8PoolModel, PoolModel
 
 
 @dataclass
@@ -30,9 +30,17 @@ class OracleState:
     step_copies: List[Tuple[int, int, int]] = None
 
 
-def run_setup(w, bulk: bool = True) -> OracleState:
+def run_setup(w, bulk: bool = True, kv_dtype: str = "fp16", k_scale: float = 1.0,
+              v_scale: float = 1.0) -> OracleState:
+    """``kv_dtype="fp8"`` stores E4M3 codes under the given per-pool scales
+    (the FP8 KV-cache variant); attention then sees the values they stand for."""
     alloc = BlockPoolModel(w.num_blocks, 16, w.free_order)
-    pool = PoolModel(w.num_blocks, w.n_kv, w.d)
+    if kv_dtype == "fp8":
+        pool = Fp8PoolModel(w.num_blocks, w.n_kv, w.d, k_scale, v_scale)
+    elif kv_dtype == "fp16":
+        pool = PoolModel(w.num_blocks, w.n_kv, w.d)
+    else:
+        raise ValueError(kv_dtype)
     cursor = 0
     all_slots: List[int] = []
     for op in w.setup:
@@ -74,7 +82,7 @@ def decode_reference(w, st: OracleState, seq_index=None) -> np.ndarray:
     outs = []
     for i in idx:
         sid = int(w.decode_ids[i])
-        k, v = st.pool.gather(st.alloc.tables[sid], st.alloc.lens[sid])
+        k, v = st.pool.gather_values(st.alloc.tables[sid], st.alloc.lens[sid])
         outs.append(decode_attention_one(w.q[i], k, v, w.scale))
     return np.stack(outs)
 
@@ -82,5 +90,5 @@ def decode_reference(w, st: OracleState, seq_index=None) -> np.ndarray:
 def prefill_reference(w, st: OracleState, rows=None, heads=None) -> np.ndarray:
     pf = w.prefill
     sid = pf.seq_id
-    k, v = st.pool.gather(st.alloc.tables[sid], st.alloc.lens[sid])
+    k, v = st.pool.gather_values(st.alloc.tables[sid], st.alloc.lens[sid])
     return prefill_chunk_attention(pf.q, k, v, pf.q_start, w.scale, rows=rows, heads=heads)

@@ -69,6 +69,12 @@ class pa_kv_view(C.Structure):
                 ("block_size", C.c_int32), ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32)]
 
 
+class pa_kv_view_fp8(C.Structure):
+    _fields_ = [("k_pool", C.c_void_p), ("v_pool", C.c_void_p), ("num_blocks", C.c_int32),
+                ("block_size", C.c_int32), ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+                ("k_scale", C.c_float), ("v_scale", C.c_float)]
+
+
 # name -> (restype, argtypes)
 _P = C.c_void_p
 _I32 = C.c_int32
@@ -109,6 +115,11 @@ _SIGS = {
     "pa_paged_attention_decode": (C.c_int, [_P, _P, pa_kv_view, _P, _I32, _P, _I32, _I32,
                                             C.c_float, _I32, _I32, _P, _I32, _P, _U64, C.c_uint32,
                                             _P]),
+    "pa_reshape_and_cache_fp8": (C.c_int, [_P, _P, _P, _I32, pa_kv_view_fp8, _P]),
+    "pa_copy_blocks_fp8": (C.c_int, [_P, _I32, pa_kv_view_fp8, _P]),
+    "pa_paged_attention_decode_fp8": (C.c_int, [_P, _P, pa_kv_view_fp8, _P, _I32, _P, _I32, _I32,
+                                                C.c_float, _I32, _I32, _P, _I32, _P, _U64,
+                                                C.c_uint32, _P]),
     "pa_prefill_workspace_bytes": (_U64, [_I32, _I32, _I32, _I32]),
     "pa_paged_attention_prefill": (C.c_int, [_P, _P, pa_kv_view, _P, _I32, _I32, _I32, _I32,
                                              C.c_float, _P, _U64, _P]),
@@ -376,6 +387,12 @@ def kv_view(k_pool, v_pool, num_blocks: int, num_kv_heads: int, head_dim: int) -
                       int(num_kv_heads), int(head_dim))
 
 
+def kv_view_fp8(k_pool, v_pool, num_blocks: int, num_kv_heads: int, head_dim: int,
+                k_scale: float, v_scale: float) -> pa_kv_view_fp8:
+    return pa_kv_view_fp8(_dptr(k_pool), _dptr(v_pool), int(num_blocks), BLOCK_SIZE,
+                          int(num_kv_heads), int(head_dim), float(k_scale), float(v_scale))
+
+
 def pa_reshape_and_cache(k, v, slot_mapping, num_tokens: int, kv: pa_kv_view, stream=None) -> None:
     _check(LIB.pa_reshape_and_cache(_dptr(k), _dptr(v), _dptr(slot_mapping), int(num_tokens), kv,
                                     _stream(stream)), "pa_reshape_and_cache")
@@ -383,6 +400,17 @@ def pa_reshape_and_cache(k, v, slot_mapping, num_tokens: int, kv: pa_kv_view, st
 
 def pa_copy_blocks(copies, n: int, kv: pa_kv_view, stream=None) -> None:
     _check(LIB.pa_copy_blocks(_dptr(copies), int(n), kv, _stream(stream)), "pa_copy_blocks")
+
+
+def pa_reshape_and_cache_fp8(k, v, slot_mapping, num_tokens: int, kv: pa_kv_view_fp8,
+                             stream=None) -> None:
+    _check(LIB.pa_reshape_and_cache_fp8(_dptr(k), _dptr(v), _dptr(slot_mapping), int(num_tokens),
+                                        kv, _stream(stream)), "pa_reshape_and_cache_fp8")
+
+
+def pa_copy_blocks_fp8(copies, n: int, kv: pa_kv_view_fp8, stream=None) -> None:
+    _check(LIB.pa_copy_blocks_fp8(_dptr(copies), int(n), kv, _stream(stream)),
+           "pa_copy_blocks_fp8")
 
 
 def pa_decode_workspace_bytes(batch: int, num_q_heads: int, head_dim: int, max_seq_len: int,
@@ -419,6 +447,18 @@ def pa_paged_attention_decode(out, q, kv: pa_kv_view, tables, max_blocks: int, s
                                          _dptr(work_items), int(n_items), _dptr(workspace),
                                          int(workspace_bytes), int(flags), _stream(stream)),
            "pa_paged_attention_decode")
+
+
+def pa_paged_attention_decode_fp8(out, q, kv: pa_kv_view_fp8, tables, max_blocks: int, seq_lens,
+                                  batch: int, num_q_heads: int, scale: float, partition_size: int,
+                                  max_seq_len: int, work_items, n_items: int, workspace,
+                                  workspace_bytes: int, stream=None, flags: int = 0) -> None:
+    _check(LIB.pa_paged_attention_decode_fp8(_dptr(out), _dptr(q), kv, _dptr(tables),
+                                             int(max_blocks), _dptr(seq_lens), int(batch),
+                                             int(num_q_heads), float(scale), int(partition_size),
+                                             int(max_seq_len), _dptr(work_items), int(n_items),
+                                             _dptr(workspace), int(workspace_bytes), int(flags),
+                                             _stream(stream)), "pa_paged_attention_decode_fp8")
 
 
 def pa_prefill_workspace_bytes(chunk_len: int, num_q_heads: int, head_dim: int,

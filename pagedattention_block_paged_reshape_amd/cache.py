@@ -26,22 +26,37 @@ DEFAULT_PARTITION = 512
 
 
 class PagedKVCache:
+    """``kv_dtype`` "fp16" (default) or "fp8": E4M3 codes with one scale per
+    pool (``k_scale``, ``v_scale``), half the bytes per token; fp16 rows are
+    quantised as they are stored."""
+
     def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int,
                  free_order: Optional[Sequence[int]] = None, device="cuda:0",
-                 fill_byte: Optional[int] = None):
+                 fill_byte: Optional[int] = None, kv_dtype: str = "fp16",
+                 k_scale: float = 1.0, v_scale: float = 1.0):
+        if kv_dtype not in ("fp16", "fp8"):
+            raise ValueError(f"kv_dtype must be 'fp16' or 'fp8', not {kv_dtype!r}")
         self.num_blocks = int(num_blocks)
         self.n_kv = int(num_kv_heads)
         self.d = int(head_dim)
         self.device = torch.device(device)
+        self.kv_dtype = kv_dtype
+        self.fp8 = kv_dtype == "fp8"
+        self.k_scale, self.v_scale = float(k_scale), float(v_scale)
         self.pool = L.pa_pool_create(self.num_blocks, free_order)
         # [block][kv head][tile of 16 slots x d values, in the library's operand order]
         shape = (self.num_blocks, self.n_kv, L.BLOCK_SIZE * self.d)
-        self.k_pool = torch.empty(shape, dtype=torch.float16, device=self.device)
-        self.v_pool = torch.empty(shape, dtype=torch.float16, device=self.device)
+        dt = torch.uint8 if self.fp8 else torch.float16
+        self.k_pool = torch.empty(shape, dtype=dt, device=self.device)
+        self.v_pool = torch.empty(shape, dtype=dt, device=self.device)
         if fill_byte is not None:
             self.k_pool.view(torch.uint8).fill_(fill_byte)
             self.v_pool.view(torch.uint8).fill_(fill_byte)
-        self.kv = L.kv_view(self.k_pool, self.v_pool, self.num_blocks, self.n_kv, self.d)
+        if self.fp8:
+            self.kv = L.kv_view_fp8(self.k_pool, self.v_pool, self.num_blocks, self.n_kv, self.d,
+                                    self.k_scale, self.v_scale)
+        else:
+            self.kv = L.kv_view(self.k_pool, self.v_pool, self.num_blocks, self.n_kv, self.d)
 
     def close(self):
         if self.pool:
@@ -73,6 +88,28 @@ class PagedKVCache:
     def seq_len(self, seq_id: int) -> int:
         return L.pa_seq_table(self.pool, seq_id)[1]
 
+    # -- device calls of this pool's type ------------------------------------
+    def store(self, k_rows, v_rows, d_slots, n: int, stream) -> None:
+        """pa_reshape_and_cache (fp16 pools) or pa_reshape_and_cache_fp8."""
+        fn = L.pa_reshape_and_cache_fp8 if self.fp8 else L.pa_reshape_and_cache
+        fn(k_rows, v_rows, d_slots, n, self.kv, stream)
+
+    def copy_blocks(self, d_copies, n: int, stream) -> None:
+        """pa_copy_blocks (fp16 pools) or pa_copy_blocks_fp8."""
+        fn = L.pa_copy_blocks_fp8 if self.fp8 else L.pa_copy_blocks
+        fn(d_copies, n, self.kv, stream)
+
+    def decode(self, out, q, tables, max_blocks, lens, batch, n_q, scale, partition, max_len,
+               items, n_items, workspace, ws_bytes, stream, flags=0) -> None:
+        """pa_paged_attention_decode (fp16 pools) or pa_paged_attention_decode_fp8."""
+        fn = L.pa_paged_attention_decode_fp8 if self.fp8 else L.pa_paged_attention_decode
+        fn(out, q, self.kv, tables, max_blocks, lens, batch, n_q, scale, partition, max_len,
+           items, n_items, workspace, ws_bytes, stream, flags=flags)
+
+    def require_fp16(self, what: str) -> None:
+        if self.fp8:
+            raise NotImplementedError(f"{what} reads fp16 pools only")
+
     # -- one append: reserve, copy-on-write, store --------------------------
     def append(self, seq_ids, n_new, k_rows: torch.Tensor, v_rows: torch.Tensor,
                stream: Optional[torch.cuda.Stream] = None):
@@ -88,10 +125,10 @@ class PagedKVCache:
             if len(copies):
                 d_copies = torch.from_numpy(np.ascontiguousarray(copies)).to(
                     self.device, non_blocking=False)
-                L.pa_copy_blocks(d_copies, len(copies), self.kv, stream)
+                self.copy_blocks(d_copies, len(copies), stream)
             if T:
                 d_slots = torch.from_numpy(slots).to(self.device, non_blocking=False)
-                L.pa_reshape_and_cache(k_rows, v_rows, d_slots, T, self.kv, stream)
+                self.store(k_rows, v_rows, d_slots, T, stream)
         return slots, copies
 
     def tables(self, seq_ids, max_blocks: Optional[int] = None):
@@ -144,12 +181,11 @@ class DecodePlan:
             (self.batch, self.n_q, cache.d), dtype=torch.float16, device=cache.device)
 
     def run(self, q: torch.Tensor, stream=None) -> torch.Tensor:
-        L.pa_paged_attention_decode(self.out, q, self.cache.kv, self.tables, self.max_blocks,
-                                    self.lens, self.batch, self.n_q, self.scale, self.partition,
-                                    self.max_len, self.items, self.n_items, self.workspace,
-                                    self.ws_bytes,
-                                    stream or torch.cuda.current_stream(self.cache.device),
-                                    flags=self.flags)
+        self.cache.decode(self.out, q, self.tables, self.max_blocks, self.lens, self.batch,
+                          self.n_q, self.scale, self.partition, self.max_len, self.items,
+                          self.n_items, self.workspace, self.ws_bytes,
+                          stream or torch.cuda.current_stream(self.cache.device),
+                          flags=self.flags)
         return self.out
 
 
@@ -158,6 +194,7 @@ class PrefillPlan:
 
     def __init__(self, cache: PagedKVCache, seq_id: int, q_start: int, chunk_len: int,
                  num_q_heads: int, scale: float):
+        cache.require_fp16("pa_paged_attention_prefill")
         self.cache = cache
         tab, _, self.seq_len, self.table_len = cache.tables([seq_id])
         self.table = tab[0].contiguous()

@@ -8,7 +8,10 @@
 // parallel sampling").  Both are bit copies.
 //
 // Pool layout (see include/pa.h): [N][H][tile], tiles in MFMA operand order
-// (k_tile_off / v_tile_off).
+// (k_tile_off / v_tile_off; FP8 pools k8_tile_off / v8_tile_off).
+//
+// FP8 pools (ta-paperlens "in practice": a smaller KV data type as a serving
+// setting) store OCP E4M3 codes with one scale per pool.
 #include "pa_device.h"
 
 namespace pa {
@@ -66,12 +69,99 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(const pa_copy* __restr
   }
 }
 
+// FP8 pools: the value times the fp32 reciprocal of the pool's scale, clamped
+// to the E4M3 range by comparisons (so NaN passes through), converted with
+// round-to-nearest-even.  Two values go into the low (hi = false) or high
+// 16 bits of `w`, first value in the lower byte.
+__device__ __forceinline__ float clamp_e4m3(float x) {
+  return x > 448.0f ? 448.0f : (x < -448.0f ? -448.0f : x);
+}
+template <bool HI>
+__device__ __forceinline__ uint32_t pack_e4m3x2(f16 a, f16 b, float inv, uint32_t w) {
+  const float x = clamp_e4m3(static_cast<float>(a) * inv);
+  const float y = clamp_e4m3(static_cast<float>(b) * inv);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(x, y, static_cast<int>(w), HI));
+}
+// Eight values as eight codes, element e in byte e.
+__device__ __forceinline__ uint2 quantize8(f16x8 v, float inv) {
+  uint2 r;
+  r.x = pack_e4m3x2<false>(v[0], v[1], inv, 0u);
+  r.x = pack_e4m3x2<true>(v[2], v[3], inv, r.x);
+  r.y = pack_e4m3x2<false>(v[4], v[5], inv, 0u);
+  r.y = pack_e4m3x2<true>(v[6], v[7], inv, r.y);
+  return r;
+}
+
+// The fp16 kernel's thread mapping: the 8 K codes of a chunk are contiguous
+// in the FP8 tile (one 8-byte store); the 8 V codes land 16 bytes apart.
+template <int D>
+__global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
+    const f16* __restrict__ k, const f16* __restrict__ v, const int32_t* __restrict__ slots,
+    int32_t num_tokens, int32_t n_kv, int32_t num_blocks, float k_inv, float v_inv,
+    uint8_t* __restrict__ kp, uint8_t* __restrict__ vp) {
+  constexpr int kChunks = D / 8;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t total = static_cast<int64_t>(num_tokens) * n_kv * kChunks;
+  if (idx >= total) return;
+  const int chunk = static_cast<int>(idx % kChunks);
+  const int64_t th = idx / kChunks;
+  const int h = static_cast<int>(th % n_kv);
+  const int64_t t = th / n_kv;
+  const int32_t s = slots[t];
+  if (s < 0 || s >= num_blocks * kBlock) return;
+  const int64_t blk = s / kBlock;
+  const int off = s % kBlock;
+  const int64_t src = (t * n_kv + h) * D + chunk * 8;
+  const uint2 kc = quantize8(*reinterpret_cast<const f16x8*>(k + src), k_inv);
+  const uint2 vc = quantize8(*reinterpret_cast<const f16x8*>(v + src), v_inv);
+  const int64_t tile = (blk * n_kv + h) * (kBlock * D);
+  *reinterpret_cast<uint2*>(kp + tile + k8_tile_off(off, chunk * 8)) = kc;
+  uint8_t* vt = vp + tile + v8_tile_off(off, chunk * 8);
+#pragma unroll
+  for (int e = 0; e < 8; ++e)  // dims chunk*8 + e: same 16-dim half, 16 bytes apart
+    vt[e * 16] = static_cast<uint8_t>((e < 4 ? vc.x : vc.y) >> (8 * (e & 3)));
+}
+
+// Copy-on-write copy in FP8 pools: slots [0, n) as 8-byte K runs and single
+// V bytes.
+template <int D>
+__global__ __launch_bounds__(256) void copy_blocks_fp8_kernel(const pa_copy* __restrict__ copies,
+                                                              int32_t n_kv, int32_t num_blocks,
+                                                              uint8_t* __restrict__ kp,
+                                                              uint8_t* __restrict__ vp) {
+  const pa_copy c = copies[blockIdx.x];
+  const int h = blockIdx.y;
+  if (c.src < 0 || c.src >= num_blocks || c.dst < 0 || c.dst >= num_blocks) return;
+  if (c.n_slots <= 0 || c.n_slots > kBlock || c.src == c.dst) return;
+  const int n = c.n_slots;
+  const int64_t st = (static_cast<int64_t>(c.src) * n_kv + h) * (kBlock * D);
+  const int64_t dt = (static_cast<int64_t>(c.dst) * n_kv + h) * (kBlock * D);
+  for (int i = threadIdx.x; i < n * (D / 8); i += blockDim.x) {
+    const int off = k8_tile_off(i % n, (i / n) * 8);
+    *reinterpret_cast<uint2*>(kp + dt + off) = *reinterpret_cast<const uint2*>(kp + st + off);
+  }
+  for (int i = threadIdx.x; i < n * D; i += blockDim.x) {
+    const int off = v8_tile_off(i % n, i / n);
+    vp[dt + off] = vp[st + off];
+  }
+}
+
 static bool valid_view(const pa_kv_view& kv) {
   return kv.k_pool != nullptr && kv.v_pool != nullptr && kv.num_blocks > 0 &&
          static_cast<int64_t>(kv.num_blocks) * kBlock < (1LL << 31) &&
          kv.block_size == kBlock && kv.num_kv_heads > 0 &&
          (kv.head_dim == 64 || kv.head_dim == 128) && aligned16(kv.k_pool) &&
          aligned16(kv.v_pool);
+}
+
+static bool valid_scale(float x) { return x > 0.0f && x <= 3.0e38f; }
+
+static bool valid_view(const pa_kv_view_fp8& kv) {
+  return kv.k_pool != nullptr && kv.v_pool != nullptr && kv.num_blocks > 0 &&
+         static_cast<int64_t>(kv.num_blocks) * kBlock < (1LL << 31) &&
+         kv.block_size == kBlock && kv.num_kv_heads > 0 &&
+         (kv.head_dim == 64 || kv.head_dim == 128) && aligned16(kv.k_pool) &&
+         aligned16(kv.v_pool) && valid_scale(kv.k_scale) && valid_scale(kv.v_scale);
 }
 
 }  // namespace pa
@@ -117,5 +207,47 @@ extern "C" pa_status pa_copy_blocks(const pa_copy* copies, int32_t n, pa_kv_view
   else
     copy_blocks_kernel<64><<<grid, dim3(256), 0, s>>>(copies, kv.num_kv_heads, kv.num_blocks,
                                                       kp, vp);
+  return launch_status();
+}
+
+extern "C" pa_status pa_reshape_and_cache_fp8(const pa_half* k, const pa_half* v,
+                                              const int32_t* slot_mapping, int32_t num_tokens,
+                                              pa_kv_view_fp8 kv, void* stream) {
+  if (!valid_view(kv) || num_tokens < 0) return PA_ERR_INVALID;
+  if (num_tokens == 0) return PA_OK;
+  if (k == nullptr || v == nullptr || slot_mapping == nullptr || !aligned16(k) || !aligned16(v))
+    return PA_ERR_INVALID;
+  const int64_t total = static_cast<int64_t>(num_tokens) * kv.num_kv_heads * (kv.head_dim / 8);
+  const int64_t blocks = (total + 255) / 256;
+  if (blocks > INT32_MAX) return PA_ERR_INVALID;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const f16* kk = reinterpret_cast<const f16*>(k);
+  const f16* vv = reinterpret_cast<const f16*>(v);
+  const float k_inv = 1.0f / kv.k_scale;  // fp32, once per call
+  const float v_inv = 1.0f / kv.v_scale;
+  if (kv.head_dim == 128)
+    reshape_and_cache_fp8_kernel<128><<<dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s>>>(
+        kk, vv, slot_mapping, num_tokens, kv.num_kv_heads, kv.num_blocks, k_inv, v_inv,
+        kv.k_pool, kv.v_pool);
+  else
+    reshape_and_cache_fp8_kernel<64><<<dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s>>>(
+        kk, vv, slot_mapping, num_tokens, kv.num_kv_heads, kv.num_blocks, k_inv, v_inv,
+        kv.k_pool, kv.v_pool);
+  return launch_status();
+}
+
+extern "C" pa_status pa_copy_blocks_fp8(const pa_copy* copies, int32_t n, pa_kv_view_fp8 kv,
+                                        void* stream) {
+  if (!valid_view(kv) || n < 0) return PA_ERR_INVALID;
+  if (n == 0) return PA_OK;
+  if (copies == nullptr || kv.num_kv_heads > 65535) return PA_ERR_INVALID;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(static_cast<uint32_t>(n), static_cast<uint32_t>(kv.num_kv_heads));
+  if (kv.head_dim == 128)
+    copy_blocks_fp8_kernel<128><<<grid, dim3(256), 0, s>>>(copies, kv.num_kv_heads,
+                                                           kv.num_blocks, kv.k_pool, kv.v_pool);
+  else
+    copy_blocks_fp8_kernel<64><<<grid, dim3(256), 0, s>>>(copies, kv.num_kv_heads,
+                                                          kv.num_blocks, kv.k_pool, kv.v_pool);
   return launch_status();
 }

@@ -85,6 +85,7 @@ struct DecodeArgs {
   f16* ws_o;    // [B][n_kv][p_max][G][D] fp16
   float* ws_m;  // [B][n_kv][p_max][G]
   float* ws_l;  // [B][n_kv][p_max][G]
+  float v_scale;  // FP8 pools: the V scale, applied when a unit is normalised
 };
 
 // One wavefront's share of a unit: running max and sum per query head and
@@ -213,52 +214,140 @@ __device__ __forceinline__ f16x8 load_tile16(const f16* p) {
   return KEEP ? *q : __builtin_nontemporal_load(q);
 }
 
-template <int D, bool KEEP>
+template <bool KEEP>
+__device__ __forceinline__ u32x4 load_bytes16(const uint8_t* p) {
+  const u32x4* q = reinterpret_cast<const u32x4*>(p);
+  return KEEP ? *q : __builtin_nontemporal_load(q);
+}
+
+// One block's operand registers: K[NK] and V[NV]; a register set holds NB
+// blocks.  fp16 tiles load straight into the MFMA operands; FP8 tiles load as
+// bytes (half the registers) and are widened when computed, and a set holds
+// two blocks, so that a wavefront keeps as many bytes in flight as with fp16.
+template <int D, bool FP8>
+struct TileRegs {
+  typedef f16x8 K;
+  typedef f16x4 V;
+  static constexpr int NK = D / 32;
+  static constexpr int NV = D / 16;
+  static constexpr int NB = 1;
+};
+template <int D>
+struct TileRegs<D, true> {
+  typedef u32x4 K;  // bytes [16 lane, 16 lane + 16) of each 1 KiB K span
+  typedef u32x4 V;
+  static constexpr int NK = D / 64;
+  static constexpr int NV = D / 64;
+  static constexpr int NB = 2;
+};
+
+template <int D, bool KEEP, bool FP8>
 __device__ __forceinline__ void load_block(const DecodeArgs& a, int g, int pb, int lane,
-                                           f16x8* kd, f16x4* vd) {
+                                           typename TileRegs<D, FP8>::K* kd,
+                                           typename TileRegs<D, FP8>::V* vd) {
   const int64_t tile = (static_cast<int64_t>(pb) * a.n_kv + g) * (kBlock * D);  // uniform
-  const f16* kt = a.kp + tile + lane * 8;
-  const f16* vt = a.vp + tile + lane * 8;
+  if constexpr (FP8) {
+    // tile in bytes: lane i reads bytes [16i, 16i + 16) of each 1 KiB span
+    const uint8_t* kt = reinterpret_cast<const uint8_t*>(a.kp) + tile + lane * 16;
+    const uint8_t* vt = reinterpret_cast<const uint8_t*>(a.vp) + tile + lane * 16;
 #pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk)
-    kd[kk] = load_tile16<D, KEEP>(kt + kk * 512);
+    for (int p = 0; p < D / 64; ++p) kd[p] = load_bytes16<KEEP>(kt + p * 1024);
 #pragma unroll
-  for (int cc = 0; cc < D / 32; ++cc) {
-    const f16x8 pair = load_tile16<D, KEEP>(vt + cc * 512);
-    vd[2 * cc] = f16x4{pair[0], pair[1], pair[2], pair[3]};
-    vd[2 * cc + 1] = f16x4{pair[4], pair[5], pair[6], pair[7]};
+    for (int p = 0; p < D / 64; ++p) vd[p] = load_bytes16<KEEP>(vt + p * 1024);
+  } else {
+    const f16* kt = a.kp + tile + lane * 8;
+    const f16* vt = a.vp + tile + lane * 8;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+      kd[kk] = load_tile16<D, KEEP>(kt + kk * 512);
+#pragma unroll
+    for (int cc = 0; cc < D / 32; ++cc) {
+      const f16x8 pair = load_tile16<D, KEEP>(vt + cc * 512);
+      vd[2 * cc] = f16x4{pair[0], pair[1], pair[2], pair[3]};
+      vd[2 * cc + 1] = f16x4{pair[4], pair[5], pair[6], pair[7]};
+    }
   }
 }
 
-// Physical block behind the wave's i-th load: unit u's blocks first; past
-// them the next unit's first block (so that it is in flight during u's
-// epilogue), or, when there is none, block 0: one tile that every such
-// stand-in load shares, so it stays cached (the loads are non-temporal, so
-// re-reading u's last block would go to HBM again).
+// Four E4M3 codes (byte j of w is element j) as fp16.  Every E4M3 value is
+// exact in fp16, so with a unit scale the conversion is exact.
+__device__ __forceinline__ f16x4 e4m3x4_to_f16(uint32_t w) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 r = {
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true))};
+  return __builtin_bit_cast(f16x4, r);
+}
+
+// FP8 block registers as the fp16 operands load_block gives for fp16 tiles:
+// load p's dwords 0-1 / 2-3 are K steps 2p / 2p+1; its dword t is V dim tile
+// 4p + t.
+template <int D>
+__device__ __forceinline__ void widen(const u32x4* kr, const u32x4* vr, f16x8* kf, f16x4* vf) {
+#pragma unroll
+  for (int p = 0; p < D / 64; ++p) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const f16x4 lo = e4m3x4_to_f16(kr[p][2 * h]);
+      const f16x4 hi = e4m3x4_to_f16(kr[p][2 * h + 1]);
+      kf[2 * p + h] = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) vf[4 * p + t] = e4m3x4_to_f16(vr[p][t]);
+  }
+}
+
+// Physical block behind the wave's i-th load (slot s of its register set):
+// unit u's blocks first; past them the next unit's block s (so that it is in
+// flight during u's epilogue), or, when there is none or `zero` is set,
+// block 0: one tile that every such stand-in load shares, so it stays cached
+// (the loads are non-temporal, so re-reading u's last block would go to HBM
+// again).
 __device__ __forceinline__ int unit_block(const Unit& u, int i) {
   return i < kWave ? __builtin_amdgcn_readlane(u.my_pb, i)
                    : __builtin_amdgcn_readlane(u.my_pb2, i - kWave);
 }
 
-__device__ __forceinline__ int pick_block(const Unit& u, const Unit& nx, int i) {
+__device__ __forceinline__ int pick_block(const Unit& u, const Unit& nx, int i, int s = 0,
+                                          bool zero = false) {
   int pb;
   if (i < u.cnt)
     pb = unit_block(u, i);
-  else if (nx.cnt > 0)
-    pb = unit_block(nx, 0);
+  else if (!zero && nx.cnt > s)
+    pb = unit_block(nx, s);
   else
     pb = 0;
   return uniform(pb);
 }
 
+// Load register set (ks, vs) with the wave's blocks j0 .. j0 + NB - 1 of u.
+// A set that carries over to the next unit (`carry`, and entirely past u's
+// end) takes nx's first NB blocks; any other stand-in of a two-block set
+// reads block 0, so that no block is fetched twice.
+template <int D, bool KEEP, bool FP8>
+__device__ __forceinline__ void load_set(const DecodeArgs& a, int g, const Unit& u,
+                                         const Unit& nx, int j0, bool carry, int lane,
+                                         typename TileRegs<D, FP8>::K* ks,
+                                         typename TileRegs<D, FP8>::V* vs) {
+  typedef TileRegs<D, FP8> TR;
+#pragma unroll
+  for (int s = 0; s < TR::NB; ++s) {
+    const bool zero = TR::NB > 1 && !(carry && j0 >= u.cnt);
+    load_block<D, KEEP, FP8>(a, g, pick_block(u, nx, j0 + s, s, zero), lane, ks + s * TR::NK,
+                             vs + s * TR::NV);
+  }
+}
+
 // The wavefront's pass over its blocks of unit u on kv head g.  On entry
-// kA/vA hold u's first block (when u.cnt > 0); on exit they hold nx's first
-// block (when nx.cnt > 0).
-template <int D, bool KEEP>
+// kA/vA hold u's first NB blocks (when u.cnt > 0); on exit they hold nx's
+// first NB blocks (when nx.cnt > 0).
+template <int D, bool KEEP, bool FP8>
 __device__ __forceinline__ void run_unit(const DecodeArgs& a, int g, int wave, int lane,
                                          const Unit& u, const Unit& nx, const f16x8* qf,
-                                         f16x8* kA, f16x4* vA, f16x8* kB, f16x4* vB,
-                                         WaveState<D>& st) {
+                                         typename TileRegs<D, FP8>::K* kA,
+                                         typename TileRegs<D, FP8>::V* vA,
+                                         typename TileRegs<D, FP8>::K* kB,
+                                         typename TileRegs<D, FP8>::V* vB, WaveState<D>& st) {
   constexpr int KS = D / 32;  // K-steps of the score MFMA
   constexpr int DT = D / 16;  // 16-wide dimension tiles of the output
   const int lg = lane >> 4;   // lane group: which 8 (K) or 4 (V, P) k-values
@@ -268,7 +357,7 @@ __device__ __forceinline__ void run_unit(const DecodeArgs& a, int g, int wave, i
 #pragma unroll
   for (int c = 0; c < DT; ++c) st.o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (u.cnt == 0) {
-    if (nx.cnt > 0) load_block<D, KEEP>(a, g, pick_block(u, nx, 0), lane, kA, vA);
+    if (nx.cnt > 0) load_set<D, KEEP, FP8>(a, g, u, nx, 0, true, lane, kA, vA);
     return;
   }
   const int L = u.L;
@@ -325,15 +414,34 @@ __device__ __forceinline__ void run_unit(const DecodeArgs& a, int g, int wave, i
     for (int c = 0; c < DT; ++c) st.o[c] = mfma16x16x16(vf[c], pf, st.o[c]);
   };
 
-  // Two register sets in ping-pong: while one block is computed the next
-  // one's loads are in flight; no register copies, so the compiler's wait
-  // counts only cover the block being consumed.  Every load is
+  // FP8 tiles are widened to fp16 first (K's scale is folded into
+  // scale_log2, V's into the final normalisation).
+  auto step = [&](int i, typename TileRegs<D, FP8>::K* kr, typename TileRegs<D, FP8>::V* vr) {
+    if constexpr (FP8) {
+      f16x8 kf[KS];
+      f16x4 vf[DT];
+      widen<D>(kr, vr, kf, vf);
+      compute(i, kf, vf);
+    } else {
+      compute(i, kr, vr);
+    }
+  };
+
+  // Two register sets in ping-pong: while one set's blocks are computed the
+  // other's loads are in flight; no register copies, so the compiler's wait
+  // counts only cover the blocks being consumed.  Every load is
   // unconditional (pick_block), the last one into kA/vA being nx's first.
-  for (int i = 0; i < u.cnt; i += 2) {
-    load_block<D, KEEP>(a, g, pick_block(u, nx, i + 1), lane, kB, vB);
-    compute(i, kA, vA);
-    load_block<D, KEEP>(a, g, pick_block(u, nx, i + 2), lane, kA, vA);
-    if (i + 1 < u.cnt) compute(i + 1, kB, vB);
+  typedef TileRegs<D, FP8> TR;
+  constexpr int NB = TR::NB;
+  for (int i = 0; i < u.cnt; i += 2 * NB) {
+    load_set<D, KEEP, FP8>(a, g, u, nx, i + NB, false, lane, kB, vB);
+#pragma unroll
+    for (int s = 0; s < NB; ++s)
+      if (s == 0 || i + s < u.cnt) step(i + s, kA + s * TR::NK, vA + s * TR::NV);
+    load_set<D, KEEP, FP8>(a, g, u, nx, i + 2 * NB, true, lane, kA, vA);
+#pragma unroll
+    for (int s = 0; s < NB; ++s)
+      if (i + NB + s < u.cnt) step(i + NB + s, kB + s * TR::NK, vB + s * TR::NV);
   }
 }
 
@@ -376,10 +484,10 @@ __device__ __forceinline__ bool post_state(const MergeSlot<D>& ms, const WaveSta
 // Merge the posted states of a unit in fixed wave order: each lane produces
 // 8 consecutive dims of one head and hands them, with the head's running max
 // and sum, to emit(h, d0, r, m, l).  An empty request reads as zeros, a
-// flagged one as NaN.
-template <int D, typename Emit>
+// flagged one as NaN.  FP8 pools scale the normalised rows by v_scale.
+template <int D, bool FP8, typename Emit>
 __device__ __forceinline__ void merge_unit(const MergeSlot<D>& ms, int G, int L, int lane,
-                                           Emit emit) {
+                                           float v_scale, Emit emit) {
   constexpr int OROW = D + 4;
   const bool any_bad =
       __hip_atomic_load(ms.bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
@@ -401,7 +509,8 @@ __device__ __forceinline__ void merge_unit(const MergeSlot<D>& ms, int G, int L,
         a1 += e * *reinterpret_cast<const f32x4*>(row + 4);
       }
     }
-    const float inv = any_bad ? __builtin_nanf("") : (L > 0 ? 1.0f / wsum : 0.0f);
+    const float inv =
+        any_bad ? __builtin_nanf("") : (L > 0 ? (FP8 ? v_scale / wsum : 1.0f / wsum) : 0.0f);
     f16x8 r;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -435,10 +544,10 @@ __device__ __forceinline__ void store_rows(const DecodeArgs& a, int g, int b, in
   }
 }
 
-template <int D>
+template <int D, bool FP8>
 __device__ __forceinline__ void merge_store(const DecodeArgs& a, const MergeSlot<D>& ms, int g,
                                             int b, int p, int L, int n_parts, int lane) {
-  merge_unit<D>(ms, a.G, L, lane, [&](int h, int d0, f16x8 r, float m, float l) {
+  merge_unit<D, FP8>(ms, a.G, L, lane, a.v_scale, [&](int h, int d0, f16x8 r, float m, float l) {
     store_rows<D>(a, g, b, p, n_parts, h, d0, r, m, l);
   });
 }
@@ -533,7 +642,7 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeArgs a) {
 }
 
 // Grid form: one workgroup per (kv head, request, partition).
-template <int D, bool KEEP>
+template <int D, bool KEEP, bool FP8>
 __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(DecodeArgs a) {
   const int g = blockIdx.x;
   const int b = blockIdx.y;
@@ -559,17 +668,19 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(Decode
   const int lane = threadIdx.x & 63;
   const Unit u = make_unit(a, b, p, wave, lane);
   const Unit nx = no_unit();
-  f16x8 qf[D / 32], kA[D / 32], kB[D / 32];
-  f16x4 vA[D / 16], vB[D / 16];
+  typedef TileRegs<D, FP8> TR;
+  f16x8 qf[D / 32];
+  typename TR::K kA[TR::NB * TR::NK], kB[TR::NB * TR::NK];
+  typename TR::V vA[TR::NB * TR::NV], vB[TR::NB * TR::NV];
   if (u.cnt > 0) {
     load_q<D>(a, g, b, lane, qf);
-    load_block<D, KEEP>(a, g, pick_block(u, nx, 0), lane, kA, vA);
+    load_set<D, KEEP, FP8>(a, g, u, nx, 0, true, lane, kA, vA);
   }
   WaveState<D> st;
-  run_unit<D, KEEP>(a, g, wave, lane, u, nx, qf, kA, vA, kB, vB, st);
+  run_unit<D, KEEP, FP8>(a, g, wave, lane, u, nx, qf, kA, vA, kB, vB, st);
   const MergeSlot<D> ms{sm_m, sm_l, reinterpret_cast<float*>(sm_o4), &sm_arrive, &sm_bad};
   if (post_state<D>(ms, st, a.G, wave, lane, u.bad))
-    merge_store<D>(a, ms, g, b, p, u.L, n_parts, lane);
+    merge_store<D, FP8>(a, ms, g, b, p, u.L, n_parts, lane);
 }
 
 // Work-list form: gridDim.y resident workgroups per kv head walk `items`
@@ -588,7 +699,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(Decode
 // retire in order, so a store issued at a unit's end would make the next
 // unit's first wait also wait for the store's acknowledgement; measured on
 // the Llama-3-70B-shaped layer that cost ~8 % of the launch.
-template <int D, bool KEEP>
+template <int D, bool KEEP, bool FP8>
 __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(PA_WL_WAVES_PER_EU)))
 void decode_worklist_kernel(DecodeArgs a, const int32_t* __restrict__ items, int32_t n_items,
                             int32_t ring) {
@@ -645,16 +756,18 @@ void decode_worklist_kernel(DecodeArgs a, const int32_t* __restrict__ items, int
 
   if (item(0) >= n_items) return;
   Unit u = unit_at(item(0));
-  f16x8 qf[D / 32], kA[D / 32], kB[D / 32];
-  f16x4 vA[D / 16], vB[D / 16];
+  typedef TileRegs<D, FP8> TR;
+  f16x8 qf[D / 32];
+  typename TR::K kA[TR::NB * TR::NK], kB[TR::NB * TR::NK];
+  typename TR::V vA[TR::NB * TR::NV], vB[TR::NB * TR::NV];
   load_q<D>(a, g, u.b, lane, qf);
-  if (u.cnt > 0) load_block<D, KEEP>(a, g, pick_block(u, no_unit(), 0), lane, kA, vA);
+  if (u.cnt > 0) load_set<D, KEEP, FP8>(a, g, u, no_unit(), 0, true, lane, kA, vA);
 
   for (int k = 0;; ++k) {
     const bool more = item(k + 1) < n_items;
     const Unit nx = more ? unit_at(item(k + 1)) : no_unit();
     WaveState<D> st;
-    run_unit<D, KEEP>(a, g, wave, lane, u, nx, qf, kA, vA, kB, vB, st);
+    run_unit<D, KEEP, FP8>(a, g, wave, lane, u, nx, qf, kA, vA, kB, vB, st);
     if (more) load_q<D>(a, g, nx.b, lane, qf);  // in flight during the epilogue
 
     const int buf = k % kMergeSlots;
@@ -671,7 +784,8 @@ void decode_worklist_kernel(DecodeArgs a, const int32_t* __restrict__ items, int
     const int rs = k % ring;  // this unit's result slot
     if (post_state<D>(ms, st, G, wave, lane, u.bad)) {
       if (u.ok) {
-        merge_unit<D>(ms, G, u.L, lane, [&](int h, int d0, f16x8 r, float m, float l) {
+        merge_unit<D, FP8>(ms, G, u.L, lane, a.v_scale,
+                           [&](int h, int d0, f16x8 r, float m, float l) {
           *reinterpret_cast<f16x8*>(ring_o + (rs * G + h) * D + d0) = r;
           if (d0 == 0) {
             ring_m[rs * G + h] = m;
@@ -697,19 +811,35 @@ void decode_worklist_kernel(DecodeArgs a, const int32_t* __restrict__ items, int
   }
 }
 
+// The kernels of one (head_dim, KEEP, FP8) choice.
+struct DecodeKernels {
+  void (*worklist)(DecodeArgs, const int32_t*, int32_t, int32_t);
+  void (*grid)(DecodeArgs);
+};
+
+template <int D, bool KEEP, bool FP8>
+static DecodeKernels kernels_of() {
+  return {&decode_worklist_kernel<D, KEEP, FP8>, &decode_partition_kernel<D, KEEP, FP8>};
+}
+
+static DecodeKernels pick_kernels(int D, bool keep, bool fp8) {
+  if (D == 128) {
+    if (fp8) return keep ? kernels_of<128, true, true>() : kernels_of<128, false, true>();
+    return keep ? kernels_of<128, true, false>() : kernels_of<128, false, false>();
+  }
+  if (fp8) return keep ? kernels_of<64, true, true>() : kernels_of<64, false, true>();
+  return keep ? kernels_of<64, true, false>() : kernels_of<64, false, false>();
+}
+
 // Resident workgroups of the work-list kernel on the current device (cached
-// per head_dim and G; the dynamic LDS depends on G).
-static int worklist_resident_wgs(int D, bool keep, int G, size_t lds) {
-  static int per_cu[2][2][17];
+// per kernel and G; the dynamic LDS depends on G).
+static int worklist_resident_wgs(int D, bool keep, bool fp8, int G, size_t lds) {
+  static int per_cu[2][2][2][17];
   static int cus = 0;
-  int& slot = per_cu[D == 128 ? 1 : 0][keep ? 1 : 0][G];
+  int& slot = per_cu[D == 128 ? 1 : 0][keep ? 1 : 0][fp8 ? 1 : 0][G];
   if (slot == 0) {
     int n = 0;
-    const void* fn =
-        D == 128 ? (keep ? reinterpret_cast<const void*>(&decode_worklist_kernel<128, true>)
-                         : reinterpret_cast<const void*>(&decode_worklist_kernel<128, false>))
-                 : (keep ? reinterpret_cast<const void*>(&decode_worklist_kernel<64, true>)
-                         : reinterpret_cast<const void*>(&decode_worklist_kernel<64, false>));
+    const void* fn = reinterpret_cast<const void*>(pick_kernels(D, keep, fp8).worklist);
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kDecodeThreads, lds) != hipSuccess || n < 1)
       n = 1;
     slot = n;
@@ -726,32 +856,26 @@ static int worklist_resident_wgs(int D, bool keep, int G, size_t lds) {
   return slot * cus;
 }
 
-}  // namespace pa
+// Both pool types: pools, geometry and (FP8) scales, then the shared checks
+// and launches.
+struct PoolArgs {
+  const void* k_pool;
+  const void* v_pool;
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  bool fp8;
+  float k_scale;
+  float v_scale;
+};
 
-using namespace pa;
-
-
-extern "C" uint64_t pa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
-                                              int32_t head_dim, int32_t max_seq_len,
-                                              int32_t partition_size) {
-  if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len < 0 || partition_size <= 0)
-    return 0;
-  const uint64_t parts = max_seq_len == 0
-                             ? 1
-                             : (static_cast<uint64_t>(max_seq_len) + partition_size - 1) /
-                                   partition_size;
-  // fp16 normalised partial outputs, then fp32 running max and sum
-  return parts > 1 ? static_cast<uint64_t>(batch) * num_q_heads * parts * (head_dim * 2 + 8) : 0;
-}
-
-extern "C" pa_status pa_paged_attention_decode(pa_half* out, const pa_half* q, pa_kv_view kv,
-                                               const int32_t* tables, int32_t max_blocks,
-                                               const int32_t* seq_lens, int32_t batch,
-                                               int32_t num_q_heads, float scale,
-                                               int32_t partition_size, int32_t max_seq_len,
-                                               const int32_t* work_items, int32_t n_items,
-                                               void* workspace, uint64_t workspace_bytes,
-                                               uint32_t flags, void* stream) {
+static pa_status decode_launch(pa_half* out, const pa_half* q, const PoolArgs& kv,
+                               const int32_t* tables, int32_t max_blocks,
+                               const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                               float scale, int32_t partition_size, int32_t max_seq_len,
+                               const int32_t* work_items, int32_t n_items, void* workspace,
+                               uint64_t workspace_bytes, uint32_t flags, void* stream) {
   if (kv.k_pool == nullptr || kv.v_pool == nullptr || kv.block_size != kBlock ||
       kv.num_blocks <= 0 || kv.num_kv_heads <= 0 || kv.num_kv_heads > 65535)
     return PA_ERR_INVALID;
@@ -764,6 +888,9 @@ extern "C" pa_status pa_paged_attention_decode(pa_half* out, const pa_half* q, p
       partition_size > kDecodeWaves * kMaxWaveBlocks * kBlock)
     return PA_ERR_INVALID;
   if (!(scale == scale)) return PA_ERR_INVALID;
+  if (kv.fp8 && !(kv.k_scale > 0.0f && kv.k_scale <= 3.0e38f && kv.v_scale > 0.0f &&
+                  kv.v_scale <= 3.0e38f))
+    return PA_ERR_INVALID;
   if ((flags & ~static_cast<uint32_t>(PA_DECODE_KEEP_KV)) != 0) return PA_ERR_INVALID;
   const bool keep = (flags & PA_DECODE_KEEP_KV) != 0;
   if (n_items < 0 || n_items > (1 << 30) || (n_items > 0 && work_items == nullptr))
@@ -786,15 +913,18 @@ extern "C" pa_status pa_paged_attention_decode(pa_half* out, const pa_half* q, p
 
   DecodeArgs a;
   a.q = reinterpret_cast<const f16*>(q);
-  a.kp = reinterpret_cast<const f16*>(kv.k_pool);
-  a.vp = reinterpret_cast<const f16*>(kv.v_pool);
+  a.kp = static_cast<const f16*>(kv.k_pool);
+  a.vp = static_cast<const f16*>(kv.v_pool);
   a.tables = tables;
   a.seq_lens = seq_lens;
   a.max_blocks = max_blocks;
   a.num_blocks = kv.num_blocks;
   a.n_kv = kv.num_kv_heads;
   a.G = G;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  // FP8: a score is scale * q . (code * k_scale); k_scale joins the exponent's factor
+  a.scale_log2 = kv.fp8 ? scale * kv.k_scale * 1.4426950408889634f
+                        : scale * 1.4426950408889634f;
+  a.v_scale = kv.fp8 ? kv.v_scale : 1.0f;
   a.part_blocks = part_blocks;
   a.p_max = p_max;
   a.out = reinterpret_cast<f16*>(out);
@@ -808,6 +938,7 @@ extern "C" pa_status pa_paged_attention_decode(pa_half* out, const pa_half* q, p
     a.ws_l = a.ws_m + slots;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const DecodeKernels kn = pick_kernels(D, keep, kv.fp8);
   if (worklist) {
     if (n_items > 0) {
       // result ring: as many unit slots as fit in ~16 KiB (at least 2)
@@ -815,22 +946,18 @@ extern "C" pa_status pa_paged_attention_decode(pa_half* out, const pa_half* q, p
       const int ring = static_cast<int>(std::max<size_t>(2, kResultRingBytes / ring_slot));
       const size_t lds = static_cast<size_t>(kMergeSlots) * kDecodeWaves * G * (D + 4) * sizeof(float) +
                          static_cast<size_t>(ring) * ring_slot;
-      int wph = worklist_resident_wgs(D, keep, G, lds) / kv.num_kv_heads;
+      int wph = worklist_resident_wgs(D, keep, kv.fp8, G, lds) / kv.num_kv_heads;
       if (wph < 1) wph = 1;
       if (wph > n_items) wph = n_items;
       if (wph > 65535) wph = 65535;
       const dim3 grid(static_cast<uint32_t>(kv.num_kv_heads), static_cast<uint32_t>(wph));
-      auto fn = D == 128 ? (keep ? decode_worklist_kernel<128, true> : decode_worklist_kernel<128, false>)
-                         : (keep ? decode_worklist_kernel<64, true> : decode_worklist_kernel<64, false>);
-      fn<<<grid, dim3(kDecodeThreads), lds, s>>>(a, work_items, n_items, ring);
+      kn.worklist<<<grid, dim3(kDecodeThreads), lds, s>>>(a, work_items, n_items, ring);
     }
   } else {
     const size_t lds = static_cast<size_t>(kDecodeWaves) * G * (D + 4) * sizeof(float);
     const dim3 grid(static_cast<uint32_t>(kv.num_kv_heads), static_cast<uint32_t>(batch),
                     static_cast<uint32_t>(p_max));
-    auto fn = D == 128 ? (keep ? decode_partition_kernel<128, true> : decode_partition_kernel<128, false>)
-                       : (keep ? decode_partition_kernel<64, true> : decode_partition_kernel<64, false>);
-    fn<<<grid, dim3(kDecodeThreads), lds, s>>>(a);
+    kn.grid<<<grid, dim3(kDecodeThreads), lds, s>>>(a);
   }
   if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   if (p_max > 1) {
@@ -841,4 +968,48 @@ extern "C" pa_status pa_paged_attention_decode(pa_half* out, const pa_half* q, p
       decode_reduce_kernel<64><<<rgrid, dim3(kWave), 0, s>>>(a);
   }
   return launch_status();
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" uint64_t pa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
+                                              int32_t head_dim, int32_t max_seq_len,
+                                              int32_t partition_size) {
+  if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len < 0 || partition_size <= 0)
+    return 0;
+  const uint64_t parts = max_seq_len == 0
+                             ? 1
+                             : (static_cast<uint64_t>(max_seq_len) + partition_size - 1) /
+                                   partition_size;
+  // fp16 normalised partial outputs, then fp32 running max and sum
+  return parts > 1 ? static_cast<uint64_t>(batch) * num_q_heads * parts * (head_dim * 2 + 8) : 0;
+}
+
+extern "C" pa_status pa_paged_attention_decode(pa_half* out, const pa_half* q, pa_kv_view kv,
+                                               const int32_t* tables, int32_t max_blocks,
+                                               const int32_t* seq_lens, int32_t batch,
+                                               int32_t num_q_heads, float scale,
+                                               int32_t partition_size, int32_t max_seq_len,
+                                               const int32_t* work_items, int32_t n_items,
+                                               void* workspace, uint64_t workspace_bytes,
+                                               uint32_t flags, void* stream) {
+  const PoolArgs pk{kv.k_pool, kv.v_pool, kv.num_blocks, kv.block_size, kv.num_kv_heads,
+                    kv.head_dim, false, 1.0f, 1.0f};
+  return decode_launch(out, q, pk, tables, max_blocks, seq_lens, batch, num_q_heads, scale,
+                       partition_size, max_seq_len, work_items, n_items, workspace,
+                       workspace_bytes, flags, stream);
+}
+
+extern "C" pa_status pa_paged_attention_decode_fp8(
+    pa_half* out, const pa_half* q, pa_kv_view_fp8 kv, const int32_t* tables, int32_t max_blocks,
+    const int32_t* seq_lens, int32_t batch, int32_t num_q_heads, float scale,
+    int32_t partition_size, int32_t max_seq_len, const int32_t* work_items, int32_t n_items,
+    void* workspace, uint64_t workspace_bytes, uint32_t flags, void* stream) {
+  const PoolArgs pk{kv.k_pool, kv.v_pool, kv.num_blocks, kv.block_size, kv.num_kv_heads,
+                    kv.head_dim, true, kv.k_scale, kv.v_scale};
+  return decode_launch(out, q, pk, tables, max_blocks, seq_lens, batch, num_q_heads, scale,
+                       partition_size, max_seq_len, work_items, n_items, workspace,
+                       workspace_bytes, flags, stream);
 }

@@ -12,6 +12,7 @@ typedef _Float16 f16;
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlock = PA_BLOCK_SIZE;  // tokens per KV block
 constexpr int kWave = 64;              // CDNA wavefront width
@@ -60,6 +61,18 @@ __host__ __device__ __forceinline__ int k_tile_off(int s, int c) {
 }
 __host__ __device__ __forceinline__ int v_tile_off(int s, int c) {
   return (c >> 5) * 512 + (s >> 2) * 128 + (c & 15) * 8 + ((c >> 4) & 1) * 4 + (s & 3);
+}
+
+// Byte offsets of (slot s, dim c) inside a tile of the FP8 pools: the same
+// operands, one byte per value, ordered so that a 16-byte-per-lane load
+// brings two K steps (K as [D/64][4][16][2][8]) or two V pairs (V as
+// [D/64][4][16][2][2][4]) of the fp16 order above.
+__host__ __device__ __forceinline__ int k8_tile_off(int s, int c) {
+  return (c >> 6) * 1024 + ((c >> 3) & 3) * 256 + s * 16 + ((c >> 5) & 1) * 8 + (c & 7);
+}
+__host__ __device__ __forceinline__ int v8_tile_off(int s, int c) {
+  return (c >> 6) * 1024 + (s >> 2) * 256 + (c & 15) * 16 + ((c >> 5) & 1) * 8 +
+         ((c >> 4) & 1) * 4 + (s & 3);
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }

@@ -91,8 +91,8 @@ class ServingLoop:
             slots = torch.from_numpy(plan["slots"]).to(self.dev, non_blocking=True)
             if len(plan["copies"]):
                 d_copies = torch.from_numpy(np.ascontiguousarray(plan["copies"])).to(self.dev)
-                L.pa_copy_blocks(d_copies, len(plan["copies"]), self.cache.kv, stream)
-            L.pa_reshape_and_cache(k, v, slots, len(req), self.cache.kv, stream)
+                self.cache.copy_blocks(d_copies, len(plan["copies"]), stream)
+            self.cache.store(k, v, slots, len(req), stream)
             offs = np.cumsum([0] + [n for _, _, n, _ in items])
             dec = [i for i, it in enumerate(items) if it[3]]
             pre = [i for i, it in enumerate(items) if not it[3]]
@@ -122,14 +122,15 @@ class ServingLoop:
         d_len = torch.from_numpy(ln).to(self.dev, non_blocking=True)
         d_work = torch.from_numpy(np.ascontiguousarray(work)).to(self.dev, non_blocking=True)
         flags = L.PA_DECODE_KEEP_KV if self.cache.shares_blocks() else 0
-        L.pa_paged_attention_decode(out, q.contiguous(), self.cache.kv, d_tab, max_blocks, d_len,
-                                    len(ids), self.n_q, self.scale, self.partition, max_len,
-                                    d_work, len(work), ws, ws_bytes, stream, flags=flags)
+        self.cache.decode(out, q.contiguous(), d_tab, max_blocks, d_len, len(ids), self.n_q,
+                          self.scale, self.partition, max_len, d_work, len(work), ws, ws_bytes,
+                          stream, flags=flags)
         if self.keep:
             for j, (r, s, _, _) in enumerate(items):
                 self.outputs[(r, s)] = (out[j], "decode")
 
     def _prefill(self, r: int, s: int, n: int, q: torch.Tensor, stream):
+        self.cache.require_fp16("pa_paged_attention_prefill")
         tab, ln, max_blocks = self.cache.host_tables([r])
         assert int(ln[0]) == s + n
         ws_bytes = L.pa_prefill_workspace_bytes(n, self.n_q, self.d, s)

@@ -1,9 +1,10 @@
 """One decode step for a fixed batch of running requests, pipelined.
 
 Each step reserves one slot per request (``pa_append_slots``, host), stores
-the step's new K/V (``pa_reshape_and_cache``), refreshes the device block
-tables (``pa_block_tables`` + one async host-to-device copy) and attends
-(``pa_paged_attention_decode``), all enqueued on one stream.  Host staging
+the step's new K/V (``pa_reshape_and_cache``, or its FP8 form for FP8
+pools), refreshes the device block tables (``pa_block_tables`` + one async
+host-to-device copy) and attends (``pa_paged_attention_decode`` / ``_fp8``),
+all enqueued on one stream.  Host staging
 buffers are pinned and used round-robin, so the host prepares step i+1 while
 the GPU still runs step i (the scheduler loop of ta-paperlens: blocks are
 reserved for every running request before the step's forward pass).
@@ -79,16 +80,15 @@ class DecodeStepper:
                 events["cache"][0].record(stream)
             if len(copies):
                 d_copies = torch.from_numpy(np.ascontiguousarray(copies)).to(self.cache.device)
-                L.pa_copy_blocks(d_copies, len(copies), self.cache.kv, stream)
-            L.pa_reshape_and_cache(k_new, v_new, self.d_slots[r], self.B, self.cache.kv, stream)
+                self.cache.copy_blocks(d_copies, len(copies), stream)
+            self.cache.store(k_new, v_new, self.d_slots[r], self.B, stream)
             if events is not None:
                 events["cache"][1].record(stream)
                 events["decode"][0].record(stream)
             flags = L.PA_DECODE_KEEP_KV if self.cache.shares_blocks() else 0
-            L.pa_paged_attention_decode(self.out, q, self.cache.kv, self.d_tab, self.max_blocks,
-                                        self.d_len, self.B, self.n_q, self.scale, self.partition,
-                                        max_len, self.d_items, n_items, self.workspace,
-                                        self.ws_bytes, stream, flags=flags)
+            self.cache.decode(self.out, q, self.d_tab, self.max_blocks, self.d_len, self.B,
+                              self.n_q, self.scale, self.partition, max_len, self.d_items,
+                              n_items, self.workspace, self.ws_bytes, stream, flags=flags)
             if events is not None:
                 events["decode"][1].record(stream)
         self.i += 1

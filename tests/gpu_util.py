@@ -12,6 +12,8 @@ from oracle import decode_reference, prefill_reference, run_setup, run_step
 # Every pool byte starts as 0x7E: each fp16 reads 0x7E7E, a NaN, so a kernel
 # that reads a slot nobody wrote (or fails to mask one) produces NaN.
 FILL = 0x7E
+# FP8 pools start as 0x7F bytes: every code is an E4M3 NaN.
+FILL8 = 0x7F
 RTOL, ATOL = 1e-2, 2e-3     # elementwise |gpu - oracle| <= ATOL + RTOL * |oracle|
 
 
@@ -20,11 +22,16 @@ def log(msg):
     sys.stdout.flush()
 
 
-def gpu_run(w, partition=512, fill=FILL, device="cuda:0", decode=True, prefill=True,
-            worklist=True):
+def gpu_run(w, partition=512, fill=None, device="cuda:0", decode=True, prefill=True,
+            worklist=True, kv_dtype="fp16", k_scale=1.0, v_scale=1.0, keep_kv=None):
+    fp8 = kv_dtype == "fp8"
+    if fill is None:
+        fill = FILL8 if fp8 else FILL
     log(f"[gpu_run] {w.name}: blocks={w.num_blocks} B={w.batch} n_q={w.n_q} n_kv={w.n_kv} "
-        f"d={w.d} partition={partition} prefill={w.prefill is not None}")
-    cache = PagedKVCache(w.num_blocks, w.n_kv, w.d, w.free_order, device, fill_byte=fill)
+        f"d={w.d} partition={partition} prefill={w.prefill is not None} kv={kv_dtype}"
+        + (f" scales=({k_scale}, {v_scale})" if fp8 else ""))
+    cache = PagedKVCache(w.num_blocks, w.n_kv, w.d, w.free_order, device, fill_byte=fill,
+                         kv_dtype=kv_dtype, k_scale=k_scale, v_scale=v_scale)
     dk = torch.from_numpy(w.setup_k).to(device)
     dv = torch.from_numpy(w.setup_v).to(device)
     run_program(cache, w.setup, dk, dv)
@@ -34,7 +41,8 @@ def gpu_run(w, partition=512, fill=FILL, device="cuda:0", decode=True, prefill=T
     slots, copies = cache.append(w.step_ids, w.step_n_new, sk, sv)
     res = {"cache": cache, "step_slots": slots, "step_copies": copies}
     if decode and w.batch:
-        plan = DecodePlan(cache, w.decode_ids, w.n_q, w.scale, partition, worklist=worklist)
+        plan = DecodePlan(cache, w.decode_ids, w.n_q, w.scale, partition, worklist=worklist,
+                          keep_kv=keep_kv)
         q = torch.from_numpy(w.q).to(device)
         res["decode"] = plan.run(q).clone()
         res["plan"], res["q"] = plan, q
@@ -48,8 +56,8 @@ def gpu_run(w, partition=512, fill=FILL, device="cuda:0", decode=True, prefill=T
     return res
 
 
-def oracle_run(w):
-    st = run_setup(w)
+def oracle_run(w, kv_dtype="fp16", k_scale=1.0, v_scale=1.0):
+    st = run_setup(w, kv_dtype=kv_dtype, k_scale=k_scale, v_scale=v_scale)
     run_step(w, st)
     return st
 
@@ -91,14 +99,39 @@ def pools_to_logical(kd, vd, d):
     return k, v
 
 
-def assert_pools_bit_exact(cache, st, fill=FILL):
-    """Valid slots of live blocks equal the oracle pool bit for bit; blocks
-    no request holds still carry the fill pattern."""
-    kraw = cache.k_pool.cpu().numpy().view(np.uint16)
-    vraw = cache.v_pool.cpu().numpy().view(np.uint16)
-    kd, vd = pools_to_logical(kraw, vraw, cache.d)
-    ko = st.pool.k.view(np.uint16)
-    vo = st.pool.v.view(np.uint16)
+def pools8_to_logical(kd, vd, d):
+    """FP8 device pools ([N][H][tile] bytes) in logical [N][H][16][d] order,
+    by the layout include/pa.h states:
+    K tile [d/64][4][16][2][8] (64-dim group, 8-dim chunk in 32, slot,
+    32-dim half, dim in chunk);
+    V tile [d/64][4][16][2][2][4] (64-dim group, slot quad, dim % 16, 32-dim
+    half, 16-dim half, slot in quad)."""
+    n, h = kd.shape[0], kd.shape[1]
+    k = kd.reshape(n, h, d // 64, 4, 16, 2, 8).transpose(0, 1, 4, 2, 5, 3, 6).reshape(n, h, 16, d)
+    v = vd.reshape(n, h, d // 64, 4, 16, 2, 2, 4).transpose(0, 1, 3, 7, 2, 5, 6, 4).reshape(
+        n, h, 16, d)
+    return k, v
+
+
+def assert_pools_bit_exact(cache, st, fill=None):
+    """Valid slots of live blocks equal the oracle pool bit for bit (FP8
+    pools: code for code); blocks no request holds still carry the fill
+    pattern."""
+    if cache.fp8:
+        fill = FILL8 if fill is None else fill
+        kraw = cache.k_pool.cpu().numpy()
+        vraw = cache.v_pool.cpu().numpy()
+        kd, vd = pools8_to_logical(kraw, vraw, cache.d)
+        ko, vo = st.pool.k, st.pool.v
+        pattern = np.uint8(fill)
+    else:
+        fill = FILL if fill is None else fill
+        kraw = cache.k_pool.cpu().numpy().view(np.uint16)
+        vraw = cache.v_pool.cpu().numpy().view(np.uint16)
+        kd, vd = pools_to_logical(kraw, vraw, cache.d)
+        ko = st.pool.k.view(np.uint16)
+        vo = st.pool.v.view(np.uint16)
+        pattern = np.uint16(fill | (fill << 8))
     nvalid = valid_slots(st)
     mask = np.arange(16)[None, :] < nvalid[:, None]                    # [N][16]
     k_dev = kd.transpose(0, 2, 1, 3)[mask]
@@ -107,7 +140,6 @@ def assert_pools_bit_exact(cache, st, fill=FILL):
     v_dev = vd.transpose(0, 2, 1, 3)[mask]
     v_ref = vo.transpose(0, 2, 1, 3)[mask]
     assert np.array_equal(v_dev, v_ref), "V pool differs from the oracle"
-    pattern = np.uint16(fill | (fill << 8))
     untouched = nvalid == 0
     assert (kraw[untouched] == pattern).all(), "a block no request holds was written (K)"
     assert (vraw[untouched] == pattern).all(), "a block no request holds was written (V)"

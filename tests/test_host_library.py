@@ -257,6 +257,46 @@ def test_tile_layout_converter_matches_the_header_formulas():
         assert np.array_equal(k[0, 0], want) and np.array_equal(v[0, 0], want)
 
 
+def test_fp8_tile_layout_converter_matches_the_header_formulas():
+    gpu_util = pytest.importorskip("gpu_util")
+    for d in (64, 128):
+        kraw = np.full((1, 1, 16 * d), -1, dtype=np.int32)
+        vraw = np.full((1, 1, 16 * d), -1, dtype=np.int32)
+        for s in range(16):
+            for c in range(d):
+                kraw[0, 0, (c // 64) * 1024 + ((c // 8) % 4) * 256 + s * 16 + ((c // 32) % 2) * 8
+                     + c % 8] = s * 1000 + c
+                vraw[0, 0, (c // 64) * 1024 + (s // 4) * 256 + (c % 16) * 16 + ((c // 32) % 2) * 8
+                     + ((c // 16) % 2) * 4 + s % 4] = s * 1000 + c
+        assert (kraw >= 0).all() and (vraw >= 0).all()
+        k, v = gpu_util.pools8_to_logical(kraw, vraw, d)
+        want = np.arange(16)[:, None] * 1000 + np.arange(d)[None, :]
+        assert np.array_equal(k[0, 0], want) and np.array_equal(v[0, 0], want)
+
+
+def test_fp8_calls_reject_bad_scales_before_any_launch():
+    # dummy addresses, never dereferenced: every call below fails or returns
+    # on the host
+    for ks, vs in ((0.0, 1.0), (1.0, -2.0), (float("nan"), 1.0), (1.0, float("inf"))):
+        kv = pa.kv_view_fp8(None, None, 4, 2, 64, ks, vs)
+        kv.k_pool = kv.v_pool = 1 << 20
+        with pytest.raises(pa.PaError):
+            pa.pa_reshape_and_cache_fp8(1 << 21, 1 << 22, 1 << 23, 3, kv)
+        with pytest.raises(pa.PaError):
+            pa.pa_copy_blocks_fp8(1 << 21, 1, kv)
+        with pytest.raises(pa.PaError):
+            pa.pa_paged_attention_decode_fp8(1 << 21, 1 << 22, kv, 1 << 23, 4, 1 << 24, 1, 4,
+                                             0.125, 512, 64, None, 0, None, 0)
+    kv = pa.kv_view_fp8(None, None, 4, 2, 64, 0.5, 2.0)
+    kv.k_pool = kv.v_pool = 1 << 20
+    pa.pa_reshape_and_cache_fp8(1 << 21, 1 << 22, 1 << 23, 0, kv)          # nothing to store
+    with pytest.raises(pa.PaError):
+        pa.pa_paged_attention_decode_fp8(1 << 21, 1 << 22, kv, 1 << 23, 4, 1 << 24, 0, 4,
+                                         0.125, 512, 64, None, 0, None, 0, flags=4)
+    pa.pa_paged_attention_decode_fp8(1 << 21, 1 << 22, kv, 1 << 23, 4, 1 << 24, 0, 4, 0.125,
+                                     512, 64, None, 0, None, 0)               # batch 0
+
+
 def test_decode_rejects_unknown_flags_before_any_launch():
     # argument checks run on the host before anything touches the GPU: the
     # dummy addresses below are never dereferenced

@@ -54,6 +54,15 @@ def test_encoder_equals_brute_force_nearest_on_random_values():
         assert decode_e4m3([ci])[0] == decode_e4m3([best[0]])[0], (xi, hex(ci))
 
 
+def test_quantize_table_equals_the_encoder_value_by_value():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal(3000).astype(np.float16) * np.float16(20)
+    for scale in (1.0, 0.0123, 7.0):
+        inv = np.float32(1.0) / np.float32(scale)
+        direct = np.array([encode_e4m3([float(np.float32(xi) * inv)])[0] for xi in x])
+        assert np.array_equal(quantize(x, scale), direct)
+
+
 def test_quantize_uses_the_fp32_reciprocal_of_the_scale():
     x = np.array([0.5, -3.0, 100.0], dtype=np.float16)
     scale = 0.3
