@@ -333,6 +333,118 @@ def bench_prefill(args):
     print(json.dumps(result), flush=True)
 
 
+def bench_mixed(args):
+    """The long-context mixed step of workload 5: 8 decode requests at 32,768
+    tokens and the 512-row causal prefill chunk at offset 49,488 of a
+    50,000-token prompt, over one pool.  Times the one-launch mixed entry point
+    against the same work as separate decode and prefill launches on one
+    stream (and each part alone)."""
+    import torch
+    from synth import make_workload
+    from pagedattention_block_paged_reshape_amd.cache import (DecodePlan, MixedPlan, PagedKVCache,
+                                                              PrefillPlan, run_program)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("[bench] generating workload 5")
+    w = make_workload("5")
+    pf = w.prefill
+    cache = PagedKVCache(w.num_blocks, w.n_kv, w.d, w.free_order, dev)
+    dk = torch.from_numpy(w.setup_k).to(dev)
+    dv = torch.from_numpy(w.setup_v).to(dev)
+    run_program(cache, w.setup, dk, dv)
+    del dk, dv
+    cache.append(w.step_ids, w.step_n_new, torch.from_numpy(w.step_k).to(dev),
+                 torch.from_numpy(w.step_v).to(dev))
+    dplan = DecodePlan(cache, w.decode_ids, w.n_q, w.scale, args.partition)
+    pplan = PrefillPlan(cache, pf.seq_id, pf.q_start, pf.chunk_len, w.n_q, w.scale)
+    mplan = MixedPlan(cache, w.decode_ids, pf.seq_id, pf.q_start, pf.chunk_len, w.n_q, w.scale,
+                      args.partition)
+    qd = torch.from_numpy(w.q).to(dev)
+    qp = torch.from_numpy(pf.q).to(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def separate():
+        pplan.run(qp, stream)
+        dplan.run(qd, stream)
+
+    def mixed():
+        mplan.run(qd, qp, stream)
+
+    def time_it(fn, n):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        t0 = time.perf_counter()
+        for e in ev:
+            e[0].record(stream)
+            fn()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return np.array([a.elapsed_time(b) * 1e3 for a, b in ev]), wall
+
+    n_warm = clock_warmup(mixed, args.warm_ms)
+    log(f"[bench] clock warm-up: {n_warm} mixed launches in ~{args.warm_ms:.0f} ms")
+    t_dec, _ = time_it(lambda: dplan.run(qd, stream), args.steps)
+    t_pf, _ = time_it(lambda: pplan.run(qp, stream), args.steps)
+    t_sep, _ = time_it(separate, args.steps)
+    t_mix, wall = time_it(mixed, args.steps)
+    flops = prefill_flops(pf.q_start, pf.chunk_len, w.n_q, w.d)
+    dec_bytes = algorithmic_decode_bytes(dplan.lens.cpu().numpy(), w.n_q, w.n_kv, w.d)
+    achieved = flops / (t_mix.mean() * 1e-6) / 1e12
+    log(f"[bench] decode alone {t_dec.mean():.1f} us, prefill alone {t_pf.mean():.1f} us, "
+        f"separate launches {t_sep.mean():.1f} us, mixed launch {t_mix.mean():.1f} us "
+        f"(p50 {np.median(t_mix):.1f}, p99 {np.percentile(t_mix, 99):.1f})")
+    result = {
+        "metric": "mixed decode + prefill attention step time (config 5)",
+        "value": round(float(t_mix.mean()), 2),
+        "unit": "us per step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"config 5 ({w.name}): {w.batch} decode requests at "
+                        f"{int(dplan.lens.max())} tokens (split-K {args.partition}) + causal "
+                        f"chunk of {pf.chunk_len} rows at offset {pf.q_start} of a "
+                        f"{pf.q_start + pf.chunk_len}-token prompt, {w.n_q}/{w.n_kv} heads, "
+                        f"head_dim {w.d}, block 16, pool {w.num_blocks} blocks scattered",
+            "clock_warmup_ms": args.warm_ms,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": MFMA_F16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "pa_paged_attention_mixed (mixed_step_kernel + mixed_reduce_kernel); "
+                      "achieved = the chunk's matrix-core flops over the whole mixed launch",
+            "algorithmic_flops_per_launch": flops,
+            "decode_algorithmic_bytes_per_launch": int(dec_bytes),
+            "launch_us_mean": round(float(t_mix.mean()), 2),
+            "launch_us_p50": round(float(np.median(t_mix)), 2),
+            "launch_us_p99": round(float(np.percentile(t_mix, 99)), 2),
+            "separate_launches_us_mean": round(float(t_sep.mean()), 2),
+            "decode_alone_us_mean": round(float(t_dec.mean()), 2),
+            "prefill_alone_us_mean": round(float(t_pf.mean()), 2),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        del cache, dplan, pplan, mplan
+        torch.cuda.empty_cache()
+        result["cpu_baseline"] = cpu_prefill_baseline(w, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
 def copy_calibration(nbytes: int, reps: int):
     """A plain device copy of known size (for scaling HBM byte counters)."""
     import torch
@@ -366,6 +478,9 @@ def main():
     ap.add_argument("--copy-calibration-mb", type=int, default=0)
     ap.add_argument("--prefill", action="store_true",
                     help="time the causal prefill chunk of workload 5 instead of decode")
+    ap.add_argument("--mixed", action="store_true",
+                    help="time workload 5's decode batch and prefill chunk as one mixed "
+                         "launch (and as separate launches) instead of the decode step")
     ap.add_argument("--serve", action="store_true",
                     help="continuous-batching serving run (scheduler + kernels) instead of "
                          "the decode step")
@@ -386,6 +501,9 @@ def main():
         return
     if args.serve:
         bench_serve(args)
+        return
+    if args.mixed:
+        bench_mixed(args)
         return
 
     from synth import make_workload

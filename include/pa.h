@@ -434,12 +434,70 @@ uint64_t pa_prefill_workspace_bytes(int32_t chunk_len, int32_t num_q_heads, int3
  * `table` (device int32, >= ceil((q_start+chunk_len)/16) entries); the
  * chunk's own K/V must already be stored (pa_reshape_and_cache).
  *   out: device [chunk_len][n_q][D] fp16; q: device [chunk_len][n_q][D] fp16.
- *   head_dim must be 128; n_q/kv_heads <= 16 and divides n_q.
+ *   head_dim 64 or 128; n_q/kv_heads <= 16 and divides 128.
  *   workspace: device, >= pa_prefill_workspace_bytes(...). */
 pa_status pa_paged_attention_prefill(pa_half* out, const pa_half* q, pa_kv_view kv,
                                      const int32_t* table, int32_t table_len, int32_t q_start,
                                      int32_t chunk_len, int32_t num_q_heads, float scale,
                                      void* workspace, uint64_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Mixed step: decode batch + prefill chunk in one launch                    */
+/* ------------------------------------------------------------------------ */
+/* A scheduler step whose batch holds both decoding requests and one prompt
+ * chunk ([lens] "scheduler skeleton": one forward pass over the step's mixed
+ * batch; [ngrok] "the scheduler": long prompts are prefilled chunk by chunk
+ * alongside decoding requests).  The two parts are the arguments of
+ * pa_paged_attention_decode (work-list form) and pa_paged_attention_prefill
+ * over the same fp16 pool. */
+typedef struct pa_decode_batch {
+  pa_half* out;              /* device [batch][n_q][D] fp16 */
+  const pa_half* q;          /* device [batch][n_q][D] fp16 */
+  const int32_t* tables;     /* device int32 [batch][max_blocks] */
+  int32_t max_blocks;
+  const int32_t* seq_lens;   /* device int32 [batch] */
+  int32_t batch;             /* 0: no decode part */
+  int32_t partition_size;    /* as for pa_paged_attention_decode */
+  int32_t max_seq_len;
+  const int32_t* work_items; /* device copy of pa_decode_work_items(seq_lens) */
+  int32_t n_items;
+} pa_decode_batch;
+
+typedef struct pa_prefill_chunk {
+  pa_half* out;              /* device [chunk_len][n_q][D] fp16 */
+  const pa_half* q;          /* device [chunk_len][n_q][D] fp16 */
+  const int32_t* table;      /* device int32, the chunk's request's block table */
+  int32_t table_len;
+  int32_t q_start;
+  int32_t chunk_len;         /* 0: no prefill part */
+} pa_prefill_chunk;
+
+/* Workspace bytes pa_paged_attention_mixed needs: the decode part's
+ * pa_decode_workspace_bytes rounded up to 256, then the chunk's
+ * pa_prefill_workspace_bytes.  0 for a NULL argument. */
+uint64_t pa_mixed_workspace_bytes(const pa_decode_batch* dec, const pa_prefill_chunk* pf,
+                                  int32_t num_q_heads, int32_t head_dim);
+
+/* Decode attention for every request of `dec` and causal attention for the
+ * chunk `pf`, with the results of pa_paged_attention_decode (bitwise the
+ * same outputs) and pa_paged_attention_prefill (bitwise the same outputs),
+ * in two launches instead of four: one kernel whose first workgroups compute
+ * the chunk's tiles and whose remaining workgroups compute the decode units
+ * (two per workgroup, work list order), then one kernel that merges the
+ * partitions of both.  Decode units run on CUs as soon as prefill tiles
+ * retire, so memory-bound decode fills the compute-bound chunk's tail.
+ *   kv: one fp16 pool; num_q_heads and scale apply to both parts.
+ *   dec, pf: host structs (read during the call only); a part with batch 0 /
+ *   chunk_len 0 is skipped.  dec->work_items must be non-NULL when batch > 0
+ *   and n_items > 0 and must have been built from the same lengths.
+ *   workspace: device, 16-byte aligned, >= pa_mixed_workspace_bytes(...).
+ *   flags: 0 or PA_DECODE_KEEP_KV (decode loads), as for decode.
+ *   Every argument check of both entry points applies (PA_ERR_INVALID before
+ *   any launch); a failed launch returns PA_ERR_HIP. */
+pa_status pa_paged_attention_mixed(const pa_decode_batch* dec, const pa_prefill_chunk* pf,
+                                   pa_kv_view kv, int32_t num_q_heads, float scale,
+                                   void* workspace, uint64_t workspace_bytes, uint32_t flags,
+                                   void* stream);
 
 #ifdef __cplusplus
 }

@@ -75,6 +75,18 @@ class pa_kv_view_fp8(C.Structure):
                 ("k_scale", C.c_float), ("v_scale", C.c_float)]
 
 
+class pa_decode_batch(C.Structure):
+    _fields_ = [("out", C.c_void_p), ("q", C.c_void_p), ("tables", C.c_void_p),
+                ("max_blocks", C.c_int32), ("seq_lens", C.c_void_p), ("batch", C.c_int32),
+                ("partition_size", C.c_int32), ("max_seq_len", C.c_int32),
+                ("work_items", C.c_void_p), ("n_items", C.c_int32)]
+
+
+class pa_prefill_chunk(C.Structure):
+    _fields_ = [("out", C.c_void_p), ("q", C.c_void_p), ("table", C.c_void_p),
+                ("table_len", C.c_int32), ("q_start", C.c_int32), ("chunk_len", C.c_int32)]
+
+
 # name -> (restype, argtypes)
 _P = C.c_void_p
 _I32 = C.c_int32
@@ -123,6 +135,11 @@ _SIGS = {
     "pa_prefill_workspace_bytes": (_U64, [_I32, _I32, _I32, _I32]),
     "pa_paged_attention_prefill": (C.c_int, [_P, _P, pa_kv_view, _P, _I32, _I32, _I32, _I32,
                                              C.c_float, _P, _U64, _P]),
+    "pa_mixed_workspace_bytes": (_U64, [C.POINTER(pa_decode_batch), C.POINTER(pa_prefill_chunk),
+                                        _I32, _I32]),
+    "pa_paged_attention_mixed": (C.c_int, [C.POINTER(pa_decode_batch),
+                                           C.POINTER(pa_prefill_chunk), pa_kv_view, _I32,
+                                           C.c_float, _P, _U64, C.c_uint32, _P]),
 }
 
 
@@ -473,3 +490,29 @@ def pa_paged_attention_prefill(out, q, kv: pa_kv_view, table, table_len: int, q_
                                           int(q_start), int(chunk_len), int(num_q_heads),
                                           float(scale), _dptr(workspace), int(workspace_bytes),
                                           _stream(stream)), "pa_paged_attention_prefill")
+
+
+def decode_batch(out, q, tables, max_blocks: int, seq_lens, batch: int, partition_size: int,
+                 max_seq_len: int, work_items, n_items: int) -> pa_decode_batch:
+    return pa_decode_batch(_dptr(out), _dptr(q), _dptr(tables), int(max_blocks), _dptr(seq_lens),
+                           int(batch), int(partition_size), int(max_seq_len), _dptr(work_items),
+                           int(n_items))
+
+
+def prefill_chunk(out, q, table, table_len: int, q_start: int, chunk_len: int) -> pa_prefill_chunk:
+    return pa_prefill_chunk(_dptr(out), _dptr(q), _dptr(table), int(table_len), int(q_start),
+                            int(chunk_len))
+
+
+def pa_mixed_workspace_bytes(dec: pa_decode_batch, pf: pa_prefill_chunk, num_q_heads: int,
+                             head_dim: int) -> int:
+    return int(LIB.pa_mixed_workspace_bytes(C.byref(dec), C.byref(pf), int(num_q_heads),
+                                            int(head_dim)))
+
+
+def pa_paged_attention_mixed(dec: pa_decode_batch, pf: pa_prefill_chunk, kv: pa_kv_view,
+                             num_q_heads: int, scale: float, workspace, workspace_bytes: int,
+                             stream=None, flags: int = 0) -> None:
+    _check(LIB.pa_paged_attention_mixed(C.byref(dec), C.byref(pf), kv, int(num_q_heads),
+                                        float(scale), _dptr(workspace), int(workspace_bytes),
+                                        int(flags), _stream(stream)), "pa_paged_attention_mixed")

@@ -214,6 +214,46 @@ class PrefillPlan:
         return self.out
 
 
+class MixedPlan:
+    """Device-resident arguments of one mixed launch: a decode batch (work-list
+    form) and one prefill chunk over the same fp16 pool, attended by
+    ``pa_paged_attention_mixed``."""
+
+    def __init__(self, cache: PagedKVCache, seq_ids, prefill_seq_id: int, q_start: int,
+                 chunk_len: int, num_q_heads: int, scale: float,
+                 partition: int = DEFAULT_PARTITION, keep_kv: Optional[bool] = None):
+        cache.require_fp16("pa_paged_attention_mixed")
+        self.cache = cache
+        self.dec = DecodePlan(cache, seq_ids, num_q_heads, scale, partition, keep_kv=keep_kv)
+        self.pf = PrefillPlan(cache, prefill_seq_id, q_start, chunk_len, num_q_heads, scale)
+        self.n_q, self.scale = int(num_q_heads), float(scale)
+        self.q_dec: Optional[torch.Tensor] = None
+        self.q_pf: Optional[torch.Tensor] = None
+        self._bind()
+
+    def _bind(self):
+        d, p = self.dec, self.pf
+        self.c_dec = L.decode_batch(d.out, self.q_dec, d.tables, d.max_blocks, d.lens, d.batch,
+                                    d.partition, d.max_len, d.items, d.n_items)
+        self.c_pf = L.prefill_chunk(p.out, self.q_pf, p.table, p.table_len, p.q_start,
+                                    p.chunk_len)
+        self.ws_bytes = L.pa_mixed_workspace_bytes(self.c_dec, self.c_pf, self.n_q, self.cache.d)
+        if not hasattr(self, "workspace") or self.workspace.numel() < max(self.ws_bytes, 16):
+            self.workspace = torch.zeros(max(self.ws_bytes, 16), dtype=torch.uint8,
+                                         device=self.cache.device)
+
+    def run(self, q_decode: torch.Tensor, q_prefill: torch.Tensor, stream=None):
+        """Returns (decode output [B][n_q][D], prefill output [C][n_q][D])."""
+        if q_decode is not self.q_dec or q_prefill is not self.q_pf:
+            self.q_dec, self.q_pf = q_decode, q_prefill
+            self._bind()
+        L.pa_paged_attention_mixed(self.c_dec, self.c_pf, self.cache.kv, self.n_q, self.scale,
+                                   self.workspace, self.ws_bytes,
+                                   stream or torch.cuda.current_stream(self.cache.device),
+                                   flags=self.dec.flags)
+        return self.dec.out, self.pf.out
+
+
 def run_program(cache: PagedKVCache, setup, k_rows: torch.Tensor, v_rows: torch.Tensor):
     """Apply a list of ("add", id) / ("fork", parent, child) /
     ("append", ids, n_new) operations, taking appended rows in order."""

@@ -49,6 +49,7 @@
 #include <algorithm>
 
 #include "pa_device.h"
+#include "prefill_tile.h"
 
 namespace pa {
 
@@ -618,10 +619,8 @@ __device__ __forceinline__ void merge_partials(const DecodeArgs& a, int64_t bg, 
 // length, then all partials in one round trip.  Requests that fit in one
 // partition were written by the first kernel and are skipped.
 template <int D>
-__global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeArgs a) {
+__device__ __forceinline__ void decode_reduce_unit(const DecodeArgs& a, int g, int b) {
   constexpr int LPH = D / 16;  // lanes per query head
-  const int g = blockIdx.x;
-  const int b = blockIdx.y;
   const int G = a.G;
   const int part_tokens = a.part_blocks * kBlock;
   int L = scalar_load(a.seq_lens, b);
@@ -639,6 +638,11 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeArgs a) {
     *reinterpret_cast<f16x8*>(dst) = r[0];
     *reinterpret_cast<f16x8*>(dst + 8) = r[1];
   }
+}
+
+template <int D>
+__global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeArgs a) {
+  decode_reduce_unit<D>(a, blockIdx.x, blockIdx.y);
 }
 
 // Grid form: one workgroup per (kv head, request, partition).
@@ -870,12 +874,14 @@ struct PoolArgs {
   float v_scale;
 };
 
-static pa_status decode_launch(pa_half* out, const pa_half* q, const PoolArgs& kv,
-                               const int32_t* tables, int32_t max_blocks,
-                               const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
-                               float scale, int32_t partition_size, int32_t max_seq_len,
-                               const int32_t* work_items, int32_t n_items, void* workspace,
-                               uint64_t workspace_bytes, uint32_t flags, void* stream) {
+// Host checks of a decode batch's arguments, then its kernel arguments.  PA_OK
+// with batch == 0 means there is nothing to launch.
+static pa_status decode_prepare(pa_half* out, const pa_half* q, const PoolArgs& kv,
+                                const int32_t* tables, int32_t max_blocks,
+                                const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                                float scale, int32_t partition_size, int32_t max_seq_len,
+                                const int32_t* work_items, int32_t n_items, void* workspace,
+                                uint64_t workspace_bytes, uint32_t flags, DecodeArgs& a) {
   if (kv.k_pool == nullptr || kv.v_pool == nullptr || kv.block_size != kBlock ||
       kv.num_blocks <= 0 || kv.num_kv_heads <= 0 || kv.num_kv_heads > 65535)
     return PA_ERR_INVALID;
@@ -892,7 +898,6 @@ static pa_status decode_launch(pa_half* out, const pa_half* q, const PoolArgs& k
                   kv.v_scale <= 3.0e38f))
     return PA_ERR_INVALID;
   if ((flags & ~static_cast<uint32_t>(PA_DECODE_KEEP_KV)) != 0) return PA_ERR_INVALID;
-  const bool keep = (flags & PA_DECODE_KEEP_KV) != 0;
   if (n_items < 0 || n_items > (1 << 30) || (n_items > 0 && work_items == nullptr))
     return PA_ERR_INVALID;
   if (batch == 0) return PA_OK;
@@ -905,13 +910,11 @@ static pa_status decode_launch(pa_half* out, const pa_half* q, const PoolArgs& k
   const int p_max = max_seq_len == 0 ? 1 : (max_seq_len + partition_size - 1) / partition_size;
   if (p_max > 65535) return PA_ERR_INVALID;
   const int D = kv.head_dim;
-  const bool worklist = work_items != nullptr;
   const uint64_t need =
       pa_decode_workspace_bytes(batch, num_q_heads, D, max_seq_len, partition_size);
   if (p_max > 1 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
     return PA_ERR_INVALID;
 
-  DecodeArgs a;
   a.q = reinterpret_cast<const f16*>(q);
   a.kp = static_cast<const f16*>(kv.k_pool);
   a.vp = static_cast<const f16*>(kv.v_pool);
@@ -937,6 +940,25 @@ static pa_status decode_launch(pa_half* out, const pa_half* q, const PoolArgs& k
     a.ws_m = reinterpret_cast<float*>(a.ws_o + slots * D);
     a.ws_l = a.ws_m + slots;
   }
+  return PA_OK;
+}
+
+static pa_status decode_launch(pa_half* out, const pa_half* q, const PoolArgs& kv,
+                               const int32_t* tables, int32_t max_blocks,
+                               const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                               float scale, int32_t partition_size, int32_t max_seq_len,
+                               const int32_t* work_items, int32_t n_items, void* workspace,
+                               uint64_t workspace_bytes, uint32_t flags, void* stream) {
+  DecodeArgs a;
+  const pa_status st = decode_prepare(out, q, kv, tables, max_blocks, seq_lens, batch,
+                                      num_q_heads, scale, partition_size, max_seq_len,
+                                      work_items, n_items, workspace, workspace_bytes, flags, a);
+  if (st != PA_OK || batch == 0) return st;
+  const bool keep = (flags & PA_DECODE_KEEP_KV) != 0;
+  const bool worklist = work_items != nullptr;
+  const int D = kv.head_dim;
+  const int G = a.G;
+  const int p_max = a.p_max;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const DecodeKernels kn = pick_kernels(D, keep, kv.fp8);
   if (worklist) {
@@ -966,6 +988,172 @@ static pa_status decode_launch(pa_half* out, const pa_half* q, const PoolArgs& k
       decode_reduce_kernel<128><<<rgrid, dim3(kWave), 0, s>>>(a);
     else
       decode_reduce_kernel<64><<<rgrid, dim3(kWave), 0, s>>>(a);
+  }
+  return launch_status();
+}
+
+// ---------------------------------------------------------------------------
+// Mixed step: the decode units of a batch and the tiles of one prefill chunk
+// in one launch over one pool (a scheduler step runs both kinds of work in
+// one forward pass: ta-paperlens "scheduler skeleton"; techfeed.io ngrok
+// summary, "the scheduler").  Workgroups of 4 wavefronts; the first pf_wgs
+// take prefill tiles (kv head fastest, then query tile, then key split, as
+// the prefill launch's grid), the rest decode units, two per workgroup, one
+// per wavefront pair, each as in the grid form.  The prefill tiles, being the
+// long work, start first; decode units fill the CUs as tiles retire, so the
+// chunk's ragged end and the launch gap between the two kinds of work
+// overlap with memory-bound decode.  Decode unit t of kv head g is entry t
+// of the work list; the workgroup that holds entries 2j and 2j+1 of kv head g
+// is number pf_wgs + j*n_kv + g, so with 8 kv heads and pf_wgs a multiple of 8
+// each head's decode units land on one XCD, as in the decode launch.
+
+// LDS of a mixed workgroup: one prefill tile's, or two decode units' merge
+// states ([pair][wave][16] max and sum, [pair][wave][G <= 16][D + 4] O^T rows).
+template <int D>
+struct MixedDecodeLds {
+  __attribute__((aligned(16))) float o[2][kDecodeWaves * 16 * (D + 4)];
+  float m[2][kDecodeWaves * 16];
+  float l[2][kDecodeWaves * 16];
+  int arrive[2];
+  int bad[2];
+};
+
+template <int D>
+union MixedLds {
+  PrefillLds<D> pf;
+  MixedDecodeLds<D> dec;
+};
+
+template <int D, bool KEEP>
+__global__ __launch_bounds__(kPfThreads) void mixed_step_kernel(PrefillArgs pa, int32_t pf_wgs,
+                                                                 int32_t pf_qtiles, DecodeArgs da,
+                                                                 const int32_t* __restrict__ items,
+                                                                 int32_t n_items) {
+  __shared__ MixedLds<D> lds;
+  const int wg = blockIdx.x;
+  if (wg < pf_wgs) {
+    const int rest = wg / pa.n_kv;
+    prefill_tile<D>(pa, wg % pa.n_kv, rest % pf_qtiles, rest / pf_qtiles, lds.pf);
+    return;
+  }
+  if (threadIdx.x < 2) {
+    lds.dec.arrive[threadIdx.x] = 0;
+    lds.dec.bad[threadIdx.x] = 0;
+  }
+  __syncthreads();
+  const int j = wg - pf_wgs;
+  const int pair = uniform(threadIdx.x >> 7);
+  const int wave = uniform((threadIdx.x >> 6) & 1);
+  const int lane = threadIdx.x & 63;
+  const int g = j % da.n_kv;
+  const int t = 2 * (j / da.n_kv) + pair;
+  if (t >= n_items) return;
+  const uint32_t packed = static_cast<uint32_t>(scalar_load(items, t));
+  const Unit u = make_unit(da, static_cast<int>(packed >> 16), static_cast<int>(packed & 0xFFFFu),
+                           wave, lane);
+  const Unit nx = no_unit();
+  typedef TileRegs<D, false> TR;
+  f16x8 qf[D / 32];
+  typename TR::K kA[TR::NB * TR::NK], kB[TR::NB * TR::NK];
+  typename TR::V vA[TR::NB * TR::NV], vB[TR::NB * TR::NV];
+  if (u.cnt > 0) {
+    load_q<D>(da, g, u.b, lane, qf);
+    load_set<D, KEEP, false>(da, g, u, nx, 0, true, lane, kA, vA);
+  }
+  WaveState<D> st;
+  run_unit<D, KEEP, false>(da, g, wave, lane, u, nx, qf, kA, vA, kB, vB, st);
+  const MergeSlot<D> ms{lds.dec.m[pair], lds.dec.l[pair], lds.dec.o[pair], &lds.dec.arrive[pair],
+                        &lds.dec.bad[pair]};
+  if (post_state<D>(ms, st, da.G, wave, lane, u.bad) && u.ok)
+    merge_store<D, false>(da, ms, g, u.b, u.p, u.L, u.n_parts, lane);
+}
+
+// Second launch of the mixed step: one wavefront per prefill (row, head)
+// whose key range was split (the first pf_rows blocks), then one per decode
+// (kv head, request) with several partitions.
+template <int D>
+__global__ __launch_bounds__(kWave) void mixed_reduce_kernel(PrefillArgs pa, int32_t pf_rows,
+                                                             DecodeArgs da) {
+  const int k = blockIdx.x;
+  if (k < pf_rows) {
+    const int n_q = pa.n_kv * pa.G;
+    prefill_reduce_row<D>(pa.chunk_len, n_q, pa.splits, pa.ws_o, pa.ws_m, pa.ws_l, pa.out,
+                          k % n_q, k / n_q);
+    return;
+  }
+  const int r = k - pf_rows;
+  decode_reduce_unit<D>(da, r % da.n_kv, r / da.n_kv);
+}
+
+constexpr uint64_t kMixedWsAlign = 256;
+
+static uint64_t mixed_decode_ws(const pa_decode_batch& d, int32_t num_q_heads, int32_t head_dim) {
+  const uint64_t b = pa_decode_workspace_bytes(d.batch, num_q_heads, head_dim, d.max_seq_len,
+                                               d.partition_size);
+  return (b + kMixedWsAlign - 1) / kMixedWsAlign * kMixedWsAlign;
+}
+
+static pa_status mixed_launch(const pa_decode_batch* dec, const pa_prefill_chunk* pf,
+                              const pa_kv_view& kv, int32_t num_q_heads, float scale,
+                              void* workspace, uint64_t workspace_bytes, uint32_t flags,
+                              void* stream) {
+  if (dec == nullptr || pf == nullptr) return PA_ERR_INVALID;
+  if ((flags & ~static_cast<uint32_t>(PA_DECODE_KEEP_KV)) != 0) return PA_ERR_INVALID;
+  if (dec->batch > 0 && dec->n_items > 0 && dec->work_items == nullptr) return PA_ERR_INVALID;
+  const PoolArgs pool{kv.k_pool, kv.v_pool, kv.num_blocks, kv.block_size, kv.num_kv_heads,
+                      kv.head_dim, false, 1.0f, 1.0f};
+  const uint64_t dec_ws = mixed_decode_ws(*dec, num_q_heads, kv.head_dim);
+  if (workspace_bytes < dec_ws) return PA_ERR_INVALID;
+  DecodeArgs da{};
+  pa_status st = decode_prepare(dec->out, dec->q, pool, dec->tables, dec->max_blocks,
+                                dec->seq_lens, dec->batch, num_q_heads, scale,
+                                dec->partition_size, dec->max_seq_len, dec->work_items,
+                                dec->n_items, workspace, workspace_bytes, flags, da);
+  if (st != PA_OK) return st;
+  PrefillArgs pa{};
+  dim3 pgrid(0, 0, 0);
+  void* pf_ws = workspace == nullptr ? nullptr : static_cast<char*>(workspace) + dec_ws;
+  st = prefill_prepare(pf->out, pf->q, kv, pf->table, pf->table_len, pf->q_start, pf->chunk_len,
+                       num_q_heads, scale, pf_ws, workspace_bytes - dec_ws, pa, pgrid);
+  if (st != PA_OK) return st;
+  const int64_t pf_wgs =
+      pf->chunk_len > 0 ? static_cast<int64_t>(pgrid.x) * pgrid.y * pgrid.z : 0;
+  const int64_t dec_wgs =
+      dec->batch > 0 ? static_cast<int64_t>(kv.num_kv_heads) * ((dec->n_items + 1) / 2) : 0;
+  if (pf_wgs + dec_wgs > 0x7FFFFFFF) return PA_ERR_INVALID;
+  if (pf_wgs + dec_wgs == 0) return PA_OK;
+  const bool keep = (flags & PA_DECODE_KEEP_KV) != 0;
+  const int D = kv.head_dim;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(static_cast<uint32_t>(pf_wgs + dec_wgs));
+  const int32_t qtiles = static_cast<int32_t>(pgrid.y);
+  const int32_t n_items = dec->batch > 0 ? dec->n_items : 0;
+  if (D == 128) {
+    if (keep)
+      mixed_step_kernel<128, true><<<grid, dim3(kPfThreads), 0, s>>>(
+          pa, static_cast<int32_t>(pf_wgs), qtiles, da, dec->work_items, n_items);
+    else
+      mixed_step_kernel<128, false><<<grid, dim3(kPfThreads), 0, s>>>(
+          pa, static_cast<int32_t>(pf_wgs), qtiles, da, dec->work_items, n_items);
+  } else {
+    if (keep)
+      mixed_step_kernel<64, true><<<grid, dim3(kPfThreads), 0, s>>>(
+          pa, static_cast<int32_t>(pf_wgs), qtiles, da, dec->work_items, n_items);
+    else
+      mixed_step_kernel<64, false><<<grid, dim3(kPfThreads), 0, s>>>(
+          pa, static_cast<int32_t>(pf_wgs), qtiles, da, dec->work_items, n_items);
+  }
+  if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+  const int64_t pf_rows =
+      pf->chunk_len > 0 && pa.splits > 1 ? static_cast<int64_t>(pf->chunk_len) * num_q_heads : 0;
+  const int64_t dec_rows =
+      dec->batch > 0 && da.p_max > 1 ? static_cast<int64_t>(kv.num_kv_heads) * dec->batch : 0;
+  if (pf_rows + dec_rows > 0) {
+    const dim3 rgrid(static_cast<uint32_t>(pf_rows + dec_rows));
+    if (D == 128)
+      mixed_reduce_kernel<128><<<rgrid, dim3(kWave), 0, s>>>(pa, static_cast<int32_t>(pf_rows), da);
+    else
+      mixed_reduce_kernel<64><<<rgrid, dim3(kWave), 0, s>>>(pa, static_cast<int32_t>(pf_rows), da);
   }
   return launch_status();
 }
@@ -1012,4 +1200,20 @@ extern "C" pa_status pa_paged_attention_decode_fp8(
   return decode_launch(out, q, pk, tables, max_blocks, seq_lens, batch, num_q_heads, scale,
                        partition_size, max_seq_len, work_items, n_items, workspace,
                        workspace_bytes, flags, stream);
+}
+
+extern "C" uint64_t pa_mixed_workspace_bytes(const pa_decode_batch* dec,
+                                             const pa_prefill_chunk* pf, int32_t num_q_heads,
+                                             int32_t head_dim) {
+  if (dec == nullptr || pf == nullptr) return 0;
+  return mixed_decode_ws(*dec, num_q_heads, head_dim) +
+         prefill_ws_bytes(pf->chunk_len, num_q_heads, head_dim, pf->q_start);
+}
+
+extern "C" pa_status pa_paged_attention_mixed(const pa_decode_batch* dec,
+                                              const pa_prefill_chunk* pf, pa_kv_view kv,
+                                              int32_t num_q_heads, float scale, void* workspace,
+                                              uint64_t workspace_bytes, uint32_t flags,
+                                              void* stream) {
+  return mixed_launch(dec, pf, kv, num_q_heads, scale, workspace, workspace_bytes, flags, stream);
 }

@@ -30,289 +30,14 @@
 //  * The key range is split over gridDim.z workgroups so that the grid has
 //    several hundred workgroups; partial (o, m, l) are merged by log-sum-exp
 //    in a second kernel, as in decode.
-#include <math.h>
-
-#include "pa_device.h"
+#include "prefill_tile.h"
 
 namespace pa {
 
-constexpr int kPfThreads = 256;
-constexpr int kPfMRows = 128;   // M-rows per workgroup
-constexpr int kPfKeys = 64;     // keys per step
-constexpr int kPfMaxSplits = 32;
-constexpr int kPfTargetWgs = 512;
-
-// Splits of the key range: enough workgroups to cover the 256 CUs twice.
-__host__ __device__ inline int prefill_splits(int chunk_len, int n_q, int q_start) {
-  const long long base = (static_cast<long long>(chunk_len) * n_q + kPfMRows - 1) / kPfMRows;
-  long long s = (kPfTargetWgs + base - 1) / (base > 0 ? base : 1);
-  const long long steps = (static_cast<long long>(q_start) + chunk_len + kPfKeys - 1) / kPfKeys;
-  if (s > steps) s = steps;
-  if (s > kPfMaxSplits) s = kPfMaxSplits;
-  if (s < 1) s = 1;
-  return static_cast<int>(s);
-}
-
 template <int D>
-__global__ __launch_bounds__(256) void prefill_chunk_kernel(
-    const f16* __restrict__ q, const f16* __restrict__ kp, const f16* __restrict__ vp,
-    const int32_t* __restrict__ table, int32_t table_len, int32_t num_blocks, int32_t n_kv,
-    int32_t G, int32_t q_start, int32_t chunk_len, float scale_log2, int32_t splits,
-    f16* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_m,
-    float* __restrict__ ws_l) {
-  constexpr int KS = D / 32;       // K-steps over head_dim
-  constexpr int DT = D / 16;       // dim tiles of O^T
-  constexpr int KROW = D + 8;      // padded K row (halves)
-  constexpr int VROW = kPfKeys + 8;  // padded V^T row (halves)
-  constexpr int KCH = kPfKeys * D / 8 / kPfThreads;  // 16-B chunks per thread per tile set
-  __shared__ __attribute__((aligned(16))) f16 sk[kPfKeys * KROW];
-  __shared__ __attribute__((aligned(16))) f16 sv[D * VROW];
-  __shared__ int sbad;
-
-  const int g = blockIdx.x;
-  const int qt = blockIdx.y;
-  const int z = blockIdx.z;
-  const int n_q = n_kv * G;
-  const int QR = kPfMRows / G;  // query rows per tile
-  const int r0 = qt * QR;
-  const int seq_end = q_start + chunk_len;
-
-  const int wave = uniform(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int col = lane & 15;
-  const int lg = lane >> 4;
-
-  // keys this tile needs: 0 .. q_start + (last row) inclusive
-  const int last_row = min(r0 + QR, chunk_len) - 1;
-  const int key_end = q_start + last_row + 1;
-  const int n_steps = (key_end + kPfKeys - 1) / kPfKeys;
-  const int st0 = static_cast<int>((static_cast<long long>(n_steps) * z) / splits);
-  const int st1 = static_cast<int>((static_cast<long long>(n_steps) * (z + 1)) / splits);
-
-  // M-rows of this lane for the two n-tiles, and their query rows / heads
-  int mrow_r[2], mrow_h[2];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int m = wave * 32 + nt * 16 + col;
-    mrow_h[nt] = m / QR;
-    mrow_r[nt] = r0 + (m % QR);
-  }
-
-  // Q^T fragments (B operand): M-row's query, dims kk*32 + lg*8 .. +8
-  f16x8 qf[2][KS];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int r = min(mrow_r[nt], chunk_len - 1);
-    const f16* qrow = q + (static_cast<int64_t>(r) * n_q + g * G + mrow_h[nt]) * D + lg * 8;
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) qf[nt][kk] = *reinterpret_cast<const f16x8*>(qrow + kk * 32);
-  }
-
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.f, 0.f};
-  f32x4 o[DT][2];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) o[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  if (threadIdx.x == 0) sbad = 0;
-  bool bad = false;
-
-  // Register staging of one step's 4 K tiles and 4 V tiles.
-  f16x8 rk[KCH], rv[KCH];
-  // Physical ids of a step's 4 blocks, read (clamped into the table; entries
-  // past the sequence are never used) a step before their fetch.
-  constexpr int kStepBlocks = kPfKeys / kBlock;
-  auto read_ids = [&](int step, int (&ids)[kStepBlocks]) {
-#pragma unroll
-    for (int i = 0; i < kStepBlocks; ++i)
-      ids[i] = scalar_load(table, min(step * kStepBlocks + i, table_len - 1));
-  };
-  // Chunk u of every thread lies in one block of the step, the same for the
-  // whole wavefront (a block is kBlock * D / 8 >= 64 chunks), so the bounds
-  // checks and the tail test are scalar.
-  auto fetch = [&](int step, const int (&ids)[kStepBlocks]) {
-    const int key0 = step * kPfKeys;
-#pragma unroll
-    for (int u = 0; u < KCH; ++u) {
-      const int ci = threadIdx.x + kPfThreads * u;         // 16-byte chunk of the 4-tile set
-      const int bi = uniform(ci / (kBlock * D / 8));       // which of the 4 blocks
-      const int within = ci % (kBlock * D / 8);
-      const int lb = key0 / kBlock + bi;                   // logical block
-      const f16x8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (lb * kBlock >= seq_end || lb >= table_len) {
-        rk[u] = zero;
-        rv[u] = zero;
-        continue;
-      }
-      int pb = ids[bi];
-      if (static_cast<uint32_t>(pb) >= static_cast<uint32_t>(num_blocks)) {
-        bad = true;
-        pb = 0;
-      }
-      const int64_t tile = (static_cast<int64_t>(pb) * n_kv + g) * (kBlock * D);
-      rk[u] = *reinterpret_cast<const f16x8*>(kp + tile + within * 8);
-      f16x8 vv = *reinterpret_cast<const f16x8*>(vp + tile + within * 8);
-      if (lb * kBlock + kBlock > seq_end) {
-        // the sequence's last block: V chunk `within` holds two dims' values
-        // for slots 4q .. 4q+3 (tile order [D/32][4][16][2][4]); zero the
-        // slots past the end
-        const int q4 = ((within >> 4) & 3) * 4;
-        const int valid = seq_end - (lb * kBlock + q4);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if ((e & 3) >= valid) vv[e] = static_cast<f16>(0.0f);
-      }
-      rv[u] = vv;
-    }
-  };
-  auto stash = [&]() {
-#pragma unroll
-    for (int u = 0; u < KCH; ++u) {
-      const int ci = threadIdx.x + kPfThreads * u;
-      const int bi = ci / (kBlock * D / 8);
-      const int within = ci % (kBlock * D / 8);
-      // K chunk `within` = dims (within/16)*8 .. +8 of slot within%16
-      const int key = bi * kBlock + (within & 15);
-      const int d8 = within >> 4;
-      *reinterpret_cast<f16x8*>(sk + key * KROW + d8 * 8) = rk[u];
-      // V chunk `within` = dims c2*32 + dd and c2*32 + 16 + dd, slots 4q .. +4.
-      // V^T rows keep each 32-key half in the order the score accumulators
-      // hold P^T: key 16h + 4q + j of the half sits at 8q + 4h + j, so one
-      // 16-byte read gives a lane its 8 keys of the PV operand.
-      const int dim = (within >> 6) * 32 + (within & 15);
-      const int q4 = (within >> 4) & 3;
-      const int kpos = (bi >> 1) * 32 + q4 * 8 + (bi & 1) * 4;
-      const f16x8 vv = rv[u];
-      *reinterpret_cast<f16x4*>(sv + dim * VROW + kpos) = f16x4{vv[0], vv[1], vv[2], vv[3]};
-      *reinterpret_cast<f16x4*>(sv + (dim + 16) * VROW + kpos) = f16x4{vv[4], vv[5], vv[6], vv[7]};
-    }
-  };
-
-  int ids[kStepBlocks];
-  if (st0 < st1) {
-    read_ids(st0, ids);
-    fetch(st0, ids);
-  }
-  if (st0 + 1 < st1) read_ids(st0 + 1, ids);
-  for (int step = st0; step < st1; ++step) {
-    __syncthreads();  // previous step's LDS reads are done
-    stash();
-    __syncthreads();
-    if (step + 1 < st1) fetch(step + 1, ids);
-
-    const int key0 = step * kPfKeys;
-    // scores S^T[key][M-row]: 4 key tiles x 2 M-row tiles
-    f32x4 s[4][2];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      f16x8 ka[KS];
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk)
-        ka[kk] = *reinterpret_cast<const f16x8*>(sk + (mt * 16 + col) * KROW + kk * 32 + lg * 8);
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) acc = mfma16x16x32(ka[kk], qf[nt][kk], acc);
-        s[mt][nt] = acc;
-      }
-    }
-
-    if (step + 2 < st1) read_ids(step + 2, ids);
-
-    // causal mask, on the raw scores, only where the step crosses the
-    // diagonal of this tile (a uniform branch: most steps skip it)
-    if (key0 + kPfKeys - 1 > q_start + r0) {
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int limit = q_start + min(mrow_r[nt], chunk_len - 1);  // last key allowed
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (key0 + mt * 16 + 4 * lg + j > limit) s[mt][nt][j] = -INFINITY;
-      }
-    }
-    f16x8 pb8[2][2];  // [k-step of PV][n-tile]
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      float mloc = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mloc = fmaxf(mloc, s[mt][nt][j]);
-      mloc = wave_max_xor16_32(mloc);
-      // running max in base-2 units (scale_log2 > 0, so max(s) * c = max(s * c))
-      const float m_new = fmaxf(m_run[nt], mloc * scale_log2);
-      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-      // hardware 2^x: results below 2^-126 flush to 0, which softmax ignores
-      const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_use);
-      float psum = 0.0f;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[mt][nt][j], scale_log2, -m_use));
-          psum += p;
-          pb8[mt >> 1][nt][(mt & 1) * 4 + j] = static_cast<f16>(p);
-        }
-      l_run[nt] = l_run[nt] * alpha + psum;
-      m_run[nt] = m_new;
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[dt][nt] *= alpha;
-      }
-    }
-
-    // O^T[dim][M-row] += V^T[dim][key] . P^T[key][M-row]
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const f16x8 va =
-            *reinterpret_cast<const f16x8*>(sv + (dt * 16 + col) * VROW + ks * 32 + 8 * lg);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) o[dt][nt] = mfma16x16x32(va, pb8[ks][nt], o[dt][nt]);
-      }
-    }
-  }
-
-  if (bad) sbad = 1;
-  __syncthreads();
-  const bool any_bad = sbad != 0;
-
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const float l = wave_sum_xor16_32(l_run[nt]);
-    const int r = mrow_r[nt];
-    if (r >= chunk_len) continue;
-    const int head = g * G + mrow_h[nt];
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    const int64_t qh = static_cast<int64_t>(r) * n_q + head;
-    if (splits == 1) {
-      f16* orow = out + qh * D;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        f16x4 h4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          h4[j] = static_cast<f16>(any_bad ? __builtin_nanf("") : o[dt][nt][j] * inv);
-        *reinterpret_cast<f16x4*>(orow + dt * 16 + 4 * lg) = h4;
-      }
-    } else {
-      const int64_t slot = static_cast<int64_t>(z) * chunk_len * n_q + qh;
-      float* orow = ws_o + slot * D;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(orow + dt * 16 + 4 * lg) =
-          o[dt][nt] * inv;
-      if (lg == 0) {
-        ws_m[slot] = any_bad ? __builtin_nanf("") : m_run[nt];
-        ws_l[slot] = l;
-      }
-    }
-  }
+__global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a) {
+  __shared__ PrefillLds<D> lds;
+  prefill_tile<D>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds);
 }
 
 // Merge the key splits of each (row, head) by log-sum-exp.
@@ -323,27 +48,7 @@ __global__ __launch_bounds__(64) void prefill_reduce_kernel(int32_t chunk_len, i
                                                             const float* __restrict__ ws_m,
                                                             const float* __restrict__ ws_l,
                                                             f16* __restrict__ out) {
-  constexpr int PER = D / 64;
-  const int64_t qh = static_cast<int64_t>(blockIdx.y) * n_q + blockIdx.x;
-  const int64_t stride = static_cast<int64_t>(chunk_len) * n_q;
-  float M = -INFINITY;
-  for (int z = 0; z < splits; ++z) M = fmaxf(M, ws_m[z * stride + qh]);
-  float wsum = 0.0f, acc[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
-  for (int z = 0; z < splits; ++z) {
-    const float l = ws_l[z * stride + qh];
-    if (!(l > 0.0f) && !(ws_m[z * stride + qh] != ws_m[z * stride + qh])) continue;
-    const float w = l * exp2f(ws_m[z * stride + qh] - M);
-    wsum += w;
-    const float* op = ws_o + (z * stride + qh) * D;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] += w * op[threadIdx.x + 64 * e];
-  }
-  const float inv = 1.0f / wsum;
-  f16* orow = out + qh * D;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) orow[threadIdx.x + 64 * e] = static_cast<f16>(acc[e] * inv);
+  prefill_reduce_row<D>(chunk_len, n_q, splits, ws_o, ws_m, ws_l, out, blockIdx.x, blockIdx.y);
 }
 
 }  // namespace pa
@@ -352,10 +57,7 @@ using namespace pa;
 
 extern "C" uint64_t pa_prefill_workspace_bytes(int32_t chunk_len, int32_t num_q_heads,
                                                int32_t head_dim, int32_t q_start) {
-  if (chunk_len <= 0 || num_q_heads <= 0 || head_dim <= 0 || q_start < 0) return 0;
-  const int s = prefill_splits(chunk_len, num_q_heads, q_start);
-  if (s <= 1) return 0;
-  return static_cast<uint64_t>(s) * chunk_len * num_q_heads * (head_dim + 2) * sizeof(float);
+  return prefill_ws_bytes(chunk_len, num_q_heads, head_dim, q_start);
 }
 
 extern "C" pa_status pa_paged_attention_prefill(pa_half* out, const pa_half* q, pa_kv_view kv,
@@ -364,53 +66,22 @@ extern "C" pa_status pa_paged_attention_prefill(pa_half* out, const pa_half* q, 
                                                 int32_t num_q_heads, float scale,
                                                 void* workspace, uint64_t workspace_bytes,
                                                 void* stream) {
-  if (kv.k_pool == nullptr || kv.v_pool == nullptr || kv.block_size != kBlock ||
-      kv.num_blocks <= 0 || kv.num_kv_heads <= 0 || kv.num_kv_heads > 65535)
-    return PA_ERR_INVALID;
-  if (kv.head_dim != 128 && kv.head_dim != 64) return PA_ERR_INVALID;
-  if (q_start < 0 || chunk_len < 0 || table_len < 0) return PA_ERR_INVALID;
-  if (num_q_heads <= 0 || num_q_heads % kv.num_kv_heads != 0) return PA_ERR_INVALID;
-  const int G = num_q_heads / kv.num_kv_heads;
-  if (G > 16 || kPfMRows % G != 0) return PA_ERR_INVALID;
-  if (!(scale == scale)) return PA_ERR_INVALID;
-  if (chunk_len == 0) return PA_OK;
-  if (static_cast<int64_t>(q_start) + chunk_len > static_cast<int64_t>(table_len) * kBlock)
-    return PA_ERR_INVALID;
-  if (out == nullptr || q == nullptr || table == nullptr || !aligned16(q) || !aligned16(out) ||
-      !aligned16(kv.k_pool) || !aligned16(kv.v_pool))
-    return PA_ERR_INVALID;
-  const int QR = kPfMRows / G;
-  const int64_t qtiles = (static_cast<int64_t>(chunk_len) + QR - 1) / QR;
-  if (qtiles > 65535) return PA_ERR_INVALID;
-  const int splits = prefill_splits(chunk_len, num_q_heads, q_start);
-  if (splits > 1 && chunk_len > 65535) return PA_ERR_INVALID;
+  PrefillArgs a;
+  dim3 grid;
+  const pa_status st = prefill_prepare(out, q, kv, table, table_len, q_start, chunk_len,
+                                       num_q_heads, scale, workspace, workspace_bytes, a, grid);
+  if (st != PA_OK || chunk_len == 0) return st;
   const int D = kv.head_dim;
-  float *ws_o = nullptr, *ws_m = nullptr, *ws_l = nullptr;
-  if (splits > 1) {
-    const uint64_t need = pa_prefill_workspace_bytes(chunk_len, num_q_heads, D, q_start);
-    if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
-      return PA_ERR_INVALID;
-    const int64_t slots = static_cast<int64_t>(splits) * chunk_len * num_q_heads;
-    ws_o = static_cast<float*>(workspace);
-    ws_m = ws_o + slots * D;
-    ws_l = ws_m + slots;
-  }
+  const int splits = a.splits;
+  float* ws_o = a.ws_o;
+  float* ws_m = a.ws_m;
+  float* ws_l = a.ws_l;
+  f16* oo = a.out;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const float scale_log2 = scale * 1.4426950408889634f;
-  const dim3 grid(static_cast<uint32_t>(kv.num_kv_heads), static_cast<uint32_t>(qtiles),
-                  static_cast<uint32_t>(splits));
-  const f16* qq = reinterpret_cast<const f16*>(q);
-  const f16* kp = reinterpret_cast<const f16*>(kv.k_pool);
-  const f16* vp = reinterpret_cast<const f16*>(kv.v_pool);
-  f16* oo = reinterpret_cast<f16*>(out);
   if (D == 128)
-    prefill_chunk_kernel<128><<<grid, dim3(kPfThreads), 0, s>>>(
-        qq, kp, vp, table, table_len, kv.num_blocks, kv.num_kv_heads, G, q_start, chunk_len,
-        scale_log2, splits, oo, ws_o, ws_m, ws_l);
+    prefill_chunk_kernel<128><<<grid, dim3(kPfThreads), 0, s>>>(a);
   else
-    prefill_chunk_kernel<64><<<grid, dim3(kPfThreads), 0, s>>>(
-        qq, kp, vp, table, table_len, kv.num_blocks, kv.num_kv_heads, G, q_start, chunk_len,
-        scale_log2, splits, oo, ws_o, ws_m, ws_l);
+    prefill_chunk_kernel<64><<<grid, dim3(kPfThreads), 0, s>>>(a);
   if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   if (splits > 1) {
     const dim3 rgrid(static_cast<uint32_t>(num_q_heads), static_cast<uint32_t>(chunk_len));

@@ -311,6 +311,38 @@ def test_decode_rejects_unknown_flags_before_any_launch():
     pa.pa_paged_attention_decode(**args, flags=0)
 
 
+def test_mixed_checks_run_before_any_launch():
+    # dummy addresses, never dereferenced: every call below fails or returns
+    # on the host
+    kv = pa.kv_view(None, None, 64, 8, 128)
+    kv.k_pool = kv.v_pool = 1 << 20
+    dec = pa.decode_batch(1 << 21, 1 << 22, 1 << 23, 256, 1 << 24, 4, 512, 4096, 1 << 25, 32)
+    pf = pa.prefill_chunk(1 << 26, 1 << 27, 1 << 28, 3125, 49488, 512)
+    ws_dec = pa.pa_decode_workspace_bytes(4, 32, 128, 4096, 512)
+    ws_pf = pa.pa_prefill_workspace_bytes(512, 32, 128, 49488)
+    assert ws_dec > 0 and ws_pf > 0
+    ws = pa.pa_mixed_workspace_bytes(dec, pf, 32, 128)
+    assert ws == -(-ws_dec // 256) * 256 + ws_pf
+    big = 1 << 40
+    with pytest.raises(pa.PaError):     # unknown flag
+        pa.pa_paged_attention_mixed(dec, pf, kv, 32, 0.088, 1 << 29, big, flags=2)
+    with pytest.raises(pa.PaError):     # workspace too small for the prefill part
+        pa.pa_paged_attention_mixed(dec, pf, kv, 32, 0.088, 1 << 29, ws - 16)
+    with pytest.raises(pa.PaError):     # 30 query heads over 8 kv heads
+        pa.pa_paged_attention_mixed(dec, pf, kv, 30, 0.088, 1 << 29, big)
+    bad_pf = pa.prefill_chunk(1 << 26, 1 << 27, 1 << 28, 3125, 49489, 512)   # past the table
+    with pytest.raises(pa.PaError):
+        pa.pa_paged_attention_mixed(dec, bad_pf, kv, 32, 0.088, 1 << 29, big)
+    no_list = pa.decode_batch(1 << 21, 1 << 22, 1 << 23, 256, 1 << 24, 4, 512, 4096, None, 32)
+    with pytest.raises(pa.PaError):     # decode units but no work list
+        pa.pa_paged_attention_mixed(no_list, pf, kv, 32, 0.088, 1 << 29, big)
+    # both parts empty: nothing to launch
+    empty_dec = pa.decode_batch(1 << 21, 1 << 22, 1 << 23, 256, 1 << 24, 0, 512, 4096, None, 0)
+    empty_pf = pa.prefill_chunk(1 << 26, 1 << 27, 1 << 28, 3125, 49488, 0)
+    assert pa.pa_mixed_workspace_bytes(empty_dec, empty_pf, 32, 128) == 0
+    pa.pa_paged_attention_mixed(empty_dec, empty_pf, kv, 32, 0.088, None, 0)
+
+
 def test_pool_counts_shared_blocks():
     lib = pa.pa_pool_create(8)
     try:
