@@ -425,7 +425,7 @@ def bench_mixed(args):
             "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
             "traffic": None,
-            "kernel": "pa_paged_attention_mixed (mixed_step_kernel + mixed_reduce_kernel); "
+            "kernel": "pa_paged_attention_mixed (mixed_step_kernel + mixed_prefill_reduce_kernel + decode_reduce_kernel); "
                       "achieved = the chunk's matrix-core flops over the whole mixed launch",
             "algorithmic_flops_per_launch": flops,
             "decode_algorithmic_bytes_per_launch": int(dec_bytes),

@@ -553,16 +553,19 @@ __device__ __forceinline__ void merge_store(const DecodeArgs& a, const MergeSlot
   });
 }
 
-// Merge the partial states of one (request, query head) over the 8 * NV
-// dims from d0: with M = max_p m_p and w_p = l_p * 2^(m_p - M),
-// out = sum_p w_p o_p / sum_p w_p, the sums taken in partition order (each
-// partition's exp sum rescaled to the common max, which gives exactly the
-// softmax over the whole sequence).  `bg` is the (request, kv head)'s first
+// Merge the partial states of partitions [p_begin, p_end) of one (request,
+// query head) over the 8 * NV dims from d0: with M = max_p m_p and
+// w_p = l_p * 2^(m_p - M), acc = sum_p w_p o_p and wsum = sum_p w_p, the sums
+// taken in partition order (each partition's exp sum rescaled to the common
+// max, which gives exactly the softmax over those partitions' tokens;
+// acc / wsum is the merged output).  `bg` is the (request, kv head)'s first
 // partial slot.  The partials of up to kChunk partitions are requested at
-// once, so a request of up to kChunk partitions costs one memory round trip.
+// once, so a range of up to kChunk partitions costs one memory round trip.
+// An empty range gives M = -inf, wsum = 0, acc = 0.
 template <int D, int NV>
-__device__ __forceinline__ void merge_partials(const DecodeArgs& a, int64_t bg, int h, int d0,
-                                               int n_parts, f16x8 (&res)[NV]) {
+__device__ __forceinline__ void merge_range(const DecodeArgs& a, int64_t bg, int h, int d0,
+                                            int p_begin, int p_end, float& M, float& wsum,
+                                            float (&acc)[NV][8]) {
   constexpr int kChunk = 8;
   const int G = a.G;
   f16x8 v[kChunk][NV];
@@ -570,7 +573,7 @@ __device__ __forceinline__ void merge_partials(const DecodeArgs& a, int64_t bg, 
   auto load = [&](int p0) {
 #pragma unroll
     for (int u = 0; u < kChunk; ++u) {
-      if (p0 + u < n_parts) {
+      if (p0 + u < p_end) {
         const int64_t slot = bg + static_cast<int64_t>(p0 + u) * G + h;
 #pragma unroll
         for (int c = 0; c < NV; ++c)
@@ -580,23 +583,23 @@ __device__ __forceinline__ void merge_partials(const DecodeArgs& a, int64_t bg, 
       }
     }
   };
-  load(0);
-  float M = -INFINITY;
+  load(p_begin);
+  M = -INFINITY;
 #pragma unroll
   for (int u = 0; u < kChunk; ++u)
-    if (u < n_parts) M = fmaxf(M, mm[u]);
-  for (int p = kChunk; p < n_parts; ++p) M = fmaxf(M, a.ws_m[bg + static_cast<int64_t>(p) * G + h]);
-  float wsum = 0.0f;
-  float acc[NV][8];
+    if (p_begin + u < p_end) M = fmaxf(M, mm[u]);
+  for (int p = p_begin + kChunk; p < p_end; ++p)
+    M = fmaxf(M, a.ws_m[bg + static_cast<int64_t>(p) * G + h]);
+  wsum = 0.0f;
 #pragma unroll
   for (int c = 0; c < NV; ++c)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[c][e] = 0.0f;
-  for (int p0 = 0; p0 < n_parts; p0 += kChunk) {
-    if (p0 > 0) load(p0);
+  for (int p0 = p_begin; p0 < p_end; p0 += kChunk) {
+    if (p0 > p_begin) load(p0);
 #pragma unroll
     for (int u = 0; u < kChunk; ++u) {
-      if (p0 + u < n_parts) {
+      if (p0 + u < p_end) {
         const float w = ll[u] * exp2f(mm[u] - M);
         wsum += w;
 #pragma unroll
@@ -606,22 +609,33 @@ __device__ __forceinline__ void merge_partials(const DecodeArgs& a, int64_t bg, 
       }
     }
   }
-  const float inv = 1.0f / wsum;
-#pragma unroll
-  for (int c = 0; c < NV; ++c)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) res[c][e] = static_cast<f16>(acc[c][e] * inv);
 }
 
-// Second kernel of both launch forms: one wavefront per (kv head, request)
+// Second kernel of both launch forms: one workgroup per (kv head, request)
 // merges the request's partitions, D/16 lanes per query head and 16 dims
 // per lane.  The kernel is bound by memory latency: it reads the request's
-// length, then all partials in one round trip.  Requests that fit in one
-// partition were written by the first kernel and are skipped.
+// length, then the partials, kChunk partitions per round trip.  With one
+// wavefront (requests of up to a few partitions) that lane merges all of
+// them.  With W = blockDim.x / 64 > 1 wavefronts (long requests), wavefront
+// w merges the contiguous range [w*P/W, (w+1)*P/W) of the P partitions, and
+// the W states (M_w, wsum_w, acc_w) are combined through LDS in wavefront
+// order: M = max M_w, out = sum_w acc_w 2^(M_w - M) / sum_w wsum_w 2^(M_w - M).
+// Requests that fit in one partition were written by the first kernel and
+// are skipped.  A NaN-flagged partial makes the output NaN either way.
+constexpr int kReduceMaxWaves = 4;
+constexpr int kReduceWideParts = 16;  // requests of at least this many partitions use 4 waves
+constexpr int kReduceEntry = 18;      // floats per combine entry: M, wsum, 16 accumulators
+
 template <int D>
 __device__ __forceinline__ void decode_reduce_unit(const DecodeArgs& a, int g, int b) {
   constexpr int LPH = D / 16;  // lanes per query head
+  // dynamic LDS (W > 1 only): [W][G * LPH][kReduceEntry] floats
+  extern __shared__ f32x4 sm_o4[];
+  float* const red = reinterpret_cast<float*>(sm_o4);
   const int G = a.G;
+  const int W = blockDim.x / kWave;
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
   const int part_tokens = a.part_blocks * kBlock;
   int L = scalar_load(a.seq_lens, b);
   if (L < 0) return;                                         // written as NaN already
@@ -629,11 +643,54 @@ __device__ __forceinline__ void decode_reduce_unit(const DecodeArgs& a, int g, i
   const int n_parts = min((L + part_tokens - 1) / part_tokens, a.p_max);
   if (n_parts <= 1) return;
   const int64_t bg = (static_cast<int64_t>(b) * a.n_kv + g) * a.p_max * G;
-  for (int idx = threadIdx.x; idx < G * LPH; idx += kWave) {
+  const int p0 = wave * n_parts / W;
+  const int p1 = (wave + 1) * n_parts / W;
+  for (int idx = lane; idx < G * LPH; idx += kWave) {
     const int h = idx / LPH;
     const int d0 = (idx % LPH) * 16;
+    float M, wsum, acc[2][8];
+    merge_range<D, 2>(a, bg, h, d0, p0, p1, M, wsum, acc);
+    if (W == 1) {
+      const float inv = 1.0f / wsum;
+      f16x8 r[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[c][e] = static_cast<f16>(acc[c][e] * inv);
+      f16* dst = a.out + ((static_cast<int64_t>(b) * a.n_kv + g) * G + h) * D + d0;
+      *reinterpret_cast<f16x8*>(dst) = r[0];
+      *reinterpret_cast<f16x8*>(dst + 8) = r[1];
+    } else {
+      float* e = red + (wave * G * LPH + idx) * kReduceEntry;
+      e[0] = M;
+      e[1] = wsum;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) e[2 + 8 * c + k] = acc[c][k];
+    }
+  }
+  if (W == 1) return;
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * LPH; idx += blockDim.x) {
+    const int h = idx / LPH;
+    const int d0 = (idx % LPH) * 16;
+    float M = -INFINITY;
+    for (int w = 0; w < W; ++w) M = fmaxf(M, red[(w * G * LPH + idx) * kReduceEntry]);
+    float wsum = 0.0f, acc[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) acc[k] = 0.0f;
+    for (int w = 0; w < W; ++w) {
+      const float* e = red + (w * G * LPH + idx) * kReduceEntry;
+      const float s = exp2f(e[0] - M);
+      wsum += e[1] * s;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) acc[k] += e[2 + k] * s;
+    }
+    const float inv = 1.0f / wsum;
     f16x8 r[2];
-    merge_partials<D, 2>(a, bg, h, d0, n_parts, r);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) r[k / 8][k % 8] = static_cast<f16>(acc[k] * inv);
     f16* dst = a.out + ((static_cast<int64_t>(b) * a.n_kv + g) * G + h) * D + d0;
     *reinterpret_cast<f16x8*>(dst) = r[0];
     *reinterpret_cast<f16x8*>(dst + 8) = r[1];
@@ -641,8 +698,16 @@ __device__ __forceinline__ void decode_reduce_unit(const DecodeArgs& a, int g, i
 }
 
 template <int D>
-__global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kReduceMaxWaves * kWave) void decode_reduce_kernel(DecodeArgs a) {
   decode_reduce_unit<D>(a, blockIdx.x, blockIdx.y);
+}
+
+// Wavefronts per reduce workgroup for a batch whose longest request has
+// p_max partitions, and the dynamic LDS that takes.
+inline int reduce_waves(int p_max) { return p_max >= kReduceWideParts ? kReduceMaxWaves : 1; }
+inline size_t reduce_lds(int p_max, int G, int D) {
+  const int W = reduce_waves(p_max);
+  return W > 1 ? static_cast<size_t>(W) * G * (D / 16) * kReduceEntry * sizeof(float) : 0;
 }
 
 // Grid form: one workgroup per (kv head, request, partition).
@@ -985,9 +1050,11 @@ static pa_status decode_launch(pa_half* out, const pa_half* q, const PoolArgs& k
   if (p_max > 1) {
     const dim3 rgrid(static_cast<uint32_t>(kv.num_kv_heads), static_cast<uint32_t>(batch));
     if (D == 128)
-      decode_reduce_kernel<128><<<rgrid, dim3(kWave), 0, s>>>(a);
+      decode_reduce_kernel<128><<<rgrid, dim3(reduce_waves(p_max) * kWave),
+                                 reduce_lds(p_max, a.G, 128), s>>>(a);
     else
-      decode_reduce_kernel<64><<<rgrid, dim3(kWave), 0, s>>>(a);
+      decode_reduce_kernel<64><<<rgrid, dim3(reduce_waves(p_max) * kWave),
+                                 reduce_lds(p_max, a.G, 64), s>>>(a);
   }
   return launch_status();
 }
@@ -1068,21 +1135,15 @@ __global__ __launch_bounds__(kPfThreads) void mixed_step_kernel(PrefillArgs pa, 
     merge_store<D, false>(da, ms, g, u.b, u.p, u.L, u.n_parts, lane);
 }
 
-// Second launch of the mixed step: one wavefront per prefill (row, head)
-// whose key range was split (the first pf_rows blocks), then one per decode
-// (kv head, request) with several partitions.
+// Merges after the mixed step's kernel: the prefill (row, head) pairs whose
+// key range was split, one wavefront each, in a kernel of their own (the
+// decode merge needs ~200 VGPRs, which in one kernel would cut the many short
+// prefill merges to 2 wavefronts per SIMD; measured on the long-context
+// step: 48 us fused vs 12 + 17 us as two launches), then the decode reduce.
 template <int D>
-__global__ __launch_bounds__(kWave) void mixed_reduce_kernel(PrefillArgs pa, int32_t pf_rows,
-                                                             DecodeArgs da) {
-  const int k = blockIdx.x;
-  if (k < pf_rows) {
-    const int n_q = pa.n_kv * pa.G;
-    prefill_reduce_row<D>(pa.chunk_len, n_q, pa.splits, pa.ws_o, pa.ws_m, pa.ws_l, pa.out,
-                          k % n_q, k / n_q);
-    return;
-  }
-  const int r = k - pf_rows;
-  decode_reduce_unit<D>(da, r % da.n_kv, r / da.n_kv);
+__global__ __launch_bounds__(kWave) void mixed_prefill_reduce_kernel(PrefillArgs pa) {
+  prefill_reduce_row<D>(pa.chunk_len, pa.n_kv * pa.G, pa.splits, pa.ws_o, pa.ws_m, pa.ws_l,
+                        pa.out, blockIdx.x, blockIdx.y);
 }
 
 constexpr uint64_t kMixedWsAlign = 256;
@@ -1144,16 +1205,22 @@ static pa_status mixed_launch(const pa_decode_batch* dec, const pa_prefill_chunk
           pa, static_cast<int32_t>(pf_wgs), qtiles, da, dec->work_items, n_items);
   }
   if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
-  const int64_t pf_rows =
-      pf->chunk_len > 0 && pa.splits > 1 ? static_cast<int64_t>(pf->chunk_len) * num_q_heads : 0;
-  const int64_t dec_rows =
-      dec->batch > 0 && da.p_max > 1 ? static_cast<int64_t>(kv.num_kv_heads) * dec->batch : 0;
-  if (pf_rows + dec_rows > 0) {
-    const dim3 rgrid(static_cast<uint32_t>(pf_rows + dec_rows));
+  if (pf->chunk_len > 0 && pa.splits > 1) {
+    const dim3 rgrid(static_cast<uint32_t>(num_q_heads), static_cast<uint32_t>(pf->chunk_len));
     if (D == 128)
-      mixed_reduce_kernel<128><<<rgrid, dim3(kWave), 0, s>>>(pa, static_cast<int32_t>(pf_rows), da);
+      mixed_prefill_reduce_kernel<128><<<rgrid, dim3(kWave), 0, s>>>(pa);
     else
-      mixed_reduce_kernel<64><<<rgrid, dim3(kWave), 0, s>>>(pa, static_cast<int32_t>(pf_rows), da);
+      mixed_prefill_reduce_kernel<64><<<rgrid, dim3(kWave), 0, s>>>(pa);
+    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+  }
+  if (dec->batch > 0 && da.p_max > 1) {
+    const dim3 rgrid(static_cast<uint32_t>(kv.num_kv_heads), static_cast<uint32_t>(dec->batch));
+    if (D == 128)
+      decode_reduce_kernel<128><<<rgrid, dim3(reduce_waves(da.p_max) * kWave),
+                                 reduce_lds(da.p_max, da.G, 128), s>>>(da);
+    else
+      decode_reduce_kernel<64><<<rgrid, dim3(reduce_waves(da.p_max) * kWave),
+                                 reduce_lds(da.p_max, da.G, 64), s>>>(da);
   }
   return launch_status();
 }
