@@ -1100,7 +1100,11 @@ __global__ __launch_bounds__(kPfThreads) void mixed_step_kernel(PrefillArgs pa, 
   const int wg = blockIdx.x;
   if (wg < pf_wgs) {
     const int rest = wg / pa.n_kv;
-    prefill_tile<D>(pa, wg % pa.n_kv, rest % pf_qtiles, rest / pf_qtiles, lds.pf);
+    // no raised wave priority here, unlike the prefill launch: tiles that
+    // share CUs with decode units starved them (measured on the
+    // long-context step: 650 us with the prefill launch's priorities, also
+    // when decode units ran at a higher priority, vs 607 us without)
+    prefill_tile<D, 0>(pa, wg % pa.n_kv, rest % pf_qtiles, rest / pf_qtiles, lds.pf);
     return;
   }
   if (threadIdx.x < 2) {

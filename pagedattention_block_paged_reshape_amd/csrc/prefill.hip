@@ -34,10 +34,18 @@
 
 namespace pa {
 
+// Wave priority of the tile's phases (prefill_tile's PRIO bits): raised
+// during the softmax and the PV products.  Two tile workgroups share each
+// SIMD; letting the wavefront that is past its score products issue first
+// keeps the matrix pipe fed while the other one computes its scores.
+// Measured on the long-context chunk: 474 us vs 498 us with no priority
+// (PV alone 481-483 us, scores alone 510 us, scores + PV 502 us).
+constexpr int kPfPrio = kPfPrioSoftmax | kPfPrioPV;
+
 template <int D>
 __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a) {
   __shared__ PrefillLds<D> lds;
-  prefill_tile<D>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds);
+  prefill_tile<D, kPfPrio>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds);
 }
 
 // Merge the key splits of each (row, head) by log-sum-exp.

@@ -11,6 +11,11 @@
 namespace pa {
 
 constexpr int kPfThreads = 256;
+// Phases of a key step whose wave priority prefill_tile raises (PRIO bits).
+constexpr int kPfPrioScores = 1;   // S^T = K . Q^T products
+constexpr int kPfPrioPV = 2;       // O^T += V^T . P^T products
+constexpr int kPfPrioSoftmax = 4;  // online softmax between them
+constexpr int kPfPrioStage = 8;    // barriers, LDS stores and next loads
 constexpr int kPfMRows = 128;   // M-rows per workgroup
 constexpr int kPfKeys = 64;     // keys per step
 constexpr int kPfMaxSplits = 32;
@@ -62,7 +67,8 @@ struct PrefillArgs {
 // One workgroup's tile: kv head g, query tile qt, key split z.  All 256
 // threads of the workgroup take part (it has two workgroup barriers per key
 // step).
-template <int D>
+// PRIO: the kPfPrio* phases run at wave priority 1 (else 0).
+template <int D, int PRIO>
 __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int g, int qt, int z,
                                              PrefillLds<D>& lds) {
   const f16* __restrict__ q = a.q;
@@ -209,13 +215,16 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int g, int qt
   }
   if (st0 + 1 < st1) read_ids(st0 + 1, ids);
   for (int step = st0; step < st1; ++step) {
+    if constexpr (PRIO & kPfPrioStage) __builtin_amdgcn_s_setprio(1);
     __syncthreads();  // previous step's LDS reads are done
     stash();
     __syncthreads();
     if (step + 1 < st1) fetch(step + 1, ids);
+    if constexpr (PRIO & kPfPrioStage) __builtin_amdgcn_s_setprio(0);
 
     const int key0 = step * kPfKeys;
     // scores S^T[key][M-row]: 4 key tiles x 2 M-row tiles
+    if constexpr (PRIO & kPfPrioScores) __builtin_amdgcn_s_setprio(1);
     f32x4 s[4][2];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -232,6 +241,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int g, int qt
       }
     }
 
+    if constexpr (PRIO & kPfPrioScores) __builtin_amdgcn_s_setprio(0);
+    if constexpr (PRIO & kPfPrioSoftmax) __builtin_amdgcn_s_setprio(1);
     if (step + 2 < st1) read_ids(step + 2, ids);
 
     // causal mask, on the raw scores, only where the step crosses the
@@ -279,6 +290,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int g, int qt
     }
 
     // O^T[dim][M-row] += V^T[dim][key] . P^T[key][M-row]
+    if constexpr (PRIO & kPfPrioSoftmax) __builtin_amdgcn_s_setprio(0);
+    if constexpr (PRIO & kPfPrioPV) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -289,6 +302,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int g, int qt
         for (int nt = 0; nt < 2; ++nt) o[dt][nt] = mfma16x16x32(va, pb8[ks][nt], o[dt][nt]);
       }
     }
+    if constexpr (PRIO & kPfPrioPV) __builtin_amdgcn_s_setprio(0);
   }
 
   if (bad) sbad = 1;
