@@ -40,7 +40,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["pagedattention_block_paged_reshape_amd/csrc/decode.hip",
+KERNEL_SOURCES = ["pagedattention_block_paged_reshape_amd/csrc/decode_core.h",
+                  "pagedattention_block_paged_reshape_amd/csrc/decode.hip",
                   "pagedattention_block_paged_reshape_amd/csrc/pa_device.h"]
 TRAFFIC_FILES = {"fp16": os.path.join(PROFILES, "decode_llama3-70b_traffic.md"),
                  "fp8": os.path.join(PROFILES, "decode_llama3-70b_fp8_traffic.md")}

@@ -21,7 +21,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedattn.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["cache_ops.hip", "decode.hip", "prefill.hip"]
+HIP_SOURCES = ["cache_ops.hip", "decode.hip", "mixed.hip", "prefill.hip"]
 HOST_SOURCES = ["block_pool.cpp", "decode_plan.cpp", "scheduler.cpp"]
 
 # Packed-FP32 VALU ops are kept out of the generated code.
@@ -35,6 +35,7 @@ GXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
 # VGPRs, which they rescale with ordinary VALU ops (no AGPR round trips); for
 # the prefill kernel this also fits two wavefronts per SIMD.
 EXTRA_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "mixed.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
                "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 

@@ -1,0 +1,201 @@
+// Mixed decode + prefill launch on gfx950.
+//
+// Mixed step: the decode units of a batch and the tiles of one prefill chunk
+// in one launch over one pool (a scheduler step runs both kinds of work in
+// one forward pass: ta-paperlens "scheduler skeleton"; techfeed.io ngrok
+// summary, "the scheduler").  Workgroups of 4 wavefronts; the first pf_wgs
+// take prefill tiles (kv head fastest, then query tile, then key split, as
+// the prefill launch's grid), the rest decode units, two per workgroup, one
+// per wavefront pair, each as in the grid form.  The prefill tiles, being the
+// long work, start first; decode units fill the CUs as tiles retire, so the
+// chunk's ragged end and the launch gap between the two kinds of work
+// overlap with memory-bound decode.  Decode unit t of kv head g is entry t
+// of the work list; the workgroup that holds entries 2j and 2j+1 of kv head g
+// is number pf_wgs + j*n_kv + g, so with 8 kv heads and pf_wgs a multiple of 8
+// each head's decode units land on one XCD, as in the decode launch.
+#include "decode_core.h"
+#include "prefill_tile.h"
+
+namespace pa {
+
+// LDS of a mixed workgroup: one prefill tile's, or two decode units' merge
+// states ([pair][wave][16] max and sum, [pair][wave][G <= 16][D + 4] O^T rows).
+template <int D>
+struct MixedDecodeLds {
+  __attribute__((aligned(16))) float o[2][kDecodeWaves * 16 * (D + 4)];
+  float m[2][kDecodeWaves * 16];
+  float l[2][kDecodeWaves * 16];
+  int arrive[2];
+  int bad[2];
+};
+
+template <int D>
+union MixedLds {
+  PrefillLds<D> pf;
+  MixedDecodeLds<D> dec;
+};
+
+template <int D, bool KEEP>
+__global__ __launch_bounds__(kPfThreads) void mixed_step_kernel(PrefillArgs pa, int32_t pf_wgs,
+                                                                 int32_t pf_qtiles, DecodeArgs da,
+                                                                 const int32_t* __restrict__ items,
+                                                                 int32_t n_items) {
+  __shared__ MixedLds<D> lds;
+  const int wg = blockIdx.x;
+  if (wg < pf_wgs) {
+    const int rest = wg / pa.n_kv;
+    // no raised wave priority here, unlike the prefill launch: tiles that
+    // share CUs with decode units starved them (measured on the
+    // long-context step: 650 us with the prefill launch's priorities, also
+    // when decode units ran at a higher priority, vs 607 us without)
+    prefill_tile<D, 0>(pa, wg % pa.n_kv, rest % pf_qtiles, rest / pf_qtiles, lds.pf);
+    return;
+  }
+  if (threadIdx.x < 2) {
+    lds.dec.arrive[threadIdx.x] = 0;
+    lds.dec.bad[threadIdx.x] = 0;
+  }
+  __syncthreads();
+  const int j = wg - pf_wgs;
+  const int pair = uniform(threadIdx.x >> 7);
+  const int wave = uniform((threadIdx.x >> 6) & 1);
+  const int lane = threadIdx.x & 63;
+  const int g = j % da.n_kv;
+  const int t = 2 * (j / da.n_kv) + pair;
+  if (t >= n_items) return;
+  const uint32_t packed = static_cast<uint32_t>(scalar_load(items, t));
+  const Unit u = make_unit(da, static_cast<int>(packed >> 16), static_cast<int>(packed & 0xFFFFu),
+                           wave, lane);
+  const Unit nx = no_unit();
+  typedef TileRegs<D, false> TR;
+  f16x8 qf[D / 32];
+  typename TR::K kA[TR::NB * TR::NK], kB[TR::NB * TR::NK];
+  typename TR::V vA[TR::NB * TR::NV], vB[TR::NB * TR::NV];
+  if (u.cnt > 0) {
+    load_q<D>(da, g, u.b, lane, qf);
+    load_set<D, KEEP, false>(da, g, u, nx, 0, true, lane, kA, vA);
+  }
+  WaveState<D> st;
+  run_unit<D, KEEP, false>(da, g, wave, lane, u, nx, qf, kA, vA, kB, vB, st);
+  const MergeSlot<D> ms{lds.dec.m[pair], lds.dec.l[pair], lds.dec.o[pair], &lds.dec.arrive[pair],
+                        &lds.dec.bad[pair]};
+  if (post_state<D>(ms, st, da.G, wave, lane, u.bad) && u.ok)
+    merge_store<D, false>(da, ms, g, u.b, u.p, u.L, u.n_parts, lane);
+}
+
+// Merges after the mixed step's kernel: the prefill (row, head) pairs whose
+// key range was split, one wavefront each, in a kernel of their own (the
+// decode merge needs ~200 VGPRs, which in one kernel would cut the many short
+// prefill merges to 2 wavefronts per SIMD; measured on the long-context
+// step: 48 us fused vs 12 + 17 us as two launches), then the decode partitions
+// (the decode reduce's code under a name of this file's own).
+template <int D>
+__global__ __launch_bounds__(kReduceMaxWaves * kWave) void mixed_decode_reduce_kernel(
+    DecodeArgs a) {
+  decode_reduce_unit<D>(a, blockIdx.x, blockIdx.y);
+}
+
+template <int D>
+__global__ __launch_bounds__(kWave) void mixed_prefill_reduce_kernel(PrefillArgs pa) {
+  prefill_reduce_row<D>(pa.chunk_len, pa.n_kv * pa.G, pa.splits, pa.ws_o, pa.ws_m, pa.ws_l,
+                        pa.out, blockIdx.x, blockIdx.y);
+}
+
+constexpr uint64_t kMixedWsAlign = 256;
+
+static uint64_t mixed_decode_ws(const pa_decode_batch& d, int32_t num_q_heads, int32_t head_dim) {
+  const uint64_t b = pa_decode_workspace_bytes(d.batch, num_q_heads, head_dim, d.max_seq_len,
+                                               d.partition_size);
+  return (b + kMixedWsAlign - 1) / kMixedWsAlign * kMixedWsAlign;
+}
+
+static pa_status mixed_launch(const pa_decode_batch* dec, const pa_prefill_chunk* pf,
+                              const pa_kv_view& kv, int32_t num_q_heads, float scale,
+                              void* workspace, uint64_t workspace_bytes, uint32_t flags,
+                              void* stream) {
+  if (dec == nullptr || pf == nullptr) return PA_ERR_INVALID;
+  if ((flags & ~static_cast<uint32_t>(PA_DECODE_KEEP_KV)) != 0) return PA_ERR_INVALID;
+  if (dec->batch > 0 && dec->n_items > 0 && dec->work_items == nullptr) return PA_ERR_INVALID;
+  const PoolArgs pool{kv.k_pool, kv.v_pool, kv.num_blocks, kv.block_size, kv.num_kv_heads,
+                      kv.head_dim, false, 1.0f, 1.0f};
+  const uint64_t dec_ws = mixed_decode_ws(*dec, num_q_heads, kv.head_dim);
+  if (workspace_bytes < dec_ws) return PA_ERR_INVALID;
+  DecodeArgs da{};
+  pa_status st = decode_prepare(dec->out, dec->q, pool, dec->tables, dec->max_blocks,
+                                dec->seq_lens, dec->batch, num_q_heads, scale,
+                                dec->partition_size, dec->max_seq_len, dec->work_items,
+                                dec->n_items, workspace, workspace_bytes, flags, da);
+  if (st != PA_OK) return st;
+  PrefillArgs pa{};
+  dim3 pgrid(0, 0, 0);
+  void* pf_ws = workspace == nullptr ? nullptr : static_cast<char*>(workspace) + dec_ws;
+  st = prefill_prepare(pf->out, pf->q, kv, pf->table, pf->table_len, pf->q_start, pf->chunk_len,
+                       num_q_heads, scale, pf_ws, workspace_bytes - dec_ws, pa, pgrid);
+  if (st != PA_OK) return st;
+  const int64_t pf_wgs =
+      pf->chunk_len > 0 ? static_cast<int64_t>(pgrid.x) * pgrid.y * pgrid.z : 0;
+  const int64_t dec_wgs =
+      dec->batch > 0 ? static_cast<int64_t>(kv.num_kv_heads) * ((dec->n_items + 1) / 2) : 0;
+  if (pf_wgs + dec_wgs > 0x7FFFFFFF) return PA_ERR_INVALID;
+  if (pf_wgs + dec_wgs == 0) return PA_OK;
+  const bool keep = (flags & PA_DECODE_KEEP_KV) != 0;
+  const int D = kv.head_dim;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(static_cast<uint32_t>(pf_wgs + dec_wgs));
+  const int32_t qtiles = static_cast<int32_t>(pgrid.y);
+  const int32_t n_items = dec->batch > 0 ? dec->n_items : 0;
+  if (D == 128) {
+    if (keep)
+      mixed_step_kernel<128, true><<<grid, dim3(kPfThreads), 0, s>>>(
+          pa, static_cast<int32_t>(pf_wgs), qtiles, da, dec->work_items, n_items);
+    else
+      mixed_step_kernel<128, false><<<grid, dim3(kPfThreads), 0, s>>>(
+          pa, static_cast<int32_t>(pf_wgs), qtiles, da, dec->work_items, n_items);
+  } else {
+    if (keep)
+      mixed_step_kernel<64, true><<<grid, dim3(kPfThreads), 0, s>>>(
+          pa, static_cast<int32_t>(pf_wgs), qtiles, da, dec->work_items, n_items);
+    else
+      mixed_step_kernel<64, false><<<grid, dim3(kPfThreads), 0, s>>>(
+          pa, static_cast<int32_t>(pf_wgs), qtiles, da, dec->work_items, n_items);
+  }
+  if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+  if (pf->chunk_len > 0 && pa.splits > 1) {
+    const dim3 rgrid(static_cast<uint32_t>(num_q_heads), static_cast<uint32_t>(pf->chunk_len));
+    if (D == 128)
+      mixed_prefill_reduce_kernel<128><<<rgrid, dim3(kWave), 0, s>>>(pa);
+    else
+      mixed_prefill_reduce_kernel<64><<<rgrid, dim3(kWave), 0, s>>>(pa);
+    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+  }
+  if (dec->batch > 0 && da.p_max > 1) {
+    const dim3 rgrid(static_cast<uint32_t>(kv.num_kv_heads), static_cast<uint32_t>(dec->batch));
+    if (D == 128)
+      mixed_decode_reduce_kernel<128><<<rgrid, dim3(reduce_waves(da.p_max) * kWave),
+                                 reduce_lds(da.p_max, da.G, 128), s>>>(da);
+    else
+      mixed_decode_reduce_kernel<64><<<rgrid, dim3(reduce_waves(da.p_max) * kWave),
+                                 reduce_lds(da.p_max, da.G, 64), s>>>(da);
+  }
+  return launch_status();
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" uint64_t pa_mixed_workspace_bytes(const pa_decode_batch* dec,
+                                             const pa_prefill_chunk* pf, int32_t num_q_heads,
+                                             int32_t head_dim) {
+  if (dec == nullptr || pf == nullptr) return 0;
+  return mixed_decode_ws(*dec, num_q_heads, head_dim) +
+         prefill_ws_bytes(pf->chunk_len, num_q_heads, head_dim, pf->q_start);
+}
+
+extern "C" pa_status pa_paged_attention_mixed(const pa_decode_batch* dec,
+                                              const pa_prefill_chunk* pf, pa_kv_view kv,
+                                              int32_t num_q_heads, float scale, void* workspace,
+                                              uint64_t workspace_bytes, uint32_t flags,
+                                              void* stream) {
+  return mixed_launch(dec, pf, kv, num_q_heads, scale, workspace, workspace_bytes, flags, stream);
+}
