@@ -18,6 +18,7 @@ constexpr int kPfPrioSoftmax = 4;  // online softmax between them
 constexpr int kPfPrioStage = 8;    // barriers, LDS stores and next loads
 constexpr int kPfMRows = 128;   // M-rows per workgroup
 constexpr int kPfKeys = 64;     // keys per step
+constexpr float kPfRescaleSlack = 8.0f;  // log2 headroom of the softmax reference max
 constexpr int kPfMaxSplits = 32;
 #ifndef PA_PF_TARGET_WGS
 #define PA_PF_TARGET_WGS 512
@@ -67,6 +68,17 @@ struct PrefillArgs {
 // One workgroup's tile: kv head g, query tile qt, key split z.  All 256
 // threads of the workgroup take part (it has two workgroup barriers per key
 // step).
+// Wave priority at the switch from phase FROM to phase TO of a key step
+// (kPfPrio* bits of PRIO: priority 1, else 0).  Only a change emits an
+// s_setprio, which the compiler does not schedule across.  The loop's first
+// phase is entered from PV's level (priority 0 before the loop).
+template <int PRIO, int FROM, int TO>
+__device__ __forceinline__ void phase_prio() {
+  constexpr int from = (PRIO & FROM) ? 1 : 0;
+  constexpr int to = (PRIO & TO) ? 1 : 0;
+  if constexpr (from != to) __builtin_amdgcn_s_setprio(to);
+}
+
 // PRIO: the kPfPrio* phases run at wave priority 1 (else 0).
 template <int D, int PRIO>
 __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int g, int qt, int z,
@@ -215,16 +227,15 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int g, int qt
   }
   if (st0 + 1 < st1) read_ids(st0 + 1, ids);
   for (int step = st0; step < st1; ++step) {
-    if constexpr (PRIO & kPfPrioStage) __builtin_amdgcn_s_setprio(1);
+    phase_prio<PRIO, kPfPrioPV, kPfPrioStage>();
     __syncthreads();  // previous step's LDS reads are done
     stash();
     __syncthreads();
     if (step + 1 < st1) fetch(step + 1, ids);
-    if constexpr (PRIO & kPfPrioStage) __builtin_amdgcn_s_setprio(0);
 
     const int key0 = step * kPfKeys;
     // scores S^T[key][M-row]: 4 key tiles x 2 M-row tiles
-    if constexpr (PRIO & kPfPrioScores) __builtin_amdgcn_s_setprio(1);
+    phase_prio<PRIO, kPfPrioStage, kPfPrioScores>();
     f32x4 s[4][2];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -241,8 +252,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int g, int qt
       }
     }
 
-    if constexpr (PRIO & kPfPrioScores) __builtin_amdgcn_s_setprio(0);
-    if constexpr (PRIO & kPfPrioSoftmax) __builtin_amdgcn_s_setprio(1);
+    phase_prio<PRIO, kPfPrioScores, kPfPrioSoftmax>();
     if (step + 2 < st1) read_ids(step + 2, ids);
 
     // causal mask, on the raw scores, only where the step crosses the
@@ -258,20 +268,46 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int g, int qt
             if (key0 + mt * 16 + 4 * lg + j > limit) s[mt][nt][j] = -INFINITY;
       }
     }
-    f16x8 pb8[2][2];  // [k-step of PV][n-tile]
+    // Online softmax in base 2 against a per-row reference max m_ref (the
+    // exponent's offset): P = 2^(s * scale_log2 - m_ref), l and O
+    // accumulated against the same m_ref.  m_ref moves (rescaling l and O by
+    // 2^(m_ref_old - m_ref_new)) only when a row's score exceeds it by more
+    // than kPfRescaleSlack; otherwise P <= 2^kPfRescaleSlack, well inside
+    // fp16.  Any reference gives the same o / l, and split partials store
+    // their m_ref with l, so the merge is unchanged.  One wave-uniform branch
+    // for both M-row tiles, rarely taken after the first keys (measured on
+    // the long-context chunk: 467 us vs 474 us with a rescale whenever the
+    // max moved).  Forcing the PV products of one tile between the other
+    // tile's exponentials (scheduling hints, V operands read twice) was
+    // slower: 480-494 us.
+    float mloc[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      float mloc = -INFINITY;
+      float mx = -INFINITY;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) mloc = fmaxf(mloc, s[mt][nt][j]);
-      mloc = wave_max_xor16_32(mloc);
-      // running max in base-2 units (scale_log2 > 0, so max(s) * c = max(s * c))
-      const float m_new = fmaxf(m_run[nt], mloc * scale_log2);
-      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-      // hardware 2^x: results below 2^-126 flush to 0, which softmax ignores
-      const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_use);
+        for (int j = 0; j < 4; ++j) mx = fmaxf(mx, s[mt][nt][j]);
+      // in base-2 units (scale_log2 > 0, so max(s) * c = max(s * c))
+      mloc[nt] = wave_max_xor16_32(mx) * scale_log2;
+    }
+    if (__builtin_amdgcn_ballot_w64(mloc[0] > m_run[0] + kPfRescaleSlack ||
+                                    mloc[1] > m_run[1] + kPfRescaleSlack) != 0) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const float m_new = fmaxf(m_run[nt], mloc[nt]);
+        // hardware 2^x: results below 2^-126 flush to 0, which softmax ignores
+        const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run[nt] - m_new);
+        l_run[nt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt][nt] *= alpha;
+        m_run[nt] = m_new;
+      }
+    }
+    f16x8 pb8[2][2];  // [k-step of PV][n-tile]
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const float m_use = m_run[nt] == -INFINITY ? 0.0f : m_run[nt];
       float psum = 0.0f;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
@@ -281,17 +317,11 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int g, int qt
           psum += p;
           pb8[mt >> 1][nt][(mt & 1) * 4 + j] = static_cast<f16>(p);
         }
-      l_run[nt] = l_run[nt] * alpha + psum;
-      m_run[nt] = m_new;
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[dt][nt] *= alpha;
-      }
+      l_run[nt] += psum;
     }
 
     // O^T[dim][M-row] += V^T[dim][key] . P^T[key][M-row]
-    if constexpr (PRIO & kPfPrioSoftmax) __builtin_amdgcn_s_setprio(0);
-    if constexpr (PRIO & kPfPrioPV) __builtin_amdgcn_s_setprio(1);
+    phase_prio<PRIO, kPfPrioSoftmax, kPfPrioPV>();
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -302,8 +332,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int g, int qt
         for (int nt = 0; nt < 2; ++nt) o[dt][nt] = mfma16x16x32(va, pb8[ks][nt], o[dt][nt]);
       }
     }
-    if constexpr (PRIO & kPfPrioPV) __builtin_amdgcn_s_setprio(0);
   }
+  if constexpr ((PRIO & kPfPrioPV) != 0) __builtin_amdgcn_s_setprio(0);
 
   if (bad) sbad = 1;
   __syncthreads();

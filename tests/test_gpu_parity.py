@@ -232,6 +232,24 @@ def test_prefill_chunk_parity(decode_lengths, q_start, chunk, n_q, n_kv, d):
     log(f"prefill q_start={q_start} chunk={chunk} G={n_q // n_kv} d={d}: max err {err:.2e}")
 
 
+@pytest.mark.parametrize("q_start,chunk", [(700, 64), (2500, 300)])   # one split / several
+def test_prefill_growing_scores_move_the_softmax_reference(q_start, chunk):
+    """Key magnitudes grow with position (up to ~50x), so each row's running
+    maximum climbs by far more than the kernel's 8 (log2) units of slack
+    many times within one tile and split: every reference move rescales the
+    partial sums, and the result must still be the oracle's softmax."""
+    w = make_mixed_workload([], q_start, chunk, n_q=32, n_kv=8, d=128, seed=77 + chunk)
+    ramp = lambda pos: (1.0 + pos / 50.0)[:, None, None]
+    pos_setup = np.arange(len(w.setup_k), dtype=np.float64)
+    pos_step = q_start + np.arange(len(w.step_k), dtype=np.float64)
+    w.setup_k = (w.setup_k.astype(np.float64) * ramp(pos_setup)).astype(np.float16)
+    w.step_k = (w.step_k.astype(np.float64) * ramp(pos_step)).astype(np.float16)
+    st = oracle_run(w)
+    res = gpu_run(w, decode=False)
+    err = assert_close(res["prefill"], prefill_reference(w, st), "prefill, growing scores")
+    log(f"prefill growing scores q_start={q_start} chunk={chunk}: max err {err:.2e}")
+
+
 def test_prefill_last_row_matches_decode_kernel():
     """The chunk's last row sees exactly the prompt's keys, as a decode of
     the same request would."""
