@@ -182,7 +182,7 @@ def bench_serve(args):
     outputs uniform in [64, 256], arriving over the first 64 steps; the pool
     holds half of what all requests would need at once."""
     import torch
-    from synth.serving import make_trace, token_rows
+    from synth.serving import make_trace, token_rows_kvq
     from pagedattention_block_paged_reshape_amd.cache import PagedKVCache
     from pagedattention_block_paged_reshape_amd.serve import ServingLoop
     dev = torch.device("cuda:0")
@@ -193,7 +193,7 @@ def bench_serve(args):
     blocks = need // 2
     order = np.random.default_rng(2003).permutation(blocks).astype(np.int32)
     cache = PagedKVCache(blocks, n_kv, d, order, dev)
-    row_fn = lambda r, p, t, w: token_rows(r, p, t, w, xp=torch)
+    rows_fn = lambda r, p, wkv, wq: token_rows_kvq(r, p, wkv, wq, xp=torch)
     budget, max_running = 8192, 256
 
     def run(loop, trace):
@@ -209,11 +209,11 @@ def bench_serve(args):
                 return step
 
     # clock warm-up on a small trace of the same shape (not timed)
-    warm = ServingLoop(cache, n_q, 1.0 / np.sqrt(d), budget, max_running, row_fn=row_fn)
+    warm = ServingLoop(cache, n_q, 1.0 / np.sqrt(d), budget, max_running, rows_fn=rows_fn)
     run(warm, make_trace(32, seed=1, arrive_over=4))
     warm.close()
     torch.cuda.synchronize()
-    loop = ServingLoop(cache, n_q, 1.0 / np.sqrt(d), budget, max_running, row_fn=row_fn)
+    loop = ServingLoop(cache, n_q, 1.0 / np.sqrt(d), budget, max_running, rows_fn=rows_fn)
     t0 = time.perf_counter()
     steps = run(loop, tr)
     torch.cuda.synchronize()

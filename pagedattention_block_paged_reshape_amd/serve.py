@@ -29,9 +29,10 @@ from .cache import PagedKVCache
 class ServingLoop:
     def __init__(self, cache: PagedKVCache, num_q_heads: int, scale: float, token_budget: int,
                  max_running: int, partition: int = 512, row_fn=None,
-                 keep_outputs: bool = False):
+                 keep_outputs: bool = False, rows_fn=None):
         """row_fn(req, pos, tag, width) -> fp16 rows on the cache's device
-        (int64 device tensors in); keep_outputs stores every attention
+        (int64 device tensors in), or rows_fn(req, pos, width_kv, width_q) ->
+        (k, v, q) rows in one call; keep_outputs stores every attention
         output row by (request, position) for checking."""
         self.cache = cache
         self.n_q = int(num_q_heads)
@@ -40,6 +41,7 @@ class ServingLoop:
         self.max_running = int(max_running)
         self.partition = int(partition)
         self.row_fn = row_fn
+        self.rows_fn = rows_fn
         self.keep = keep_outputs
         # (request, position) -> (output row [n_q][d], "decode" | "prefill")
         self.outputs: Dict[Tuple[int, int], Tuple[torch.Tensor, str]] = {}
@@ -73,6 +75,12 @@ class ServingLoop:
             setattr(self, attr, ws)
         return ws
 
+    def _h2d(self, a: np.ndarray) -> torch.Tensor:
+        """Host array to the device through a pinned staging copy, so the
+        copy never waits for the GPU to drain the stream."""
+        return torch.from_numpy(np.ascontiguousarray(a)).pin_memory().to(self.dev,
+                                                                         non_blocking=True)
+
     def step(self, stream=None) -> List[int]:
         """Plan and run one step; returns the requests that finished."""
         stream = stream or torch.cuda.current_stream(self.dev)
@@ -82,23 +90,35 @@ class ServingLoop:
         if items:
             req = np.concatenate([np.full(n, r, dtype=np.int64) for r, _, n, _ in items])
             pos = np.concatenate([np.arange(s, s + n, dtype=np.int64) for _, s, n, _ in items])
-            d_req = torch.from_numpy(req).to(self.dev, non_blocking=True)
-            d_pos = torch.from_numpy(pos).to(self.dev, non_blocking=True)
+            d_req = self._h2d(req)
+            d_pos = self._h2d(pos)
             width = self.cache.n_kv * self.d
-            k = self.row_fn(d_req, d_pos, 0, width).view(-1, self.cache.n_kv, self.d)
-            v = self.row_fn(d_req, d_pos, 1, width).view(-1, self.cache.n_kv, self.d)
-            q = self.row_fn(d_req, d_pos, 2, self.n_q * self.d).view(-1, self.n_q, self.d)
-            slots = torch.from_numpy(plan["slots"]).to(self.dev, non_blocking=True)
+            if self.rows_fn is not None:
+                k, v, q = self.rows_fn(d_req, d_pos, width, self.n_q * self.d)
+                k = k.contiguous().view(-1, self.cache.n_kv, self.d)
+                v = v.contiguous().view(-1, self.cache.n_kv, self.d)
+                q = q.view(-1, self.n_q, self.d)
+            else:
+                k = self.row_fn(d_req, d_pos, 0, width).view(-1, self.cache.n_kv, self.d)
+                v = self.row_fn(d_req, d_pos, 1, width).view(-1, self.cache.n_kv, self.d)
+                q = self.row_fn(d_req, d_pos, 2, self.n_q * self.d).view(-1, self.n_q, self.d)
+            slots = self._h2d(plan["slots"])
             if len(plan["copies"]):
-                d_copies = torch.from_numpy(np.ascontiguousarray(plan["copies"])).to(self.dev)
+                d_copies = self._h2d(plan["copies"])
                 self.cache.copy_blocks(d_copies, len(plan["copies"]), stream)
             self.cache.store(k, v, slots, len(req), stream)
             offs = np.cumsum([0] + [n for _, _, n, _ in items])
             dec = [i for i, it in enumerate(items) if it[3]]
             pre = [i for i, it in enumerate(items) if not it[3]]
             if dec:
-                self._decode([items[i] for i in dec], q[torch.tensor([offs[i] for i in dec],
-                                                                      device=self.dev)], stream)
+                rows = offs[dec]
+                # decode items come first (one token each), so their query
+                # rows are usually a leading slice
+                if np.array_equal(rows, np.arange(len(dec))):
+                    q_dec = q[:len(dec)]
+                else:
+                    q_dec = q[self._h2d(rows.astype(np.int64))]
+                self._decode([items[i] for i in dec], q_dec, stream)
             for i in pre:
                 r, s, n, _ = items[i]
                 self._prefill(r, s, n, q[offs[i]:offs[i] + n], stream)
@@ -111,16 +131,18 @@ class ServingLoop:
 
     def _decode(self, items, q: torch.Tensor, stream):
         ids = [r for r, _, _, _ in items]
-        tab, ln, max_blocks = self.cache.host_tables(ids)
+        # each request's length after this step is known from its item
+        max_blocks = max(-(-(s + 1) // L.BLOCK_SIZE) for _, s, _, _ in items)
+        tab, ln = L.pa_block_tables(self.cache.pool, ids, max_blocks)
         assert [int(x) for x in ln] == [s + 1 for _, s, _, _ in items]
         max_len = int(ln.max())
         work = L.pa_decode_work_items(ln, self.partition)
         ws_bytes = L.pa_decode_workspace_bytes(len(ids), self.n_q, self.d, max_len, self.partition)
         ws = self._workspace("_ws", max(ws_bytes, 16))
         out = torch.empty((len(ids), self.n_q, self.d), dtype=torch.float16, device=self.dev)
-        d_tab = torch.from_numpy(tab).to(self.dev, non_blocking=True)
-        d_len = torch.from_numpy(ln).to(self.dev, non_blocking=True)
-        d_work = torch.from_numpy(np.ascontiguousarray(work)).to(self.dev, non_blocking=True)
+        d_tab = self._h2d(tab)
+        d_len = self._h2d(ln)
+        d_work = self._h2d(work)
         flags = L.PA_DECODE_KEEP_KV if self.cache.shares_blocks() else 0
         self.cache.decode(out, q.contiguous(), d_tab, max_blocks, d_len, len(ids), self.n_q,
                           self.scale, self.partition, max_len, d_work, len(work), ws, ws_bytes,
@@ -131,12 +153,13 @@ class ServingLoop:
 
     def _prefill(self, r: int, s: int, n: int, q: torch.Tensor, stream):
         self.cache.require_fp16("pa_paged_attention_prefill")
-        tab, ln, max_blocks = self.cache.host_tables([r])
+        max_blocks = -(-(s + n) // L.BLOCK_SIZE)
+        tab, ln = L.pa_block_tables(self.cache.pool, [r], max_blocks)
         assert int(ln[0]) == s + n
         ws_bytes = L.pa_prefill_workspace_bytes(n, self.n_q, self.d, s)
         ws = self._workspace("_pws", max(ws_bytes, 16))
         out = torch.empty((n, self.n_q, self.d), dtype=torch.float16, device=self.dev)
-        d_tab = torch.from_numpy(np.ascontiguousarray(tab[0])).to(self.dev, non_blocking=True)
+        d_tab = self._h2d(tab[0])
         L.pa_paged_attention_prefill(out, q.contiguous(), self.cache.kv, d_tab, max_blocks, s, n,
                                      self.n_q, self.scale, ws, ws_bytes, stream)
         if self.keep:

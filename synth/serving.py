@@ -47,6 +47,31 @@ def token_rows(req, pos, tag: int, width: int, xp=np):
     return (vals.to(xp.float32) / 1024.0).to(xp.float16)
 
 
+_KVQ_COLS = {}
+
+
+def token_rows_kvq(req, pos, width_kv: int, width_q: int, xp):
+    """The K, V and query rows of token_rows (tags TAG_K, TAG_V, TAG_Q) from
+    one pass over [len(req), 2 * width_kv + width_q] elements: the same
+    values, a third of the device launches.  xp is torch; returns three
+    float16 views [len(req), width]."""
+    dev = req.device
+    ck = (width_kv, width_q, str(dev))
+    if ck not in _KVQ_COLS:
+        tag = xp.cat([xp.full((width_kv,), TAG_K, dtype=xp.int64),
+                      xp.full((width_kv,), TAG_V, dtype=xp.int64),
+                      xp.full((width_q,), TAG_Q, dtype=xp.int64)]).to(dev)
+        e = xp.cat([xp.arange(width_kv, dtype=xp.int64), xp.arange(width_kv, dtype=xp.int64),
+                    xp.arange(width_q, dtype=xp.int64)]).to(dev)
+        _KVQ_COLS[ck] = (tag[None, :], (e * 0x85EBCA77)[None, :])
+    tag, e_mul = _KVQ_COLS[ck]
+    key = (((req * 131071 + pos) * 4)[:, None] + tag) & _M31
+    h = ((key * 0x9E3779B1) + e_mul) & _M31
+    h = _mix31(_mix31(h))
+    rows = ((h >> 20) - 1024).to(xp.float32).div_(1024.0).to(xp.float16)
+    return rows[:, :width_kv], rows[:, width_kv:2 * width_kv], rows[:, 2 * width_kv:]
+
+
 @dataclass
 class ServingTrace:
     """Requests (id, prompt length, output length) and the step each arrives."""

@@ -4,7 +4,9 @@ The same trace runs with a pool that holds every request and with one a
 third that size, where requests are preempted and recomputed.  Sampled
 outputs of both runs match the fp64 oracle, outputs that both runs computed
 with the decode kernel are bitwise equal (placement and history do not
-matter), and every request produces all of its tokens.
+matter), and every request produces all of its tokens.  The roomy run makes
+its rows one tensor at a time, the tight run with the fused K/V/Q generator
+the serving bench uses.
 """
 import numpy as np
 import pytest
@@ -12,7 +14,7 @@ import torch
 
 from gpu_util import ATOL, RTOL, log
 from oracle import decode_attention_one
-from synth.serving import TAG_K, TAG_Q, TAG_V, make_trace, token_rows
+from synth.serving import TAG_K, TAG_Q, TAG_V, make_trace, token_rows, token_rows_kvq
 
 pytestmark = pytest.mark.gpu
 
@@ -33,13 +35,22 @@ def rows_dev(req, pos, tag, width):
     return token_rows(req, pos, tag, width, xp=torch)
 
 
-def serve(trace, num_blocks, budget, max_running, seed=0):
+def rows_kvq_dev(req, pos, width_kv, width_q):
+    return token_rows_kvq(req, pos, width_kv, width_q, xp=torch)
+
+
+def serve(trace, num_blocks, budget, max_running, seed=0, fused_rows=False):
     from pagedattention_block_paged_reshape_amd.cache import PagedKVCache
     from pagedattention_block_paged_reshape_amd.serve import ServingLoop
     log(f"[serve] blocks={num_blocks} budget={budget} max_running={max_running}")
     order = np.random.default_rng(seed).permutation(num_blocks).astype(np.int32)
     cache = PagedKVCache(num_blocks, N_KV, D, order, "cuda:0")
-    loop = ServingLoop(cache, N_Q, SCALE, budget, max_running, row_fn=rows_dev, keep_outputs=True)
+    if fused_rows:
+        loop = ServingLoop(cache, N_Q, SCALE, budget, max_running, rows_fn=rows_kvq_dev,
+                           keep_outputs=True)
+    else:
+        loop = ServingLoop(cache, N_Q, SCALE, budget, max_running, row_fn=rows_dev,
+                           keep_outputs=True)
     nxt = 0
     for step in range(20000):
         while nxt < len(trace.prompt) and trace.arrival[nxt] <= step:
@@ -73,7 +84,7 @@ def test_serving_with_preemption_matches_oracle_and_unpressured_run():
                     arrive_over=8)
     need = [-(-(p + o) // 16) for p, o in zip(tr.prompt, tr.output)]
     big, sb, rb = serve(tr, sum(need) + 16, budget=512, max_running=32)
-    small, ss, rs = serve(tr, max(need) + 8, budget=512, max_running=32, seed=1)
+    small, ss, rs = serve(tr, max(need) + 8, budget=512, max_running=32, seed=1, fused_rows=True)
     log(f"[serve] stats roomy {sb}; tight {ss}")
     assert sb["preempted"] == 0 and ss["preempted"] >= 5
     for r in range(len(tr.prompt)):
