@@ -3,9 +3,10 @@
 A serving run needs a K, V and query row for every (request, position) it
 computes, and a run that preempts and recomputes a request must get the same
 rows again.  So rows are a pure function of (request, position, tensor,
-element): a counter-based integer hash (multiply / xor-shift steps on
-31-bit values in int64, no overflow), mapped to multiples of 1/1024 in
-[-1, 1), which fp16 holds exactly.  The same code runs on numpy arrays
+element): a counter-based integer hash (a 31-bit key per token and tensor,
+then multiply / xor-shift steps in int32 with wrap-around products and
+arithmetic shifts, which numpy and torch compute alike), mapped to multiples
+of 1/1024 in [-1, 1), which fp16 holds exactly.  The same code runs on numpy arrays
 (host) and torch tensors (device) and gives the same values.
 
 Nothing here is attention or allocation arithmetic.
@@ -19,14 +20,30 @@ import numpy as np
 
 _M31 = 0x7FFFFFFF
 TAG_K, TAG_V, TAG_Q = 0, 1, 2
+# odd multipliers below 2^31 (they fit int32 on both sides)
+_C_KEY, _C_ELEM, _C_MIX1, _C_MIX2 = 0x1E3779B1, 0x05EBCA77, 0x2C1B3C6D, 0x297A2D39
 
 
-def _mix31(h):
+def _token_key(req, pos, tag):
+    """31-bit key of (request, position, tensor) in int64 (no overflow)."""
+    return ((req * 131071 + pos) * 4 + tag) & _M31
+
+
+def _rows_from_keys(key32, e_mul, xp):
+    """key32 [T] int32 keys times _C_KEY, e_mul [W] int32 element index times
+    _C_ELEM (both wrapped to int32): an int32 hash per (key, element) with
+    wrap-around products and arithmetic shifts, which numpy and torch compute
+    alike, mapped to multiples of 1/1024 in [-1, 1) as float16."""
+    h = key32[:, None] + e_mul[None, :]
     h = h ^ (h >> 15)
-    h = (h * 0x2C1B3C6D) & _M31
-    h = h ^ (h >> 12)
-    h = (h * 0x297A2D39) & _M31
-    return h ^ (h >> 15)
+    h = h * _C_MIX1
+    h = h ^ (h >> 13)
+    h = h * _C_MIX2
+    h = h ^ (h >> 16)
+    vals = ((h >> 8) & 2047) - 1024               # integers in [-1024, 1023]
+    if xp is np:
+        return vals.astype(np.float16) / np.float16(1024.0)
+    return vals.to(xp.float16) / 1024.0
 
 
 def token_rows(req, pos, tag: int, width: int, xp=np):
@@ -35,16 +52,19 @@ def token_rows(req, pos, tag: int, width: int, xp=np):
     if xp is np:
         req = np.asarray(req, dtype=np.int64)
         pos = np.asarray(pos, dtype=np.int64)
-        e = np.arange(width, dtype=np.int64)[None, :]
-    else:
-        e = xp.arange(width, dtype=xp.int64, device=req.device)[None, :]
-    key = ((req * 131071 + pos) * 4 + tag) & _M31
-    h = ((key[:, None] * 0x9E3779B1) + e * 0x85EBCA77) & _M31
-    h = _mix31(_mix31(h))
-    vals = (h >> 20) - 1024                      # integers in [-1024, 1023]
-    if xp is np:
-        return (vals.astype(np.float64) / 1024.0).astype(np.float16)
-    return (vals.to(xp.float32) / 1024.0).to(xp.float16)
+        key32 = (_token_key(req, pos, tag) * _C_KEY & 0xFFFFFFFF).astype(np.uint32).view(np.int32)
+        e_mul = (np.arange(width, dtype=np.int64) * _C_ELEM & 0xFFFFFFFF).astype(
+            np.uint32).view(np.int32)
+        return _rows_from_keys(key32, e_mul, np)
+    key32 = _wrap32(_token_key(req, pos, tag) * _C_KEY, xp)
+    e_mul = _wrap32(xp.arange(width, dtype=xp.int64, device=req.device) * _C_ELEM, xp)
+    return _rows_from_keys(key32, e_mul, xp)
+
+
+def _wrap32(x, xp):
+    """int64 tensor -> int32 with the same low 32 bits."""
+    x = x & 0xFFFFFFFF
+    return (x - ((x >> 31) << 32)).to(xp.int32)
 
 
 _KVQ_COLS = {}
@@ -63,12 +83,19 @@ def token_rows_kvq(req, pos, width_kv: int, width_q: int, xp):
                       xp.full((width_q,), TAG_Q, dtype=xp.int64)]).to(dev)
         e = xp.cat([xp.arange(width_kv, dtype=xp.int64), xp.arange(width_kv, dtype=xp.int64),
                     xp.arange(width_q, dtype=xp.int64)]).to(dev)
-        _KVQ_COLS[ck] = (tag[None, :], (e * 0x85EBCA77)[None, :])
+        _KVQ_COLS[ck] = (tag, _wrap32(e * _C_ELEM, xp))
     tag, e_mul = _KVQ_COLS[ck]
-    key = (((req * 131071 + pos) * 4)[:, None] + tag) & _M31
-    h = ((key * 0x9E3779B1) + e_mul) & _M31
-    h = _mix31(_mix31(h))
-    rows = ((h >> 20) - 1024).to(xp.float32).div_(1024.0).to(xp.float16)
+    base = (req * 131071 + pos) * 4
+    # per (token, tag) keys, then each column picks its tag's key
+    keys = _wrap32(((base[:, None] + xp.arange(3, device=dev)[None, :]) & _M31) * _C_KEY, xp)
+    kcol = keys.index_select(1, tag)                 # [T, W] int32
+    h = kcol + e_mul[None, :]
+    h = h ^ (h >> 15)
+    h = h * _C_MIX1
+    h = h ^ (h >> 13)
+    h = h * _C_MIX2
+    h = h ^ (h >> 16)
+    rows = (((h >> 8) & 2047) - 1024).to(xp.float16) / 1024.0
     return rows[:, :width_kv], rows[:, width_kv:2 * width_kv], rows[:, 2 * width_kv:]
 
 
