@@ -133,6 +133,28 @@ pa_status pa_seq_fork(pa_pool* pool, int64_t parent, int64_t child);
  * pa_seq_register), appended to the evictable list instead. */
 pa_status pa_seq_free(pa_pool* pool, int64_t seq_id);
 
+/* Preemption by swapping ([lens] scheduler skeleton: a preempted request is
+ * either moved out to CPU memory or dropped and recomputed later; [tcd]
+ * tuning anti-patterns: swap is the last-resort spill of KV blocks to CPU
+ * memory, much slower than staying on the GPU).
+ * pa_seq_swap_out: writes the sequence's physical blocks in logical order
+ * (ceil(len/16) of them, at most cap) to `blocks` (host) and its length to
+ * *seq_len, then releases it exactly as pa_seq_free does.  The caller must
+ * enqueue pa_gather_blocks over those blocks before any later launch on the
+ * same stream writes into the pool (the blocks may be handed out again at
+ * once).  PA_ERR_UNKNOWN_SEQ, or PA_ERR_CAPACITY (nothing changes).
+ * Blocks shared with other sequences stay with them; the swapped copy is
+ * private. */
+pa_status pa_seq_swap_out(pa_pool* pool, int64_t seq_id, int32_t* blocks, int32_t cap,
+                          int32_t* n_blocks, int32_t* seq_len);
+
+/* pa_seq_swap_in: creates `seq_id` (which must not exist: PA_ERR_EXISTS)
+ * with length seq_len and ceil(seq_len/16) blocks taken from the free list
+ * in logical order (written to `blocks`, host), for pa_scatter_blocks to
+ * fill.  Atomic: PA_ERR_OUT_OF_BLOCKS or PA_ERR_CAPACITY change nothing. */
+pa_status pa_seq_swap_in(pa_pool* pool, int64_t seq_id, int32_t seq_len, int32_t* blocks,
+                         int32_t cap, int32_t* n_blocks);
+
 /* Blocks pa_append_slots would take off the free list for the same arguments
  * (new blocks + copy-on-write targets).  Pure. */
 
@@ -308,6 +330,18 @@ pa_status pa_reshape_and_cache(const pa_half* k, const pa_half* v, const int32_t
  * pa_reshape_and_cache of the same step (same stream). */
 pa_status pa_copy_blocks(const pa_copy* copies, int32_t n, pa_kv_view kv, void* stream);
 
+/* Swap transfers: whole K and V tiles (all kv heads) of n blocks between the
+ * pools and contiguous buffers [n][num_kv_heads][16*D] fp16 in the pools'
+ * tile order (a bit copy; the caller moves the buffers to and from host
+ * memory).  blocks: device int32 [n] (entries outside [0, num_blocks) are
+ * skipped); buffers: device, 16-byte aligned, n * num_kv_heads * 16 * D
+ * values each.  pa_gather_blocks reads the pools, pa_scatter_blocks writes
+ * them.  Async on `stream`. */
+pa_status pa_gather_blocks(const int32_t* blocks, int32_t n, pa_kv_view kv, pa_half* k_out,
+                           pa_half* v_out, void* stream);
+pa_status pa_scatter_blocks(const int32_t* blocks, int32_t n, pa_kv_view kv,
+                            const pa_half* k_in, const pa_half* v_in, void* stream);
+
 /* Work list for the work-list form of pa_paged_attention_decode (host, pure).
  * Request b of length L is cut into ceil(ceil(L/16) / (partition_size/16))
  * partitions; each (request, partition) becomes one entry (b << 16) | p, and a
@@ -408,6 +442,13 @@ pa_status pa_reshape_and_cache_fp8(const pa_half* k, const pa_half* v,
 
 /* pa_copy_blocks for FP8 pools (bit copy of slots [0, n_slots) of K and V). */
 pa_status pa_copy_blocks_fp8(const pa_copy* copies, int32_t n, pa_kv_view_fp8 kv, void* stream);
+
+/* pa_gather_blocks / pa_scatter_blocks for FP8 pools: the same transfers of
+ * 16*D one-byte codes per tile (the pool's scales do not move). */
+pa_status pa_gather_blocks_fp8(const int32_t* blocks, int32_t n, pa_kv_view_fp8 kv,
+                               uint8_t* k_out, uint8_t* v_out, void* stream);
+pa_status pa_scatter_blocks_fp8(const int32_t* blocks, int32_t n, pa_kv_view_fp8 kv,
+                                const uint8_t* k_in, const uint8_t* v_in, void* stream);
 
 /* pa_paged_attention_decode over FP8 pools: the same arguments, work list,
  * workspace (pa_decode_workspace_bytes) and flags; K_j and V_j are the values

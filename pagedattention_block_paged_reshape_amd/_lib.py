@@ -135,6 +135,12 @@ _SIGS = {
     "pa_prefill_workspace_bytes": (_U64, [_I32, _I32, _I32, _I32]),
     "pa_paged_attention_prefill": (C.c_int, [_P, _P, pa_kv_view, _P, _I32, _I32, _I32, _I32,
                                              C.c_float, _P, _U64, _P]),
+    "pa_seq_swap_out": (C.c_int, [_P, _I64, _P, _I32, C.POINTER(_I32), C.POINTER(_I32)]),
+    "pa_seq_swap_in": (C.c_int, [_P, _I64, _I32, _P, _I32, C.POINTER(_I32)]),
+    "pa_gather_blocks": (C.c_int, [_P, _I32, pa_kv_view, _P, _P, _P]),
+    "pa_scatter_blocks": (C.c_int, [_P, _I32, pa_kv_view, _P, _P, _P]),
+    "pa_gather_blocks_fp8": (C.c_int, [_P, _I32, pa_kv_view_fp8, _P, _P, _P]),
+    "pa_scatter_blocks_fp8": (C.c_int, [_P, _I32, pa_kv_view_fp8, _P, _P, _P]),
     "pa_mixed_workspace_bytes": (_U64, [C.POINTER(pa_decode_batch), C.POINTER(pa_prefill_chunk),
                                         _I32, _I32]),
     "pa_paged_attention_mixed": (C.c_int, [C.POINTER(pa_decode_batch),
@@ -516,3 +522,42 @@ def pa_paged_attention_mixed(dec: pa_decode_batch, pf: pa_prefill_chunk, kv: pa_
     _check(LIB.pa_paged_attention_mixed(C.byref(dec), C.byref(pf), kv, int(num_q_heads),
                                         float(scale), _dptr(workspace), int(workspace_bytes),
                                         int(flags), _stream(stream)), "pa_paged_attention_mixed")
+
+
+def pa_seq_swap_out(pool: int, seq_id: int):
+    """Release a sequence for swapping; returns (blocks in logical order, length)."""
+    n = C.c_int32(0)
+    ln = C.c_int32(0)
+    st = LIB.pa_seq_swap_out(pool, int(seq_id), None, 0, C.byref(n), C.byref(ln))
+    if st == PA_ERR_CAPACITY:
+        # ask again with room for every block (the failed call changed nothing)
+        table, _ = pa_seq_table(pool, seq_id)
+        out = np.empty(max(len(table), 1), dtype=np.int32)
+        st = LIB.pa_seq_swap_out(pool, int(seq_id), out.ctypes.data, out.size, C.byref(n),
+                                 C.byref(ln))
+        _check(st, "pa_seq_swap_out")
+        return out[:n.value], ln.value
+    _check(st, "pa_seq_swap_out")
+    return np.empty(0, dtype=np.int32), ln.value
+
+
+def pa_seq_swap_in(pool: int, seq_id: int, seq_len: int) -> np.ndarray:
+    """Re-create a swapped sequence with fresh blocks; returns them in logical order."""
+    n_need = -(-int(seq_len) // BLOCK_SIZE)
+    out = np.empty(max(n_need, 1), dtype=np.int32)
+    n = C.c_int32(0)
+    _check(LIB.pa_seq_swap_in(pool, int(seq_id), int(seq_len), out.ctypes.data, out.size,
+                              C.byref(n)), "pa_seq_swap_in")
+    return out[:n.value]
+
+
+def pa_gather_blocks(blocks, n: int, kv, k_out, v_out, stream=None) -> None:
+    fn = LIB.pa_gather_blocks_fp8 if isinstance(kv, pa_kv_view_fp8) else LIB.pa_gather_blocks
+    _check(fn(_dptr(blocks), int(n), kv, _dptr(k_out), _dptr(v_out), _stream(stream)),
+           "pa_gather_blocks")
+
+
+def pa_scatter_blocks(blocks, n: int, kv, k_in, v_in, stream=None) -> None:
+    fn = LIB.pa_scatter_blocks_fp8 if isinstance(kv, pa_kv_view_fp8) else LIB.pa_scatter_blocks
+    _check(fn(_dptr(blocks), int(n), kv, _dptr(k_in), _dptr(v_in), _stream(stream)),
+           "pa_scatter_blocks")

@@ -106,6 +106,52 @@ class PagedKVCache:
         fn(out, q, self.kv, tables, max_blocks, lens, batch, n_q, scale, partition, max_len,
            items, n_items, workspace, ws_bytes, stream, flags=flags)
 
+    # -- preemption by swapping ----------------------------------------------
+    def swap_out(self, seq_id: int, stream=None) -> dict:
+        """Move a sequence's K/V to pinned host memory and release it:
+        pa_seq_swap_out, then pa_gather_blocks into a device staging buffer
+        (enqueued before anything can reuse the blocks) and one copy to the
+        host.  Returns what swap_in needs; the host copy is complete once the
+        stream reaches the returned event."""
+        stream = stream or torch.cuda.current_stream(self.device)
+        blocks, length = L.pa_seq_swap_out(self.pool, seq_id)
+        n = len(blocks)
+        tile = (n, self.n_kv, L.BLOCK_SIZE * self.d)
+        dt = self.k_pool.dtype
+        saved = {"len": length, "n": n,
+                 "k": torch.empty(tile, dtype=dt, pin_memory=True),
+                 "v": torch.empty(tile, dtype=dt, pin_memory=True)}
+        if n:
+            with torch.cuda.stream(stream):
+                d_blocks = torch.from_numpy(blocks).pin_memory().to(self.device,
+                                                                    non_blocking=True)
+                k_buf = torch.empty(tile, dtype=dt, device=self.device)
+                v_buf = torch.empty(tile, dtype=dt, device=self.device)
+                L.pa_gather_blocks(d_blocks, n, self.kv, k_buf, v_buf, stream)
+                saved["k"].copy_(k_buf, non_blocking=True)
+                saved["v"].copy_(v_buf, non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        saved["event"] = ev
+        return saved
+
+    def swap_in(self, seq_id: int, saved: dict, stream=None) -> np.ndarray:
+        """Re-create a swapped-out sequence in fresh blocks (pa_seq_swap_in)
+        and copy its K/V back (pa_scatter_blocks).  Raises OutOfBlocksError,
+        changing nothing, when the pool cannot hold it.  Returns its new
+        blocks."""
+        stream = stream or torch.cuda.current_stream(self.device)
+        blocks = L.pa_seq_swap_in(self.pool, seq_id, saved["len"])
+        n = len(blocks)
+        if n:
+            with torch.cuda.stream(stream):
+                d_blocks = torch.from_numpy(blocks).pin_memory().to(self.device,
+                                                                    non_blocking=True)
+                k_buf = saved["k"].to(self.device, non_blocking=True)
+                v_buf = saved["v"].to(self.device, non_blocking=True)
+                L.pa_scatter_blocks(d_blocks, n, self.kv, k_buf, v_buf, stream)
+        return blocks
+
     def require_fp16(self, what: str) -> None:
         if self.fp8:
             raise NotImplementedError(f"{what} reads fp16 pools only")

@@ -273,6 +273,44 @@ pa_status pa_seq_free(pa_pool* pool, int64_t seq_id) {
   return PA_OK;
 }
 
+pa_status pa_seq_swap_out(pa_pool* pool, int64_t seq_id, int32_t* blocks, int32_t cap,
+                          int32_t* n_blocks, int32_t* seq_len) {
+  if (pool == nullptr || n_blocks == nullptr || seq_len == nullptr) return PA_ERR_INVALID;
+  auto it = pool->seqs.find(seq_id);
+  if (it == pool->seqs.end()) return PA_ERR_UNKNOWN_SEQ;
+  const Seq& s = it->second;
+  const int32_t n = static_cast<int32_t>(s.table.size());
+  if (n > cap) return PA_ERR_CAPACITY;
+  if (n > 0 && blocks == nullptr) return PA_ERR_INVALID;
+  for (int32_t i = 0; i < n; ++i) blocks[i] = s.table[i];
+  *n_blocks = n;
+  *seq_len = s.len;
+  for (int32_t b : s.table) pool->release(b);
+  pool->seqs.erase(it);
+  return PA_OK;
+}
+
+pa_status pa_seq_swap_in(pa_pool* pool, int64_t seq_id, int32_t seq_len, int32_t* blocks,
+                         int32_t cap, int32_t* n_blocks) {
+  if (pool == nullptr || n_blocks == nullptr || seq_len < 0) return PA_ERR_INVALID;
+  if (pool->seqs.count(seq_id)) return PA_ERR_EXISTS;
+  const int32_t n = ceil_div(seq_len, kBS);
+  if (n > cap) return PA_ERR_CAPACITY;
+  if (n > 0 && blocks == nullptr) return PA_ERR_INVALID;
+  if (n > pool->available()) return PA_ERR_OUT_OF_BLOCKS;
+  Seq s;
+  s.len = seq_len;
+  s.table.reserve(n);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t b = pool->pop();
+    s.table.push_back(b);
+    blocks[i] = b;
+  }
+  pool->seqs.emplace(seq_id, std::move(s));
+  *n_blocks = n;
+  return PA_OK;
+}
+
 pa_status pa_can_append(const pa_pool* pool, int32_t n, const int64_t* seq_ids,
                         const int32_t* n_new, int32_t* blocks_needed) {
   if (pool == nullptr || blocks_needed == nullptr) return PA_ERR_INVALID;

@@ -164,6 +164,60 @@ static bool valid_view(const pa_kv_view_fp8& kv) {
          aligned16(kv.v_pool) && valid_scale(kv.k_scale) && valid_scale(kv.v_scale);
 }
 
+
+// Whole tiles between the pools and a contiguous buffer [n][n_kv][tile] in
+// the pools' own tile order, for moving a preempted sequence's blocks out
+// of the pool and back (GATHER: pool -> buffer, else buffer -> pool).  One
+// workgroup per (entry, kv head), 16-byte chunks; entries outside
+// [0, num_blocks) are skipped.
+template <bool GATHER>
+__global__ __launch_bounds__(256) void block_transfer_kernel(
+    const int32_t* __restrict__ blocks, int32_t n_kv, int32_t num_blocks, int32_t tile_chunks,
+    u32x4* __restrict__ kp, u32x4* __restrict__ vp, u32x4* __restrict__ kb,
+    u32x4* __restrict__ vb) {
+  const int32_t b = blocks[blockIdx.x];
+  if (b < 0 || b >= num_blocks) return;
+  const int h = blockIdx.y;
+  const int64_t po = (static_cast<int64_t>(b) * n_kv + h) * tile_chunks;
+  const int64_t bo = (static_cast<int64_t>(blockIdx.x) * n_kv + h) * tile_chunks;
+  for (int c = threadIdx.x; c < tile_chunks; c += blockDim.x) {
+    if (GATHER) {
+      kb[bo + c] = kp[po + c];
+      vb[bo + c] = vp[po + c];
+    } else {
+      kp[po + c] = kb[bo + c];
+      vp[po + c] = vb[bo + c];
+    }
+  }
+}
+
+static pa_status block_transfer(bool gather, const int32_t* blocks, int32_t n, void* k_pool,
+                                void* v_pool, int32_t num_blocks, int32_t block_size,
+                                int32_t n_kv, int32_t head_dim, int32_t elem_bytes, void* k_buf,
+                                void* v_buf, void* stream) {
+  if (k_pool == nullptr || v_pool == nullptr || block_size != kBlock || num_blocks <= 0 ||
+      n_kv <= 0 || n_kv > 65535 || (head_dim != 64 && head_dim != 128) || n < 0)
+    return PA_ERR_INVALID;
+  if (n == 0) return PA_OK;
+  if (blocks == nullptr || k_buf == nullptr || v_buf == nullptr || !aligned16(k_buf) ||
+      !aligned16(v_buf) || !aligned16(k_pool) || !aligned16(v_pool))
+    return PA_ERR_INVALID;
+  const int32_t chunks = head_dim * elem_bytes;  // 16 * D * elem_bytes / 16
+  const dim3 grid(static_cast<uint32_t>(n), static_cast<uint32_t>(n_kv));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  u32x4* kp = static_cast<u32x4*>(k_pool);
+  u32x4* vp = static_cast<u32x4*>(v_pool);
+  u32x4* kb = static_cast<u32x4*>(k_buf);
+  u32x4* vb = static_cast<u32x4*>(v_buf);
+  if (gather)
+    block_transfer_kernel<true><<<grid, dim3(256), 0, s>>>(blocks, n_kv, num_blocks, chunks, kp,
+                                                           vp, kb, vb);
+  else
+    block_transfer_kernel<false><<<grid, dim3(256), 0, s>>>(blocks, n_kv, num_blocks, chunks, kp,
+                                                            vp, kb, vb);
+  return launch_status();
+}
+
 }  // namespace pa
 
 using namespace pa;
@@ -250,4 +304,31 @@ extern "C" pa_status pa_copy_blocks_fp8(const pa_copy* copies, int32_t n, pa_kv_
     copy_blocks_fp8_kernel<64><<<grid, dim3(256), 0, s>>>(copies, kv.num_kv_heads,
                                                           kv.num_blocks, kv.k_pool, kv.v_pool);
   return launch_status();
+}
+
+extern "C" pa_status pa_gather_blocks(const int32_t* blocks, int32_t n, pa_kv_view kv,
+                                      pa_half* k_out, pa_half* v_out, void* stream) {
+  return block_transfer(true, blocks, n, kv.k_pool, kv.v_pool, kv.num_blocks, kv.block_size,
+                        kv.num_kv_heads, kv.head_dim, 2, k_out, v_out, stream);
+}
+
+extern "C" pa_status pa_scatter_blocks(const int32_t* blocks, int32_t n, pa_kv_view kv,
+                                       const pa_half* k_in, const pa_half* v_in, void* stream) {
+  return block_transfer(false, blocks, n, kv.k_pool, kv.v_pool, kv.num_blocks, kv.block_size,
+                        kv.num_kv_heads, kv.head_dim, 2, const_cast<pa_half*>(k_in),
+                        const_cast<pa_half*>(v_in), stream);
+}
+
+extern "C" pa_status pa_gather_blocks_fp8(const int32_t* blocks, int32_t n, pa_kv_view_fp8 kv,
+                                          uint8_t* k_out, uint8_t* v_out, void* stream) {
+  return block_transfer(true, blocks, n, kv.k_pool, kv.v_pool, kv.num_blocks, kv.block_size,
+                        kv.num_kv_heads, kv.head_dim, 1, k_out, v_out, stream);
+}
+
+extern "C" pa_status pa_scatter_blocks_fp8(const int32_t* blocks, int32_t n, pa_kv_view_fp8 kv,
+                                           const uint8_t* k_in, const uint8_t* v_in,
+                                           void* stream) {
+  return block_transfer(false, blocks, n, kv.k_pool, kv.v_pool, kv.num_blocks, kv.block_size,
+                        kv.num_kv_heads, kv.head_dim, 1, const_cast<uint8_t*>(k_in),
+                        const_cast<uint8_t*>(v_in), stream);
 }

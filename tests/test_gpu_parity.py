@@ -290,6 +290,52 @@ def test_prefill_bad_table_entry_reads_nan_and_empty_chunk_is_a_noop(q_start, ch
                                           n_q, pp.scale, pp.workspace, pp.ws_bytes)
 
 
+@pytest.mark.parametrize("kv_dtype", ["fp16", "fp8"])
+def test_swap_out_and_in_restores_kv_bitwise(kv_dtype):
+    """A request swapped out to host memory, its blocks overwritten by another
+    request, then swapped back in (into whatever blocks the free list gives):
+    its K/V tiles come back bit for bit and the whole batch's decode output is
+    bitwise unchanged."""
+    import pagedattention_block_paged_reshape_amd as pa
+    from pagedattention_block_paged_reshape_amd.cache import DecodePlan
+    w = make_tiny_workload([33, 100, 517, 1200], n_q=8, n_kv=2, d=128, seed=9, dist="normal",
+                           num_blocks=160)
+    scales = dict(k_scale=0.02, v_scale=0.03) if kv_dtype == "fp8" else {}
+    res = gpu_run(w, kv_dtype=kv_dtype, **scales)
+    cache, out0 = res["cache"], res["decode"]
+    victim = int(w.decode_ids[2])
+    old_table, old_len = pa.pa_seq_table(cache.pool, victim)
+    idx = torch.from_numpy(old_table.astype(np.int64)).to(cache.device)
+    k_before = cache.k_pool[idx].clone()
+    v_before = cache.v_pool[idx].clone()
+    saved = cache.swap_out(victim)
+    saved["event"].synchronize()
+    assert saved["n"] == len(old_table) and saved["len"] == old_len
+    # another request takes every free block (the victim's first) and writes them
+    filler = 10 ** 6
+    cache.add(filler)
+    n_fill = pa.pa_num_free_blocks(cache.pool) * 16
+    g = torch.Generator(device=cache.device).manual_seed(5)
+    rows = lambda: torch.randn((n_fill, w.n_kv, w.d), generator=g, device=cache.device).half()
+    cache.append([filler], [n_fill], rows(), rows())
+    torch.cuda.synchronize()
+    assert not torch.equal(cache.k_pool[idx].view(torch.uint8), k_before.view(torch.uint8))
+    cache.free(filler)
+    new_table = cache.swap_in(victim, saved)
+    torch.cuda.synchronize()
+    pa.pa_pool_check(cache.pool)
+    assert pa.pa_seq_table(cache.pool, victim)[1] == old_len
+    nidx = torch.from_numpy(np.asarray(new_table, dtype=np.int64)).to(cache.device)
+    assert torch.equal(cache.k_pool[nidx].view(torch.uint8), k_before.view(torch.uint8))
+    assert torch.equal(cache.v_pool[nidx].view(torch.uint8), v_before.view(torch.uint8))
+    plan = DecodePlan(cache, w.decode_ids, w.n_q, w.scale, 512)
+    out1 = plan.run(res["q"]).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.int16), out0.view(torch.int16))
+    log(f"swap {kv_dtype}: {saved['n']} blocks out and back, old {old_table.tolist()[:4]}..., "
+        f"new {list(new_table)[:4]}...")
+
+
 def test_decode_empty_batch_is_a_noop():
     import pagedattention_block_paged_reshape_amd as pa
     w = make_tiny_workload([20], n_q=8, n_kv=2, d=128, seed=5, dist="normal")

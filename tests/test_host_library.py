@@ -123,6 +123,81 @@ def test_random_programs_match_oracle_exactly(seed):
         tw.close()
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_swap_out_and_in_match_free_and_reallocation_in_the_oracle(seed):
+    """Swapping a sequence out releases its blocks exactly as freeing it does
+    (same free list, same reference counts, shared blocks kept by their other
+    holders); swapping it back in takes ceil(len/16) fresh blocks in logical
+    order, as a new sequence appending len tokens does in the oracle's model,
+    and fails with no state change when the pool is short."""
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(6, 40))
+    tw = Twin(n, rng.permutation(n))
+    live, swapped, nid = [], {}, 0
+    try:
+        for _ in range(200):
+            op = int(rng.integers(0, 8))
+            if op == 0 or not live:
+                pa.pa_seq_add(tw.lib, nid)
+                tw.ref.add(nid)
+                live.append(nid)
+                nid += 1
+            elif op == 1:
+                p = int(rng.choice(live))
+                pa.pa_seq_fork(tw.lib, p, nid)
+                tw.ref.fork(p, nid)
+                live.append(nid)
+                nid += 1
+            elif op in (2, 3) and len(live) > 1:
+                s = int(rng.choice(live))
+                exp_blocks, exp_len = list(tw.ref.tables[s]), tw.ref.lens[s]
+                blocks, ln = pa.pa_seq_swap_out(tw.lib, s)
+                assert blocks.tolist() == exp_blocks and ln == exp_len
+                tw.ref.free_seq(s)
+                live.remove(s)
+                swapped[s] = ln
+            elif op == 4 and swapped:
+                s = int(rng.choice(list(swapped)))
+                ln = swapped[s]
+                need = -(-ln // 16)
+                if need > len(tw.ref.free):
+                    before = pa.pa_free_list(tw.lib).tolist()
+                    with pytest.raises(pa.OutOfBlocksError):
+                        pa.pa_seq_swap_in(tw.lib, s, ln)
+                    assert pa.pa_free_list(tw.lib).tolist() == before
+                else:
+                    blocks = pa.pa_seq_swap_in(tw.lib, s, ln)
+                    tw.ref.add(s)
+                    if ln:
+                        tw.ref.append([s], [ln])
+                    assert blocks.tolist() == tw.ref.tables[s]
+                    del swapped[s]
+                    live.append(s)
+            else:
+                k = int(rng.integers(1, min(4, len(live)) + 1))
+                ids = [int(x) for x in rng.choice(live, size=k, replace=False)]
+                nn = [int(x) for x in rng.integers(0, 35, size=k)]
+                try:
+                    exp = tw.ref.append(ids, nn)
+                except OutOfBlocks:
+                    with pytest.raises(pa.OutOfBlocksError):
+                        pa.pa_append_slots(tw.lib, ids, nn)
+                else:
+                    slots, copies = pa.pa_append_slots(tw.lib, ids, nn)
+                    assert slots.tolist() == exp[0]
+            tw.compare()
+            pa.pa_pool_check(tw.lib)
+        with pytest.raises(pa.PaError):             # swapped-out ids are unknown
+            for s in swapped:
+                pa.pa_seq_swap_out(tw.lib, s)
+            raise pa.PaError(1, "no swapped sequence left to probe")
+        if live:
+            with pytest.raises(pa.PaError):         # a live id cannot be swapped in
+                pa.pa_seq_swap_in(tw.lib, live[0], 16)
+    finally:
+        tw.close()
+
+
 def test_errors_leave_state_unchanged():
     tw = Twin(3)
     try:
