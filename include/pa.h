@@ -281,6 +281,8 @@ typedef struct pa_sched_stats {
   int64_t steps;
   int64_t preemptions;
   int64_t finished;
+  int32_t n_swapped;  /* swapped-out requests waiting to resume */
+  int32_t reserved;
 } pa_sched_stats;
 
 pa_status pa_sched_create(pa_pool* pool, int32_t token_budget, int32_t max_running,
@@ -295,6 +297,39 @@ pa_status pa_sched_schedule(pa_sched* sched, pa_sched_item* items, int32_t item_
 pa_status pa_sched_commit(pa_sched* sched, int64_t* finished, int32_t cap,
                           int32_t* n_finished);
 pa_status pa_sched_get_stats(const pa_sched* sched, pa_sched_stats* stats);
+/* Swap mode ([lens] scheduler skeleton: a preempted request is moved to CPU
+ * memory instead of being dropped; [tcd]: swap as the last-resort spill).
+ * pa_sched_set_swap(1) before a step: from then on a preempted request that
+ * has computed tokens is released with pa_seq_swap_out, keeps its computed
+ * count and goes to the head of a swapped queue (one with nothing computed
+ * is preempted as in recompute mode).  Each pa_sched_schedule first resumes
+ * swapped requests from the head of that queue, before any other work,
+ * while fewer than max_running run and the free blocks cover the request's
+ * ceil(computed/16) blocks plus one block per running request; a resumed
+ * request gets fresh blocks (pa_seq_swap_in) and runs like the others.  A
+ * request resumed and preempted again in the same step goes back to the
+ * head of the swapped queue with no data movement.  Switching swap mode off
+ * while requests are swapped out is PA_ERR_INVALID.
+ * pa_sched_swaps (between schedule and commit) lists the step's transfers
+ * in the order the caller must run them, before any of the step's own
+ * pool writes: swap-outs (gather those blocks' K/V, then keep them on the
+ * host), then swap-ins (scatter the saved K/V into the new blocks).  blocks
+ * receives every operation's blocks in logical order; op.first is the
+ * offset of its first one.  PA_ERR_CAPACITY (with the counts set) when cap
+ * or blocks_cap is short. */
+typedef struct pa_sched_swap {
+  int64_t req_id;
+  int32_t kind;      /* 0: swap out, 1: swap in                    */
+  int32_t seq_len;   /* tokens held (the request's computed count) */
+  int64_t first;     /* offset of its first block in `blocks`      */
+  int32_t n_blocks;
+  int32_t reserved;
+} pa_sched_swap;
+
+pa_status pa_sched_set_swap(pa_sched* sched, int32_t enable);
+pa_status pa_sched_swaps(const pa_sched* sched, pa_sched_swap* ops, int32_t cap, int32_t* n_ops,
+                         int32_t* blocks, int64_t blocks_cap, int64_t* n_blocks);
+
 /* One request's progress: input tokens computed, outputs so far, preemptions. */
 pa_status pa_sched_request(const pa_sched* sched, int64_t req_id, int32_t* computed,
                            int32_t* generated, int32_t* preemptions);

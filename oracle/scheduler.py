@@ -34,6 +34,19 @@ Readings (the pages leave these open):
     requests admitted in this very step count as running for this.
   * A preempted request recomputes prompt + generated tokens from position 0
     (recompute mode).
+  * Swap mode (the skeleton's other choice: move the preempted request to CPU
+    memory instead of dropping it): the victim keeps its computed count, its
+    blocks' K/V are copied out and its blocks released (exactly as a free),
+    and it goes to the head of a swapped queue.  At the start of each step,
+    before anything else, swapped requests resume from the head of that
+    queue while fewer than ``max_running`` run and the free blocks cover the
+    request's ceil(computed/16) blocks plus one block per running request
+    (headroom for their next tokens); a resumed request takes fresh blocks
+    in logical order (as a new request appending ``computed`` tokens) and
+    runs like any other.  A victim with nothing computed is preempted as in
+    recompute mode; a victim resumed in the same step goes back to the head
+    of the swapped queue with its fresh blocks released and no data moved
+    (its saved copy is still the current one).
 """
 from __future__ import annotations
 
@@ -65,10 +78,15 @@ class StepPlan:
     copies: List[Tuple[int, int, int]] = field(default_factory=list)
     preempted: List[int] = field(default_factory=list)
     admitted: List[int] = field(default_factory=list)
+    # swap mode: (rid, blocks in logical order, computed length) moved out /
+    # back in this step, in the order they happen
+    swap_out: List[Tuple[int, List[int], int]] = field(default_factory=list)
+    swap_in: List[Tuple[int, List[int], int]] = field(default_factory=list)
 
 
 class SchedulerModel:
-    def __init__(self, pool: BlockPoolModel, token_budget: int, max_running: int):
+    def __init__(self, pool: BlockPoolModel, token_budget: int, max_running: int,
+                 swap: bool = False):
         if token_budget < 1 or max_running < 1:
             raise ValueError("budget and max_running must be positive")
         self.pool = pool
@@ -79,6 +97,8 @@ class SchedulerModel:
         self.running: List[int] = []
         self.finished: List[int] = []
         self.last: StepPlan = StepPlan()
+        self.swap = bool(swap)
+        self.swapped: Deque[int] = deque()
 
     def add_request(self, rid: int, prompt: int, out: int) -> None:
         """A request that could not fit the pool even alone (its prompt and
@@ -99,6 +119,15 @@ class SchedulerModel:
         plan = StepPlan()
         budget = self.budget
         chunks: List[Tuple[int, int]] = []      # (rid, n) in reservation order
+        while self.swapped and len(self.running) < self.max_running:
+            r = self.reqs[self.swapped[0]]
+            if self._blocks_for_new(r.computed) + len(self.running) > self.pool.num_free():
+                break
+            self.swapped.popleft()
+            self.pool.add(r.rid)
+            self.pool.append([r.rid], [r.computed])
+            self.running.append(r.rid)
+            plan.swap_in.append((r.rid, list(self.pool.tables[r.rid]), r.computed))
         for rid in self.running:                 # decode first
             r = self.reqs[rid]
             if r.total - r.computed == 1 and r.computed >= r.prompt and budget > 0:
@@ -134,10 +163,21 @@ class SchedulerModel:
             except OutOfBlocks:
                 victim = self.running.pop()
                 v = self.reqs[victim]
-                self.pool.free_seq(victim)
-                v.computed = 0
+                resumed = [i for i, x in enumerate(plan.swap_in) if x[0] == victim]
+                if self.swap and resumed:
+                    # back to where it was: its saved copy is still current
+                    self.pool.free_seq(victim)
+                    del plan.swap_in[resumed[0]]
+                    self.swapped.appendleft(victim)
+                elif self.swap and v.computed > 0:
+                    plan.swap_out.append((victim, list(self.pool.tables[victim]), v.computed))
+                    self.pool.free_seq(victim)
+                    self.swapped.appendleft(victim)
+                else:
+                    self.pool.free_seq(victim)
+                    v.computed = 0
+                    self.waiting.appendleft(victim)
                 v.preemptions += 1
-                self.waiting.appendleft(victim)
                 plan.preempted.append(victim)
                 chunks = [c for c in chunks if c[0] != victim]
                 if victim in plan.admitted:

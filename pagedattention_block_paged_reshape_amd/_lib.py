@@ -55,7 +55,13 @@ class pa_sched_item(C.Structure):
 
 class pa_sched_stats(C.Structure):
     _fields_ = [("n_waiting", C.c_int32), ("n_running", C.c_int32), ("steps", C.c_int64),
-                ("preemptions", C.c_int64), ("finished", C.c_int64)]
+                ("preemptions", C.c_int64), ("finished", C.c_int64), ("n_swapped", C.c_int32),
+                ("reserved", C.c_int32)]
+
+
+class pa_sched_swap(C.Structure):
+    _fields_ = [("req_id", C.c_int64), ("kind", C.c_int32), ("seq_len", C.c_int32),
+                ("first", C.c_int64), ("n_blocks", C.c_int32), ("reserved", C.c_int32)]
 
 
 class pa_pool_stats(C.Structure):
@@ -115,6 +121,8 @@ _SIGS = {
     "pa_sched_add_request": (C.c_int, [_P, _I64, _I32, _I32]),
     "pa_sched_schedule": (C.c_int, [_P, _P, _I32, C.POINTER(_I32), _P, C.c_int64, _P, _I32,
                                     C.POINTER(_I32), _P, _I32, C.POINTER(_I32)]),
+    "pa_sched_set_swap": (C.c_int, [_P, _I32]),
+    "pa_sched_swaps": (C.c_int, [_P, _P, _I32, C.POINTER(_I32), _P, _I64, C.POINTER(_I64)]),
     "pa_sched_commit": (C.c_int, [_P, _P, _I32, C.POINTER(_I32)]),
     "pa_sched_get_stats": (C.c_int, [_P, C.POINTER(pa_sched_stats)]),
     "pa_sched_request": (C.c_int, [_P, _I64, C.POINTER(_I32), C.POINTER(_I32), C.POINTER(_I32)]),
@@ -357,6 +365,27 @@ def pa_sched_schedule(sched: int, token_budget: int, max_running: int) -> dict:
     n_slots = sum(it[2] for it in its)
     return {"items": its, "slots": slots[:n_slots].copy(), "copies": copies[:nc.value].copy(),
             "preempted": pre[:npre.value].tolist()}
+
+
+def pa_sched_set_swap(sched: int, enable: bool) -> None:
+    _check(LIB.pa_sched_set_swap(sched, 1 if enable else 0), "pa_sched_set_swap")
+
+
+def pa_sched_swaps(sched: int) -> list:
+    """The planned step's transfers, in the order to run them: a list of
+    (request, "out" | "in", tokens held, blocks in logical order)."""
+    n, nb = _I32(), _I64()
+    st = LIB.pa_sched_swaps(sched, None, 0, C.byref(n), None, 0, C.byref(nb))
+    if st == PA_OK:
+        return []
+    if st != PA_ERR_CAPACITY:
+        _check(st, "pa_sched_swaps")
+    ops = (pa_sched_swap * n.value)()
+    blocks = np.empty(max(nb.value, 1), dtype=np.int32)
+    _check(LIB.pa_sched_swaps(sched, ops, n.value, C.byref(n), blocks.ctypes.data, nb.value,
+                              C.byref(nb)), "pa_sched_swaps")
+    return [(ops[i].req_id, "out" if ops[i].kind == 0 else "in", ops[i].seq_len,
+             blocks[ops[i].first:ops[i].first + ops[i].n_blocks].copy()) for i in range(n.value)]
 
 
 def pa_sched_commit(sched: int, cap: int) -> list:

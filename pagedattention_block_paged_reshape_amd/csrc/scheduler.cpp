@@ -13,7 +13,10 @@
 //   - ta-paperlens "LLM serving from scratch", scheduler skeleton: admit from
 //     the waiting queue while the head can be allocated, step all running
 //     requests, remove finished ones and free their blocks, and while out of
-//     blocks preempt running[-1].
+//     blocks preempt running[-1] -- moved to CPU memory or dropped for
+//     recomputation.  Swap mode takes the first: a preempted request keeps
+//     its progress, its blocks are moved out (the caller copies them to host
+//     memory) and it resumes, ahead of new admissions, in fresh blocks.
 #include <algorithm>
 #include <cstdint>
 #include <deque>
@@ -40,6 +43,13 @@ struct Req {
 
 inline int32_t blocks_for(int64_t tokens) { return static_cast<int32_t>((tokens + kBS - 1) / kBS); }
 
+struct SwapOp {
+  int64_t req;
+  int32_t kind;  // 0: out, 1: in
+  int32_t len;
+  std::vector<int32_t> blocks;
+};
+
 }  // namespace
 
 struct pa_sched {
@@ -52,6 +62,9 @@ struct pa_sched {
   // the planned step, consumed by pa_sched_commit
   std::vector<pa_sched_item> planned;
   bool has_plan = false;
+  bool swap = false;
+  std::deque<int64_t> swapped;   // swapped-out requests, next to resume first
+  std::vector<SwapOp> swap_ops;  // the planned step's: outs, then ins
   int64_t steps = 0, preemptions = 0, finished = 0;
 };
 
@@ -102,6 +115,23 @@ pa_status pa_sched_schedule(pa_sched* s, pa_sched_item* items, int32_t item_cap,
       preempt_cap < s->max_running || items == nullptr || slot_mapping == nullptr ||
       copies == nullptr || preempted == nullptr)
     return PA_ERR_CAPACITY;
+
+  // swap mode: resume swapped requests first, while the pool holds their
+  // blocks plus one block per running request
+  std::vector<SwapOp> ins, outs;
+  while (!s->swapped.empty() && static_cast<int32_t>(s->running.size()) < s->max_running) {
+    const int64_t id = s->swapped.front();
+    const Req& r = s->reqs[id];
+    const int32_t nb = blocks_for(r.computed);
+    if (nb + static_cast<int32_t>(s->running.size()) > pa_num_free_blocks(s->pool)) break;
+    SwapOp op{id, 1, r.computed, std::vector<int32_t>(static_cast<size_t>(nb))};
+    int32_t got = 0;
+    const pa_status st = pa_seq_swap_in(s->pool, id, r.computed, op.blocks.data(), nb, &got);
+    if (st != PA_OK) return st;
+    s->swapped.pop_front();
+    s->running.push_back(id);
+    ins.push_back(std::move(op));
+  }
 
   int32_t budget = s->budget;
   std::vector<int64_t> ids;
@@ -157,12 +187,32 @@ pa_status pa_sched_schedule(pa_sched* s, pa_sched_item* items, int32_t item_cap,
     const int64_t victim = s->running.back();  // the request added last
     s->running.pop_back();
     Req& v = s->reqs[victim];
-    const pa_status fs = pa_seq_free(s->pool, victim);
-    if (fs != PA_OK) return fs;
-    v.computed = 0;
+    auto resumed = std::find_if(ins.begin(), ins.end(),
+                                [victim](const SwapOp& o) { return o.req == victim; });
+    if (s->swap && resumed != ins.end()) {
+      // resumed in this very step: back to the swapped queue, its saved copy
+      // is still the current one and nothing moves
+      const pa_status fs = pa_seq_free(s->pool, victim);
+      if (fs != PA_OK) return fs;
+      ins.erase(resumed);
+      s->swapped.push_front(victim);
+    } else if (s->swap && v.computed > 0) {
+      SwapOp op{victim, 0, 0, std::vector<int32_t>(static_cast<size_t>(blocks_for(v.computed)))};
+      int32_t nb = 0;
+      const pa_status fs = pa_seq_swap_out(s->pool, victim, op.blocks.data(),
+                                           static_cast<int32_t>(op.blocks.size()), &nb, &op.len);
+      if (fs != PA_OK) return fs;
+      op.blocks.resize(static_cast<size_t>(nb));
+      outs.push_back(std::move(op));
+      s->swapped.push_front(victim);
+    } else {
+      const pa_status fs = pa_seq_free(s->pool, victim);
+      if (fs != PA_OK) return fs;
+      v.computed = 0;
+      s->waiting.push_front(victim);
+    }
     ++v.preemptions;
     ++s->preemptions;
-    s->waiting.push_front(victim);
     preempted[n_pre++] = victim;
     for (size_t i = 0; i < ids.size(); ++i) {
       if (ids[i] == victim) {
@@ -184,6 +234,8 @@ pa_status pa_sched_schedule(pa_sched* s, pa_sched_item* items, int32_t item_cap,
     items[i] = it;
     s->planned.push_back(it);
   }
+  s->swap_ops = std::move(outs);
+  for (SwapOp& op : ins) s->swap_ops.push_back(std::move(op));
   *n_items = static_cast<int32_t>(ids.size());
   *n_copies = ncopy;
   *n_preempted = n_pre;
@@ -215,14 +267,45 @@ pa_status pa_sched_commit(pa_sched* s, int64_t* finished, int32_t cap, int32_t* 
     ++s->finished;
   }
   s->planned.clear();
+  s->swap_ops.clear();
   s->has_plan = false;
   *n_finished = nf;
+  return PA_OK;
+}
+
+pa_status pa_sched_set_swap(pa_sched* s, int32_t enable) {
+  if (s == nullptr || s->has_plan) return PA_ERR_INVALID;
+  if (!enable && !s->swapped.empty()) return PA_ERR_INVALID;  // they could never resume
+  s->swap = enable != 0;
+  return PA_OK;
+}
+
+pa_status pa_sched_swaps(const pa_sched* s, pa_sched_swap* ops, int32_t cap, int32_t* n_ops,
+                         int32_t* blocks, int64_t blocks_cap, int64_t* n_blocks) {
+  if (s == nullptr || n_ops == nullptr || n_blocks == nullptr || !s->has_plan)
+    return PA_ERR_INVALID;
+  int64_t total = 0;
+  for (const SwapOp& op : s->swap_ops) total += static_cast<int64_t>(op.blocks.size());
+  const int32_t n = static_cast<int32_t>(s->swap_ops.size());
+  *n_ops = n;
+  *n_blocks = total;
+  if (n > cap || total > blocks_cap) return PA_ERR_CAPACITY;
+  if ((n > 0 && ops == nullptr) || (total > 0 && blocks == nullptr)) return PA_ERR_INVALID;
+  int64_t off = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const SwapOp& op = s->swap_ops[static_cast<size_t>(i)];
+    ops[i] = pa_sched_swap{op.req, op.kind, op.len, off,
+                           static_cast<int32_t>(op.blocks.size()), 0};
+    for (int32_t b : op.blocks) blocks[off++] = b;
+  }
   return PA_OK;
 }
 
 pa_status pa_sched_get_stats(const pa_sched* s, pa_sched_stats* st) {
   if (s == nullptr || st == nullptr) return PA_ERR_INVALID;
   st->n_waiting = static_cast<int32_t>(s->waiting.size());
+  st->n_swapped = static_cast<int32_t>(s->swapped.size());
+  st->reserved = 0;
   st->n_running = static_cast<int32_t>(s->running.size());
   st->steps = s->steps;
   st->preemptions = s->preemptions;

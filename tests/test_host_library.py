@@ -594,6 +594,72 @@ def test_scheduler_matches_oracle_exactly(seed):
         pa.pa_pool_destroy(pool)
 
 
+def _swap_scheduler_trace(seed):
+    """Swap mode on random arrivals and a small pool: every step's chunks,
+    slots, preemptions, swap-outs and swap-ins (request, tokens held, blocks)
+    and finished requests equal the model's."""
+    from oracle.scheduler import SchedulerModel
+    rng = np.random.default_rng(300 + seed)
+    n = int(rng.integers(16, 80))
+    order = rng.permutation(n)
+    budget = int(rng.integers(4, 300))
+    max_running = int(rng.integers(1, 16))
+    pool = pa.pa_pool_create(n, order)
+    sched = pa.pa_sched_create(pool, budget, max_running)
+    pa.pa_sched_set_swap(sched, True)
+    model = SchedulerModel(BlockPoolModel(n, 16, order), budget, max_running, swap=True)
+    rid = 0
+    swaps = 0
+    try:
+        for step in range(100000):
+            if step < 150:
+                for _ in range(int(rng.integers(0, 3))):
+                    prompt = int(rng.integers(1, 16 * max(1, n // 3)))
+                    out = int(rng.integers(1, 40))
+                    model.add_request(rid, prompt, out)
+                    pa.pa_sched_add_request(sched, rid, prompt, out)
+                    rid += 1
+            exp = model.schedule()
+            got = pa.pa_sched_schedule(sched, budget, max_running)
+            assert got["items"] == [tuple(i) for i in exp.items], step
+            assert got["slots"].tolist() == exp.slots
+            assert [tuple(c) for c in got["copies"].tolist()] == exp.copies
+            assert got["preempted"] == exp.preempted
+            ops = pa.pa_sched_swaps(sched)
+            exp_ops = [(r, "out", ln, b) for r, b, ln in exp.swap_out] + \
+                      [(r, "in", ln, b) for r, b, ln in exp.swap_in]
+            assert [(r, k, ln, b.tolist()) for r, k, ln, b in ops] == exp_ops, step
+            swaps += len(ops)
+            assert pa.pa_sched_commit(sched, max_running) == model.commit()
+            pa.pa_pool_check(pool)
+            assert pa.pa_free_list(pool).tolist() == model.pool.free
+            st = pa.pa_sched_get_stats(sched)
+            assert (st["n_waiting"], st["n_running"], st["n_swapped"]) == \
+                (len(model.waiting), len(model.running), len(model.swapped))
+            if step >= 150 and not (model.waiting or model.running or model.swapped):
+                break
+        assert st["finished"] == rid == len(model.finished)
+        for r in range(rid):
+            m = model.reqs[r]
+            assert pa.pa_sched_request(sched, r) == (m.computed, m.generated, m.preemptions)
+        with pytest.raises(pa.PaError):       # the planned step's list is gone after commit
+            pa.pa_sched_swaps(sched)
+    finally:
+        pa.pa_sched_destroy(sched)
+        pa.pa_pool_destroy(pool)
+    return swaps
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_swap_scheduler_matches_oracle_exactly(seed):
+    _swap_scheduler_trace(seed)
+
+
+def test_swap_scheduler_traces_do_swap():
+    # the traces are tight enough that requests are swapped out and back in
+    assert sum(_swap_scheduler_trace(k) for k in range(8)) > 10
+
+
 def test_scheduler_argument_checks():
     pool = pa.pa_pool_create(4)
     sched = pa.pa_sched_create(pool, 16, 2)

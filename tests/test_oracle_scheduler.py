@@ -10,7 +10,7 @@ from oracle.scheduler import SchedulerModel
 
 def run_to_end(s, max_steps=100000):
     steps = []
-    while s.waiting or s.running:
+    while s.waiting or s.running or s.swapped:
         steps.append(s.schedule())
         s.commit()
         assert len(steps) < max_steps
@@ -129,6 +129,84 @@ def test_random_traces_keep_the_invariants(seed):
     assert pool.num_free() == n
     for r in s.reqs.values():                    # every input token computed at least once
         assert processed[r.rid] >= r.prompt + r.out - 1
+
+
+def test_swap_preemption_keeps_the_victims_progress():
+    # ta-paperlens skeleton: preempt(running[-1]), moved to CPU memory instead
+    # of dropped; it resumes where it stopped, recomputing nothing
+    pool = BlockPoolModel(5)
+    s = SchedulerModel(pool, token_budget=64, max_running=8, swap=True)
+    s.add_request(0, prompt=32, out=40)
+    s.add_request(1, prompt=32, out=40)
+    p = s.schedule(); s.commit()
+    assert p.admitted == [0, 1] and pool.num_free() == 1
+    for _ in range(20):
+        table1, len1 = list(pool.tables[1]), s.reqs[1].computed
+        p = s.schedule()
+        if p.preempted:
+            break
+        s.commit()
+    assert p.preempted == [1] and p.swap_out == [(1, table1, len1)]
+    assert s.reqs[1].computed == len1 > 0 and list(s.swapped) == [1] and not s.waiting
+    assert 1 not in s.running and 1 not in pool.tables
+    s.commit()
+    resumed = None
+    while resumed is None:
+        p = s.schedule()
+        for rid, blocks, ln in p.swap_in:
+            resumed = (rid, blocks, ln)
+        s.commit()
+    assert resumed[0] == 1 and resumed[2] == len1 and len(resumed[1]) == -(-len1 // 16)
+    steps = run_to_end(s)
+    assert sorted(s.finished) == [0, 1] and pool.num_free() == 5 and steps
+
+
+def _swap_trace(seed):
+    # with swapping nothing is recomputed: over the whole run each request's
+    # chunks cover its prompt and all but its last output token exactly once,
+    # in order; a swapped-out request keeps its progress and resumes with
+    # ceil(computed/16) fresh blocks
+    rng = np.random.default_rng(50 + seed)
+    n = int(rng.integers(20, 80))
+    pool = BlockPoolModel(n, 16, rng.permutation(n))
+    budget = int(rng.integers(8, 200))
+    s = SchedulerModel(pool, token_budget=budget, max_running=int(rng.integers(1, 12)), swap=True)
+    rid, nxt = 0, {}
+    swaps = 0
+    for step in range(100000):
+        if step < 200:
+            for _ in range(int(rng.integers(0, 3))):
+                prompt = int(rng.integers(1, 16 * max(1, n // 4)))
+                s.add_request(rid, prompt=prompt, out=int(rng.integers(1, 30)))
+                rid += 1
+        before = {r: list(t) for r, t in pool.tables.items()}
+        p = s.schedule()
+        for r_, blocks, ln in p.swap_out:
+            assert blocks == before[r_] and ln == s.reqs[r_].computed > 0
+            swaps += 1
+        for r_, blocks, ln in p.swap_in:
+            assert len(blocks) == -(-ln // 16) and ln == s.reqs[r_].computed
+        for r_, start, k, _ in p.items:
+            assert start == nxt.get(r_, 0)       # contiguous, never repeated
+            nxt[r_] = start + k
+        s.commit()
+        pool.check()
+        if step >= 200 and not (s.waiting or s.running or s.swapped):
+            break
+    assert sorted(s.finished) == list(range(rid)) and pool.num_free() == n
+    for r in s.reqs.values():
+        assert nxt[r.rid] == r.prompt + r.out - 1
+    return swaps
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_swap_mode_computes_every_token_exactly_once(seed):
+    _swap_trace(seed)
+
+
+def test_swap_traces_do_swap():
+    # the traces are tight enough to exercise swapping
+    assert sum(_swap_trace(k) for k in range(5)) > 10
 
 
 def test_request_larger_than_the_pool_is_refused():
