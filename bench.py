@@ -205,7 +205,8 @@ def bench_serve(args):
             loop.step()
             step += 1
             st = loop.sched_stats()
-            if nxt == len(trace.prompt) and st["n_waiting"] == 0 and st["n_running"] == 0:
+            if (nxt == len(trace.prompt) and st["n_waiting"] == 0 and st["n_running"] == 0
+                    and st["n_swapped"] == 0):
                 return step
 
     # clock warm-up on a small trace of the same shape (not timed)
@@ -213,7 +214,8 @@ def bench_serve(args):
     run(warm, make_trace(32, seed=1, arrive_over=4))
     warm.close()
     torch.cuda.synchronize()
-    loop = ServingLoop(cache, n_q, 1.0 / np.sqrt(d), budget, max_running, rows_fn=rows_fn)
+    loop = ServingLoop(cache, n_q, 1.0 / np.sqrt(d), budget, max_running, rows_fn=rows_fn,
+                       swap=args.swap)
     t0 = time.perf_counter()
     steps = run(loop, tr)
     torch.cuda.synchronize()
@@ -242,6 +244,8 @@ def bench_serve(args):
             "pool_blocks": blocks, "token_budget": budget, "max_running": max_running,
             "prefill_tokens": st["prefill_tokens"], "decode_tokens": st["decode_tokens"],
             "preemptions": st["preempted"], "generated_tokens": out_tokens,
+            "preemption_mode": "swap" if args.swap else "recompute",
+            "swapped_out": st["swapped_out"], "swapped_in": st["swapped_in"],
         },
         "roofline": None,
         "cpu_baseline": None,
@@ -482,6 +486,9 @@ def main():
     ap.add_argument("--mixed", action="store_true",
                     help="time workload 5's decode batch and prefill chunk as one mixed "
                          "launch (and as separate launches) instead of the decode step")
+    ap.add_argument("--swap", action="store_true",
+                    help="with --serve: preempt by swapping to host memory instead of "
+                         "recomputing")
     ap.add_argument("--serve", action="store_true",
                     help="continuous-batching serving run (scheduler + kernels) instead of "
                          "the decode step")

@@ -107,49 +107,58 @@ class PagedKVCache:
            items, n_items, workspace, ws_bytes, stream, flags=flags)
 
     # -- preemption by swapping ----------------------------------------------
-    def swap_out(self, seq_id: int, stream=None) -> dict:
-        """Move a sequence's K/V to pinned host memory and release it:
-        pa_seq_swap_out, then pa_gather_blocks into a device staging buffer
-        (enqueued before anything can reuse the blocks) and one copy to the
-        host.  Returns what swap_in needs; the host copy is complete once the
-        stream reaches the returned event."""
+    def gather_to_host(self, blocks, stream=None):
+        """K and V tiles of `blocks` (host int32, logical order) into pinned
+        host tensors [n][n_kv][16*d]: pa_gather_blocks into a device staging
+        buffer, then one copy each, enqueued on `stream` (complete once the
+        stream gets there)."""
         stream = stream or torch.cuda.current_stream(self.device)
-        blocks, length = L.pa_seq_swap_out(self.pool, seq_id)
         n = len(blocks)
         tile = (n, self.n_kv, L.BLOCK_SIZE * self.d)
         dt = self.k_pool.dtype
-        saved = {"len": length, "n": n,
-                 "k": torch.empty(tile, dtype=dt, pin_memory=True),
-                 "v": torch.empty(tile, dtype=dt, pin_memory=True)}
+        k_host = torch.empty(tile, dtype=dt, pin_memory=True)
+        v_host = torch.empty(tile, dtype=dt, pin_memory=True)
         if n:
             with torch.cuda.stream(stream):
-                d_blocks = torch.from_numpy(blocks).pin_memory().to(self.device,
-                                                                    non_blocking=True)
+                d_blocks = torch.from_numpy(np.ascontiguousarray(blocks, dtype=np.int32)) \
+                    .pin_memory().to(self.device, non_blocking=True)
                 k_buf = torch.empty(tile, dtype=dt, device=self.device)
                 v_buf = torch.empty(tile, dtype=dt, device=self.device)
                 L.pa_gather_blocks(d_blocks, n, self.kv, k_buf, v_buf, stream)
-                saved["k"].copy_(k_buf, non_blocking=True)
-                saved["v"].copy_(v_buf, non_blocking=True)
-        ev = torch.cuda.Event()
-        ev.record(stream)
-        saved["event"] = ev
-        return saved
+                k_host.copy_(k_buf, non_blocking=True)
+                v_host.copy_(v_buf, non_blocking=True)
+        return k_host, v_host
 
-    def swap_in(self, seq_id: int, saved: dict, stream=None) -> np.ndarray:
-        """Re-create a swapped-out sequence in fresh blocks (pa_seq_swap_in)
-        and copy its K/V back (pa_scatter_blocks).  Raises OutOfBlocksError,
-        changing nothing, when the pool cannot hold it.  Returns its new
-        blocks."""
+    def scatter_from_host(self, blocks, k_host, v_host, stream=None) -> None:
+        """Write tiles saved by gather_to_host into `blocks` (pa_scatter_blocks)."""
         stream = stream or torch.cuda.current_stream(self.device)
-        blocks = L.pa_seq_swap_in(self.pool, seq_id, saved["len"])
         n = len(blocks)
         if n:
             with torch.cuda.stream(stream):
-                d_blocks = torch.from_numpy(blocks).pin_memory().to(self.device,
-                                                                    non_blocking=True)
-                k_buf = saved["k"].to(self.device, non_blocking=True)
-                v_buf = saved["v"].to(self.device, non_blocking=True)
+                d_blocks = torch.from_numpy(np.ascontiguousarray(blocks, dtype=np.int32)) \
+                    .pin_memory().to(self.device, non_blocking=True)
+                k_buf = k_host.to(self.device, non_blocking=True)
+                v_buf = v_host.to(self.device, non_blocking=True)
                 L.pa_scatter_blocks(d_blocks, n, self.kv, k_buf, v_buf, stream)
+
+    def swap_out(self, seq_id: int, stream=None) -> dict:
+        """Move a sequence's K/V to pinned host memory and release it
+        (pa_seq_swap_out, then gather_to_host, enqueued before anything can
+        reuse the blocks).  Returns what swap_in needs; the host copy is
+        complete once the stream reaches the returned event."""
+        stream = stream or torch.cuda.current_stream(self.device)
+        blocks, length = L.pa_seq_swap_out(self.pool, seq_id)
+        k_host, v_host = self.gather_to_host(blocks, stream)
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        return {"len": length, "n": len(blocks), "k": k_host, "v": v_host, "event": ev}
+
+    def swap_in(self, seq_id: int, saved: dict, stream=None) -> np.ndarray:
+        """Re-create a swapped-out sequence in fresh blocks (pa_seq_swap_in)
+        and copy its K/V back.  Raises OutOfBlocksError, changing nothing,
+        when the pool cannot hold it.  Returns its new blocks."""
+        blocks = L.pa_seq_swap_in(self.pool, seq_id, saved["len"])
+        self.scatter_from_host(blocks, saved["k"], saved["v"], stream)
         return blocks
 
     def require_fp16(self, what: str) -> None:

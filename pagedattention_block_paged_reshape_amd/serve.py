@@ -12,6 +12,10 @@ retire finished ones, preempt when out of blocks; [ngrok] scheduler section):
      sequences in one pa_paged_attention_decode launch; prefill chunks each
      get a pa_paged_attention_prefill launch (causal over the cache);
   4. pa_sched_commit retires finished requests and frees their blocks.
+With swap=True the scheduler preempts by swapping ([lens] skeleton: move
+the request to CPU memory instead of recomputing it): before anything else
+in a step, this loop copies the K/V of requests swapped out to pinned host
+memory and writes those of resumed requests back into their new blocks.
 This module only marshals arguments and launches; every step of the path
 runs in the library.
 """
@@ -29,7 +33,7 @@ from .cache import PagedKVCache
 class ServingLoop:
     def __init__(self, cache: PagedKVCache, num_q_heads: int, scale: float, token_budget: int,
                  max_running: int, partition: int = 512, row_fn=None,
-                 keep_outputs: bool = False, rows_fn=None):
+                 keep_outputs: bool = False, rows_fn=None, swap: bool = False):
         """row_fn(req, pos, tag, width) -> fp16 rows on the cache's device
         (int64 device tensors in), or rows_fn(req, pos, width_kv, width_q) ->
         (k, v, q) rows in one call; keep_outputs stores every attention
@@ -46,10 +50,14 @@ class ServingLoop:
         # (request, position) -> (output row [n_q][d], "decode" | "prefill")
         self.outputs: Dict[Tuple[int, int], Tuple[torch.Tensor, str]] = {}
         self.sched = L.pa_sched_create(cache.pool, self.budget, self.max_running)
+        self.swap = bool(swap)
+        if self.swap:
+            L.pa_sched_set_swap(self.sched, True)
+        self.saved: Dict[int, Tuple[torch.Tensor, torch.Tensor]] = {}  # swapped-out K/V
         dev = cache.device
         self.d = cache.d
         self.stats = {"steps": 0, "decode_tokens": 0, "prefill_tokens": 0, "preempted": 0,
-                      "finished": 0}
+                      "finished": 0, "swapped_out": 0, "swapped_in": 0}
         self._ws = torch.zeros(16, dtype=torch.uint8, device=dev)
         self._pws = torch.zeros(16, dtype=torch.uint8, device=dev)
         self.dev = dev
@@ -87,6 +95,16 @@ class ServingLoop:
         plan = L.pa_sched_schedule(self.sched, self.budget, self.max_running)
         items = plan["items"]
         self.stats["preempted"] += len(plan["preempted"])
+        if self.swap:
+            # outs first: their blocks may already belong to this step's writes
+            for rid, kind, _, blocks in L.pa_sched_swaps(self.sched):
+                if kind == "out":
+                    self.saved[rid] = self.cache.gather_to_host(blocks, stream)
+                    self.stats["swapped_out"] += 1
+                else:
+                    k_host, v_host = self.saved.pop(rid)
+                    self.cache.scatter_from_host(blocks, k_host, v_host, stream)
+                    self.stats["swapped_in"] += 1
         if items:
             req = np.concatenate([np.full(n, r, dtype=np.int64) for r, _, n, _ in items])
             pos = np.concatenate([np.arange(s, s + n, dtype=np.int64) for _, s, n, _ in items])
