@@ -660,6 +660,34 @@ def test_swap_scheduler_traces_do_swap():
     assert sum(_swap_scheduler_trace(k) for k in range(8)) > 10
 
 
+def test_swap_mode_switch_checks():
+    """Swap mode can change only between steps, and cannot be switched off
+    while requests are swapped out (they could never resume)."""
+    pool = pa.pa_pool_create(5)
+    sched = pa.pa_sched_create(pool, 64, 8)
+    try:
+        pa.pa_sched_set_swap(sched, True)
+        pa.pa_sched_add_request(sched, 0, 32, 40)
+        pa.pa_sched_add_request(sched, 1, 32, 40)
+        swapped = False
+        for _ in range(40):
+            pa.pa_sched_schedule(sched, 64, 8)
+            with pytest.raises(pa.PaError):          # a plan is open
+                pa.pa_sched_set_swap(sched, False)
+            pa.pa_sched_commit(sched, 8)
+            if pa.pa_sched_get_stats(sched)["n_swapped"]:
+                swapped = True
+                with pytest.raises(pa.PaError):      # request 1 is swapped out
+                    pa.pa_sched_set_swap(sched, False)
+                break
+        assert swapped
+        with pytest.raises(pa.PaError):              # no plan open
+            pa.pa_sched_swaps(sched)
+    finally:
+        pa.pa_sched_destroy(sched)
+        pa.pa_pool_destroy(pool)
+
+
 def test_scheduler_argument_checks():
     pool = pa.pa_pool_create(4)
     sched = pa.pa_sched_create(pool, 16, 2)
