@@ -266,7 +266,8 @@ def bench_prefill(args):
     log("[bench] generating workload 5")
     w = make_workload("5")
     pf = w.prefill
-    cache = PagedKVCache(w.num_blocks, w.n_kv, w.d, w.free_order, dev)
+    cache = PagedKVCache(w.num_blocks, w.n_kv, w.d, w.free_order, dev, kv_dtype=args.kv_dtype,
+                         k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE)
     dk = torch.from_numpy(w.setup_k).to(dev)
     dv = torch.from_numpy(w.setup_v).to(dev)
     run_program(cache, w.setup, dk, dv)
@@ -315,6 +316,7 @@ def bench_prefill(args):
                         f"{w.num_blocks} blocks scattered",
             "chunk": pf.chunk_len,
             "q_start": pf.q_start,
+            "kv_dtype": args.kv_dtype,
             "clock_warmup_ms": args.warm_ms,
         },
         "roofline": {

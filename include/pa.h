@@ -517,6 +517,18 @@ pa_status pa_paged_attention_prefill(pa_half* out, const pa_half* q, pa_kv_view 
                                      int32_t chunk_len, int32_t num_q_heads, float scale,
                                      void* workspace, uint64_t workspace_bytes, void* stream);
 
+/* pa_paged_attention_prefill over FP8 pools: the same arguments and
+ * workspace; K_j and V_j are the values the codes stand for.  The codes are
+ * widened to fp16 exactly as the tiles are staged, k_scale joins the softmax
+ * exponent's factor (scale * k_scale) and v_scale multiplies the normalised
+ * output; everything else is the fp16 kernel's arithmetic.  Scales must be
+ * positive and finite (PA_ERR_INVALID). */
+pa_status pa_paged_attention_prefill_fp8(pa_half* out, const pa_half* q, pa_kv_view_fp8 kv,
+                                         const int32_t* table, int32_t table_len,
+                                         int32_t q_start, int32_t chunk_len, int32_t num_q_heads,
+                                         float scale, void* workspace, uint64_t workspace_bytes,
+                                         void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Mixed step: decode batch + prefill chunk in one launch                    */
 /* ------------------------------------------------------------------------ */

@@ -143,6 +143,8 @@ _SIGS = {
     "pa_prefill_workspace_bytes": (_U64, [_I32, _I32, _I32, _I32]),
     "pa_paged_attention_prefill": (C.c_int, [_P, _P, pa_kv_view, _P, _I32, _I32, _I32, _I32,
                                              C.c_float, _P, _U64, _P]),
+    "pa_paged_attention_prefill_fp8": (C.c_int, [_P, _P, pa_kv_view_fp8, _P, _I32, _I32, _I32,
+                                                 _I32, C.c_float, _P, _U64, _P]),
     "pa_seq_swap_out": (C.c_int, [_P, _I64, _P, _I32, C.POINTER(_I32), C.POINTER(_I32)]),
     "pa_seq_swap_in": (C.c_int, [_P, _I64, _I32, _P, _I32, C.POINTER(_I32)]),
     "pa_gather_blocks": (C.c_int, [_P, _I32, pa_kv_view, _P, _P, _P]),
@@ -518,13 +520,15 @@ def pa_prefill_workspace_bytes(chunk_len: int, num_q_heads: int, head_dim: int,
     return int(LIB.pa_prefill_workspace_bytes(chunk_len, num_q_heads, head_dim, q_start))
 
 
-def pa_paged_attention_prefill(out, q, kv: pa_kv_view, table, table_len: int, q_start: int,
+def pa_paged_attention_prefill(out, q, kv, table, table_len: int, q_start: int,
                                chunk_len: int, num_q_heads: int, scale: float, workspace,
                                workspace_bytes: int, stream=None) -> None:
-    _check(LIB.pa_paged_attention_prefill(_dptr(out), _dptr(q), kv, _dptr(table), int(table_len),
-                                          int(q_start), int(chunk_len), int(num_q_heads),
-                                          float(scale), _dptr(workspace), int(workspace_bytes),
-                                          _stream(stream)), "pa_paged_attention_prefill")
+    """fp16 pools (pa_kv_view) or FP8 pools (pa_kv_view_fp8: the _fp8 entry point)."""
+    fn = LIB.pa_paged_attention_prefill_fp8 if isinstance(kv, pa_kv_view_fp8) \
+        else LIB.pa_paged_attention_prefill
+    _check(fn(_dptr(out), _dptr(q), kv, _dptr(table), int(table_len), int(q_start),
+              int(chunk_len), int(num_q_heads), float(scale), _dptr(workspace),
+              int(workspace_bytes), _stream(stream)), "pa_paged_attention_prefill")
 
 
 def decode_batch(out, q, tables, max_blocks: int, seq_lens, batch: int, partition_size: int,

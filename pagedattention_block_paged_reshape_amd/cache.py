@@ -249,7 +249,6 @@ class PrefillPlan:
 
     def __init__(self, cache: PagedKVCache, seq_id: int, q_start: int, chunk_len: int,
                  num_q_heads: int, scale: float):
-        cache.require_fp16("pa_paged_attention_prefill")
         self.cache = cache
         tab, _, self.seq_len, self.table_len = cache.tables([seq_id])
         self.table = tab[0].contiguous()

@@ -42,10 +42,10 @@ namespace pa {
 // (PV alone 481-483 us, scores alone 510 us, scores + PV 502 us).
 constexpr int kPfPrio = kPfPrioSoftmax | kPfPrioPV;
 
-template <int D>
+template <int D, bool FP8>
 __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a) {
   __shared__ PrefillLds<D> lds;
-  prefill_tile<D, kPfPrio>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds);
+  prefill_tile<D, kPfPrio, FP8>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds);
 }
 
 // Merge the key splits of each (row, head) by log-sum-exp.
@@ -57,6 +57,60 @@ __global__ __launch_bounds__(64) void prefill_reduce_kernel(int32_t chunk_len, i
                                                             const float* __restrict__ ws_l,
                                                             f16* __restrict__ out) {
   prefill_reduce_row<D>(chunk_len, n_q, splits, ws_o, ws_m, ws_l, out, blockIdx.x, blockIdx.y);
+}
+
+// Both pool types: checks, then the chunk kernel and (with key splits) the
+// merge.  k_pool / v_pool hold fp16 values or (fp8) E4M3 codes.
+static pa_status prefill_launch(pa_half* out, const pa_half* q, const pa_kv_view& kv, bool fp8,
+                                float k_scale, float v_scale, const int32_t* table,
+                                int32_t table_len, int32_t q_start, int32_t chunk_len,
+                                int32_t num_q_heads, float scale, void* workspace,
+                                uint64_t workspace_bytes, void* stream) {
+  if (fp8 && !(k_scale > 0.0f && k_scale <= 3.0e38f && v_scale > 0.0f && v_scale <= 3.0e38f))
+    return PA_ERR_INVALID;
+  PrefillArgs a{};
+  dim3 grid;
+  const pa_status st = prefill_prepare(out, q, kv, table, table_len, q_start, chunk_len,
+                                       num_q_heads, scale, workspace, workspace_bytes, a, grid);
+  if (st != PA_OK || chunk_len == 0) return st;
+  a.v_scale = 1.0f;
+  if (fp8) {
+    a.kp8 = reinterpret_cast<const uint8_t*>(kv.k_pool);
+    a.vp8 = reinterpret_cast<const uint8_t*>(kv.v_pool);
+    a.kp = a.vp = nullptr;
+    // a score is scale * q . (code * k_scale): k_scale joins the exponent's factor
+    a.scale_log2 *= k_scale;
+    a.v_scale = v_scale;
+  }
+  const int D = kv.head_dim;
+  const int splits = a.splits;
+  float* ws_o = a.ws_o;
+  float* ws_m = a.ws_m;
+  float* ws_l = a.ws_l;
+  f16* oo = a.out;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (D == 128) {
+    if (fp8)
+      prefill_chunk_kernel<128, true><<<grid, dim3(kPfThreads), 0, s>>>(a);
+    else
+      prefill_chunk_kernel<128, false><<<grid, dim3(kPfThreads), 0, s>>>(a);
+  } else {
+    if (fp8)
+      prefill_chunk_kernel<64, true><<<grid, dim3(kPfThreads), 0, s>>>(a);
+    else
+      prefill_chunk_kernel<64, false><<<grid, dim3(kPfThreads), 0, s>>>(a);
+  }
+  if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+  if (splits > 1) {
+    const dim3 rgrid(static_cast<uint32_t>(num_q_heads), static_cast<uint32_t>(chunk_len));
+    if (D == 128)
+      prefill_reduce_kernel<128><<<rgrid, dim3(64), 0, s>>>(chunk_len, num_q_heads, splits,
+                                                            ws_o, ws_m, ws_l, oo);
+    else
+      prefill_reduce_kernel<64><<<rgrid, dim3(64), 0, s>>>(chunk_len, num_q_heads, splits,
+                                                           ws_o, ws_m, ws_l, oo);
+  }
+  return launch_status();
 }
 
 }  // namespace pa
@@ -74,31 +128,18 @@ extern "C" pa_status pa_paged_attention_prefill(pa_half* out, const pa_half* q, 
                                                 int32_t num_q_heads, float scale,
                                                 void* workspace, uint64_t workspace_bytes,
                                                 void* stream) {
-  PrefillArgs a;
-  dim3 grid;
-  const pa_status st = prefill_prepare(out, q, kv, table, table_len, q_start, chunk_len,
-                                       num_q_heads, scale, workspace, workspace_bytes, a, grid);
-  if (st != PA_OK || chunk_len == 0) return st;
-  const int D = kv.head_dim;
-  const int splits = a.splits;
-  float* ws_o = a.ws_o;
-  float* ws_m = a.ws_m;
-  float* ws_l = a.ws_l;
-  f16* oo = a.out;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (D == 128)
-    prefill_chunk_kernel<128><<<grid, dim3(kPfThreads), 0, s>>>(a);
-  else
-    prefill_chunk_kernel<64><<<grid, dim3(kPfThreads), 0, s>>>(a);
-  if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
-  if (splits > 1) {
-    const dim3 rgrid(static_cast<uint32_t>(num_q_heads), static_cast<uint32_t>(chunk_len));
-    if (D == 128)
-      prefill_reduce_kernel<128><<<rgrid, dim3(64), 0, s>>>(chunk_len, num_q_heads, splits,
-                                                            ws_o, ws_m, ws_l, oo);
-    else
-      prefill_reduce_kernel<64><<<rgrid, dim3(64), 0, s>>>(chunk_len, num_q_heads, splits,
-                                                           ws_o, ws_m, ws_l, oo);
-  }
-  return launch_status();
+  return prefill_launch(out, q, kv, false, 1.0f, 1.0f, table, table_len, q_start, chunk_len,
+                        num_q_heads, scale, workspace, workspace_bytes, stream);
+}
+
+extern "C" pa_status pa_paged_attention_prefill_fp8(pa_half* out, const pa_half* q,
+                                                    pa_kv_view_fp8 kv, const int32_t* table,
+                                                    int32_t table_len, int32_t q_start,
+                                                    int32_t chunk_len, int32_t num_q_heads,
+                                                    float scale, void* workspace,
+                                                    uint64_t workspace_bytes, void* stream) {
+  const pa_kv_view v{reinterpret_cast<pa_half*>(kv.k_pool), reinterpret_cast<pa_half*>(kv.v_pool),
+                     kv.num_blocks, kv.block_size, kv.num_kv_heads, kv.head_dim};
+  return prefill_launch(out, q, v, true, kv.k_scale, kv.v_scale, table, table_len, q_start,
+                        chunk_len, num_q_heads, scale, workspace, workspace_bytes, stream);
 }

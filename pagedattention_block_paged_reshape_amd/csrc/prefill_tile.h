@@ -63,7 +63,22 @@ struct PrefillArgs {
   float* ws_o;
   float* ws_m;
   float* ws_l;
+  // FP8 pools (E4M3 codes, one scale per pool): k_scale is folded into
+  // scale_log2 by the host, v_scale multiplies the normalised output
+  const uint8_t* kp8;
+  const uint8_t* vp8;
+  float v_scale;
 };
+
+// Four E4M3 codes (byte j of w is element j) as fp16 (exact: every E4M3
+// value is an fp16 value).
+__device__ __forceinline__ f16x4 pf_e4m3x4_to_f16(uint32_t w) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 r = {
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true))};
+  return __builtin_bit_cast(f16x4, r);
+}
 
 // One workgroup's tile: kv head g, query tile qt, key split z.  All 256
 // threads of the workgroup take part (it has two workgroup barriers per key
@@ -80,7 +95,7 @@ __device__ __forceinline__ void phase_prio() {
 }
 
 // PRIO: the kPfPrio* phases run at wave priority 1 (else 0).
-template <int D, int PRIO>
+template <int D, int PRIO, bool FP8 = false>
 __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int g, int qt, int z,
                                              PrefillLds<D>& lds) {
   const f16* __restrict__ q = a.q;
@@ -151,6 +166,10 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int g, int qt
 
   // Register staging of one step's 4 K tiles and 4 V tiles.
   f16x8 rk[KCH], rv[KCH];
+  // FP8 pools: a tile is 16 * D bytes = D chunks of 16 codes; thread t holds
+  // chunk (t + 256u) % D of block (t + 256u) / D (uniform over a wavefront)
+  constexpr int KCH8 = (kPfKeys / kBlock) * D / kPfThreads;
+  u32x4 rk8[KCH8 > 0 ? KCH8 : 1], rv8[KCH8 > 0 ? KCH8 : 1];
   // Physical ids of a step's 4 blocks, read (clamped into the table; entries
   // past the sequence are never used) a step before their fetch.
   constexpr int kStepBlocks = kPfKeys / kBlock;
@@ -197,6 +216,70 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int g, int qt
       rv[u] = vv;
     }
   };
+  auto fetch8 = [&](int step, const int (&ids)[kStepBlocks]) {
+    const int key0 = step * kPfKeys;
+#pragma unroll
+    for (int u = 0; u < KCH8; ++u) {
+      const int ci = threadIdx.x + kPfThreads * u;
+      const int bi = uniform(ci / D);
+      const int within = ci % D;
+      const int lb = key0 / kBlock + bi;
+      if (lb * kBlock >= seq_end || lb >= table_len) {
+        rk8[u] = u32x4{0u, 0u, 0u, 0u};
+        rv8[u] = u32x4{0u, 0u, 0u, 0u};
+        continue;
+      }
+      int pb = ids[bi];
+      if (static_cast<uint32_t>(pb) >= static_cast<uint32_t>(num_blocks)) {
+        bad = true;
+        pb = 0;
+      }
+      const int64_t tile = (static_cast<int64_t>(pb) * n_kv + g) * (kBlock * D);
+      rk8[u] = *reinterpret_cast<const u32x4*>(a.kp8 + tile + within * 16);
+      u32x4 vv = *reinterpret_cast<const u32x4*>(a.vp8 + tile + within * 16);
+      if (lb * kBlock + kBlock > seq_end) {
+        // the sequence's last block: V chunk `within` holds slots 4q .. 4q+3
+        // (q = (within/16) % 4), slot 4q + j in byte j of each dword; zero
+        // the codes past the end (code 0 is +0)
+        const int valid = seq_end - (lb * kBlock + ((within >> 4) & 3) * 4);
+        const uint32_t keep =
+            valid >= 4 ? 0xFFFFFFFFu : (valid <= 0 ? 0u : (1u << (8 * valid)) - 1u);
+        vv &= u32x4{keep, keep, keep, keep};
+      }
+      rv8[u] = vv;
+    }
+  };
+  // FP8 chunk `within` of block bi: K slot within%16, dims 8*d8 .. +8 (bytes
+  // 0-7) and 8*(d8+4) .. +8 (bytes 8-15), d8 = 8*(within/64) + (within/16)%4;
+  // V dims c0 + 32*(t/2) + 16*(t%2) (dword t) at slots 4q .. 4q+3,
+  // c0 = 64*(within/64) + within%16.  Widened to fp16 into the same LDS rows
+  // as the fp16 path.
+  auto stash8 = [&]() {
+#pragma unroll
+    for (int u = 0; u < KCH8; ++u) {
+      const int ci = threadIdx.x + kPfThreads * u;
+      const int bi = ci / D;
+      const int within = ci % D;
+      const int key = bi * kBlock + (within & 15);
+      const int d8 = 8 * (within >> 6) + ((within >> 4) & 3);
+      const u32x4 kw = rk8[u];
+      const f16x4 k0 = pf_e4m3x4_to_f16(kw[0]), k1 = pf_e4m3x4_to_f16(kw[1]);
+      const f16x4 k2 = pf_e4m3x4_to_f16(kw[2]), k3 = pf_e4m3x4_to_f16(kw[3]);
+      *reinterpret_cast<f16x8*>(sk + key * KROW + d8 * 8) =
+          f16x8{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
+      *reinterpret_cast<f16x8*>(sk + key * KROW + (d8 + 4) * 8) =
+          f16x8{k2[0], k2[1], k2[2], k2[3], k3[0], k3[1], k3[2], k3[3]};
+      const int c0 = 64 * (within >> 6) + (within & 15);
+      const int q4 = (within >> 4) & 3;
+      const int kpos = (bi >> 1) * 32 + q4 * 8 + (bi & 1) * 4;
+      const u32x4 vw = rv8[u];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int dim = c0 + 32 * (t >> 1) + 16 * (t & 1);
+        *reinterpret_cast<f16x4*>(sv + dim * VROW + kpos) = pf_e4m3x4_to_f16(vw[t]);
+      }
+    }
+  };
   auto stash = [&]() {
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
@@ -223,15 +306,17 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int g, int qt
   int ids[kStepBlocks];
   if (st0 < st1) {
     read_ids(st0, ids);
-    fetch(st0, ids);
+    if constexpr (FP8) fetch8(st0, ids); else fetch(st0, ids);
   }
   if (st0 + 1 < st1) read_ids(st0 + 1, ids);
   for (int step = st0; step < st1; ++step) {
     phase_prio<PRIO, kPfPrioPV, kPfPrioStage>();
     __syncthreads();  // previous step's LDS reads are done
-    stash();
+    if constexpr (FP8) stash8(); else stash();
     __syncthreads();
-    if (step + 1 < st1) fetch(step + 1, ids);
+    if (step + 1 < st1) {
+      if constexpr (FP8) fetch8(step + 1, ids); else fetch(step + 1, ids);
+    }
 
     const int key0 = step * kPfKeys;
     // scores S^T[key][M-row]: 4 key tiles x 2 M-row tiles
@@ -345,7 +430,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int g, int qt
     const int r = mrow_r[nt];
     if (r >= chunk_len) continue;
     const int head = g * G + mrow_h[nt];
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const float inv = l > 0.0f ? (FP8 ? a.v_scale / l : 1.0f / l) : 0.0f;
     const int64_t qh = static_cast<int64_t>(r) * n_q + head;
     if (splits == 1) {
       f16* orow = out + qh * D;

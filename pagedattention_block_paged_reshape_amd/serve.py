@@ -170,7 +170,6 @@ class ServingLoop:
                 self.outputs[(r, s)] = (out[j], "decode")
 
     def _prefill(self, r: int, s: int, n: int, q: torch.Tensor, stream):
-        self.cache.require_fp16("pa_paged_attention_prefill")
         max_blocks = -(-(s + n) // L.BLOCK_SIZE)
         tab, ln = L.pa_block_tables(self.cache.pool, [r], max_blocks)
         assert int(ln[0]) == s + n

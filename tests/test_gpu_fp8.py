@@ -14,10 +14,10 @@ import torch
 
 from gpu_util import (FILL8, assert_close, assert_pools_bit_exact, gpu_run, log, oracle_run,
                       pools8_to_logical)
-from oracle import decode_reference
+from oracle import decode_reference, prefill_reference
 from oracle.fp8 import decode_e4m3
 from oracle.pool import Fp8PoolModel
-from synth import make_tiny_workload, make_workload
+from synth import make_mixed_workload, make_tiny_workload, make_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -160,8 +160,8 @@ def test_fp8_decode_with_saturated_codes():
     assert_close(res["decode"], decode_reference(w, st), "fp8 saturated")
 
 
-def test_fp8_decode_is_placement_invariant_and_prefill_refuses_fp8_pools():
-    from pagedattention_block_paged_reshape_amd.cache import PrefillPlan
+def test_fp8_decode_is_placement_invariant_and_mixed_refuses_fp8_pools():
+    from pagedattention_block_paged_reshape_amd.cache import MixedPlan
     w = make_tiny_workload(RAGGED, n_q=32, n_kv=8, d=128, seed=31, dist="normal")
     a = gpu_run(w, kv_dtype="fp8", k_scale=K_SCALE, v_scale=V_SCALE)
     w.free_order = np.random.default_rng(77).permutation(w.num_blocks).astype(np.int32)
@@ -169,4 +169,41 @@ def test_fp8_decode_is_placement_invariant_and_prefill_refuses_fp8_pools():
     torch.cuda.synchronize()
     assert torch.equal(a["decode"].view(torch.int16), b["decode"].view(torch.int16))
     with pytest.raises(NotImplementedError):
-        PrefillPlan(a["cache"], int(w.decode_ids[0]), 0, 1, w.n_q, w.scale)
+        MixedPlan(a["cache"], w.decode_ids, int(w.decode_ids[0]), 0, 1, w.n_q, w.scale)
+
+
+# --------------------------------------------------------------- prefill
+
+@pytest.mark.parametrize("decode_lengths,q_start,chunk,n_q,n_kv,d", [
+    ([], 0, 48, 4, 2, 128),            # whole causal prompt from position 0
+    ([17, 300], 37, 100, 32, 8, 128),  # unaligned start, ragged end, decode beside it
+    ([], 640, 129, 16, 16, 128),       # G = 1
+    ([], 333, 77, 64, 8, 128),         # G = 8
+    ([], 250, 130, 8, 2, 64),          # head_dim 64
+    ([], 4093, 512, 32, 8, 128),       # several key splits
+])
+def test_fp8_prefill_chunk_parity(decode_lengths, q_start, chunk, n_q, n_kv, d):
+    """Causal chunks over FP8 pools (every pool byte starts as a NaN code, so
+    an unmasked code past the end shows): within tolerance of the oracle
+    attending the dequantised values."""
+    w = make_mixed_workload(decode_lengths, q_start, chunk, n_q=n_q, n_kv=n_kv, d=d,
+                            seed=5 * q_start + chunk)
+    st = oracle_run(w, kv_dtype="fp8", k_scale=K_SCALE, v_scale=V_SCALE)
+    res = gpu_run(w, kv_dtype="fp8", k_scale=K_SCALE, v_scale=V_SCALE)
+    assert_pools_bit_exact(res["cache"], st)
+    err = assert_close(res["prefill"], prefill_reference(w, st), "fp8 prefill")
+    if w.batch:
+        assert_close(res["decode"], decode_reference(w, st), "fp8 decode beside the chunk")
+    log(f"fp8 prefill q_start={q_start} chunk={chunk} G={n_q // n_kv} d={d}: max err {err:.2e}")
+
+
+def test_fp8_config5_prefill_chunk():
+    """The long-context chunk (512 rows at 49,488) over FP8 pools, in the
+    launch the fp16 bench times; sampled rows, all heads."""
+    w = make_workload(5)
+    st = oracle_run(w, kv_dtype="fp8", k_scale=K_SCALE, v_scale=V_SCALE)
+    res = gpu_run(w, kv_dtype="fp8", k_scale=K_SCALE, v_scale=V_SCALE, decode=False)
+    rows = [0, 5, 31, 32, 255, 256, 400, 511]
+    err = assert_close(res["prefill"][rows], prefill_reference(w, st, rows=rows),
+                       "fp8 config 5 prefill (sampled rows)")
+    log(f"fp8 config 5 prefill: max err {err:.2e}")
