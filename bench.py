@@ -345,7 +345,8 @@ def bench_mixed(args):
     tokens and the 512-row causal prefill chunk at offset 49,488 of a
     50,000-token prompt, over one pool.  Times the one-launch mixed entry point
     against the same work as separate decode and prefill launches on one
-    stream (and each part alone)."""
+    stream (and each part alone).  With ``--kv-dtype fp8`` the pool holds
+    E4M3 codes and the _fp8 entry points run."""
     import torch
     from synth import make_workload
     from pagedattention_block_paged_reshape_amd.cache import (DecodePlan, MixedPlan, PagedKVCache,
@@ -355,7 +356,9 @@ def bench_mixed(args):
     log("[bench] generating workload 5")
     w = make_workload("5")
     pf = w.prefill
-    cache = PagedKVCache(w.num_blocks, w.n_kv, w.d, w.free_order, dev)
+    fp8 = args.kv_dtype == "fp8"
+    cache = PagedKVCache(w.num_blocks, w.n_kv, w.d, w.free_order, dev, kv_dtype=args.kv_dtype,
+                         k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE)
     dk = torch.from_numpy(w.setup_k).to(dev)
     dv = torch.from_numpy(w.setup_v).to(dev)
     run_program(cache, w.setup, dk, dv)
@@ -399,13 +402,15 @@ def bench_mixed(args):
     t_sep, _ = time_it(separate, args.steps)
     t_mix, wall = time_it(mixed, args.steps)
     flops = prefill_flops(pf.q_start, pf.chunk_len, w.n_q, w.d)
-    dec_bytes = algorithmic_decode_bytes(dplan.lens.cpu().numpy(), w.n_q, w.n_kv, w.d)
+    dec_bytes = algorithmic_decode_bytes(dplan.lens.cpu().numpy(), w.n_q, w.n_kv, w.d,
+                                         kv_bytes=1 if fp8 else 2)
     achieved = flops / (t_mix.mean() * 1e-6) / 1e12
     log(f"[bench] decode alone {t_dec.mean():.1f} us, prefill alone {t_pf.mean():.1f} us, "
         f"separate launches {t_sep.mean():.1f} us, mixed launch {t_mix.mean():.1f} us "
         f"(p50 {np.median(t_mix):.1f}, p99 {np.percentile(t_mix, 99):.1f})")
     result = {
-        "metric": "mixed decode + prefill attention step time (config 5)",
+        "metric": "mixed decode + prefill attention step time (config 5"
+                  + (", FP8 E4M3 pool)" if fp8 else ")"),
         "value": round(float(t_mix.mean()), 2),
         "unit": "us per step",
         "n_gpus": 1,
@@ -423,6 +428,7 @@ def bench_mixed(args):
                         f"chunk of {pf.chunk_len} rows at offset {pf.q_start} of a "
                         f"{pf.q_start + pf.chunk_len}-token prompt, {w.n_q}/{w.n_kv} heads, "
                         f"head_dim {w.d}, block 16, pool {w.num_blocks} blocks scattered",
+            "kv_dtype": args.kv_dtype,
             "clock_warmup_ms": args.warm_ms,
         },
         "roofline": {
@@ -432,7 +438,7 @@ def bench_mixed(args):
             "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
             "traffic": None,
-            "kernel": "pa_paged_attention_mixed (mixed_step_kernel + mixed_prefill_reduce_kernel + decode_reduce_kernel); "
+            "kernel": f"pa_paged_attention_mixed{'_fp8' if fp8 else ''} (mixed_step_kernel + mixed_prefill_reduce_kernel + decode_reduce_kernel); "
                       "achieved = the chunk's matrix-core flops over the whole mixed launch",
             "algorithmic_flops_per_launch": flops,
             "decode_algorithmic_bytes_per_launch": int(dec_bytes),

@@ -537,7 +537,7 @@ pa_status pa_paged_attention_prefill_fp8(pa_half* out, const pa_half* q, pa_kv_v
  * batch; [ngrok] "the scheduler": long prompts are prefilled chunk by chunk
  * alongside decoding requests).  The two parts are the arguments of
  * pa_paged_attention_decode (work-list form) and pa_paged_attention_prefill
- * over the same fp16 pool. */
+ * over the same pool (fp16 here, FP8 E4M3 in pa_paged_attention_mixed_fp8). */
 typedef struct pa_decode_batch {
   pa_half* out;              /* device [batch][n_q][D] fp16 */
   const pa_half* q;          /* device [batch][n_q][D] fp16 */
@@ -587,6 +587,17 @@ pa_status pa_paged_attention_mixed(const pa_decode_batch* dec, const pa_prefill_
                                    pa_kv_view kv, int32_t num_q_heads, float scale,
                                    void* workspace, uint64_t workspace_bytes, uint32_t flags,
                                    void* stream);
+
+/* pa_paged_attention_mixed over an FP8 E4M3 pool (pa_kv_view_fp8, one K and
+ * one V scale per pool): the outputs of pa_paged_attention_decode_fp8 and
+ * pa_paged_attention_prefill_fp8 on the same arguments, bitwise, from one
+ * attention kernel.  Workspace size, flags and error behaviour as for
+ * pa_paged_attention_mixed; scales must be positive and finite
+ * (PA_ERR_INVALID). */
+pa_status pa_paged_attention_mixed_fp8(const pa_decode_batch* dec, const pa_prefill_chunk* pf,
+                                       pa_kv_view_fp8 kv, int32_t num_q_heads, float scale,
+                                       void* workspace, uint64_t workspace_bytes, uint32_t flags,
+                                       void* stream);
 
 #ifdef __cplusplus
 }

@@ -156,6 +156,9 @@ _SIGS = {
     "pa_paged_attention_mixed": (C.c_int, [C.POINTER(pa_decode_batch),
                                            C.POINTER(pa_prefill_chunk), pa_kv_view, _I32,
                                            C.c_float, _P, _U64, C.c_uint32, _P]),
+    "pa_paged_attention_mixed_fp8": (C.c_int, [C.POINTER(pa_decode_batch),
+                                               C.POINTER(pa_prefill_chunk), pa_kv_view_fp8, _I32,
+                                               C.c_float, _P, _U64, C.c_uint32, _P]),
 }
 
 
@@ -552,9 +555,11 @@ def pa_mixed_workspace_bytes(dec: pa_decode_batch, pf: pa_prefill_chunk, num_q_h
 def pa_paged_attention_mixed(dec: pa_decode_batch, pf: pa_prefill_chunk, kv: pa_kv_view,
                              num_q_heads: int, scale: float, workspace, workspace_bytes: int,
                              stream=None, flags: int = 0) -> None:
-    _check(LIB.pa_paged_attention_mixed(C.byref(dec), C.byref(pf), kv, int(num_q_heads),
-                                        float(scale), _dptr(workspace), int(workspace_bytes),
-                                        int(flags), _stream(stream)), "pa_paged_attention_mixed")
+    """fp16 pools (pa_kv_view) or FP8 pools (pa_kv_view_fp8: the _fp8 entry point)."""
+    fn = LIB.pa_paged_attention_mixed_fp8 if isinstance(kv, pa_kv_view_fp8) \
+        else LIB.pa_paged_attention_mixed
+    _check(fn(C.byref(dec), C.byref(pf), kv, int(num_q_heads), float(scale), _dptr(workspace),
+              int(workspace_bytes), int(flags), _stream(stream)), "pa_paged_attention_mixed")
 
 
 def pa_seq_swap_out(pool: int, seq_id: int):

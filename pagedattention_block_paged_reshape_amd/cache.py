@@ -161,10 +161,6 @@ class PagedKVCache:
         self.scatter_from_host(blocks, saved["k"], saved["v"], stream)
         return blocks
 
-    def require_fp16(self, what: str) -> None:
-        if self.fp8:
-            raise NotImplementedError(f"{what} reads fp16 pools only")
-
     # -- one append: reserve, copy-on-write, store --------------------------
     def append(self, seq_ids, n_new, k_rows: torch.Tensor, v_rows: torch.Tensor,
                stream: Optional[torch.cuda.Stream] = None):
@@ -270,13 +266,12 @@ class PrefillPlan:
 
 class MixedPlan:
     """Device-resident arguments of one mixed launch: a decode batch (work-list
-    form) and one prefill chunk over the same fp16 pool, attended by
-    ``pa_paged_attention_mixed``."""
+    form) and one prefill chunk over the same pool (fp16 or FP8), attended by
+    ``pa_paged_attention_mixed`` (``pa_paged_attention_mixed_fp8``)."""
 
     def __init__(self, cache: PagedKVCache, seq_ids, prefill_seq_id: int, q_start: int,
                  chunk_len: int, num_q_heads: int, scale: float,
                  partition: int = DEFAULT_PARTITION, keep_kv: Optional[bool] = None):
-        cache.require_fp16("pa_paged_attention_mixed")
         self.cache = cache
         self.dec = DecodePlan(cache, seq_ids, num_q_heads, scale, partition, keep_kv=keep_kv)
         self.pf = PrefillPlan(cache, prefill_seq_id, q_start, chunk_len, num_q_heads, scale)

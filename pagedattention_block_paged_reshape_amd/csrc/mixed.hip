@@ -35,7 +35,7 @@ union MixedLds {
   MixedDecodeLds<D> dec;
 };
 
-template <int D, bool KEEP>
+template <int D, bool KEEP, bool FP8>
 __global__ __launch_bounds__(kPfThreads) void mixed_step_kernel(PrefillArgs pa, int32_t pf_wgs,
                                                                  int32_t pf_qtiles, DecodeArgs da,
                                                                  const int32_t* __restrict__ items,
@@ -48,7 +48,7 @@ __global__ __launch_bounds__(kPfThreads) void mixed_step_kernel(PrefillArgs pa, 
     // share CUs with decode units starved them (measured on the
     // long-context step: 650 us with the prefill launch's priorities, also
     // when decode units ran at a higher priority, vs 607 us without)
-    prefill_tile<D, 0>(pa, wg % pa.n_kv, rest % pf_qtiles, rest / pf_qtiles, lds.pf);
+    prefill_tile<D, 0, FP8>(pa, wg % pa.n_kv, rest % pf_qtiles, rest / pf_qtiles, lds.pf);
     return;
   }
   if (threadIdx.x < 2) {
@@ -67,20 +67,20 @@ __global__ __launch_bounds__(kPfThreads) void mixed_step_kernel(PrefillArgs pa, 
   const Unit u = make_unit(da, static_cast<int>(packed >> 16), static_cast<int>(packed & 0xFFFFu),
                            wave, lane);
   const Unit nx = no_unit();
-  typedef TileRegs<D, false> TR;
+  typedef TileRegs<D, FP8> TR;
   f16x8 qf[D / 32];
   typename TR::K kA[TR::NB * TR::NK], kB[TR::NB * TR::NK];
   typename TR::V vA[TR::NB * TR::NV], vB[TR::NB * TR::NV];
   if (u.cnt > 0) {
     load_q<D>(da, g, u.b, lane, qf);
-    load_set<D, KEEP, false>(da, g, u, nx, 0, true, lane, kA, vA);
+    load_set<D, KEEP, FP8>(da, g, u, nx, 0, true, lane, kA, vA);
   }
   WaveState<D> st;
-  run_unit<D, KEEP, false>(da, g, wave, lane, u, nx, qf, kA, vA, kB, vB, st);
+  run_unit<D, KEEP, FP8>(da, g, wave, lane, u, nx, qf, kA, vA, kB, vB, st);
   const MergeSlot<D> ms{lds.dec.m[pair], lds.dec.l[pair], lds.dec.o[pair], &lds.dec.arrive[pair],
                         &lds.dec.bad[pair]};
   if (post_state<D>(ms, st, da.G, wave, lane, u.bad) && u.ok)
-    merge_store<D, false>(da, ms, g, u.b, u.p, u.L, u.n_parts, lane);
+    merge_store<D, FP8>(da, ms, g, u.b, u.p, u.L, u.n_parts, lane);
 }
 
 // Merges after the mixed step's kernel: the prefill (row, head) pairs whose
@@ -109,15 +109,31 @@ static uint64_t mixed_decode_ws(const pa_decode_batch& d, int32_t num_q_heads, i
   return (b + kMixedWsAlign - 1) / kMixedWsAlign * kMixedWsAlign;
 }
 
+template <bool KEEP, bool FP8>
+static void launch_step(int D, dim3 grid, hipStream_t s, const PrefillArgs& pa, int32_t pf_wgs,
+                        int32_t qtiles, const DecodeArgs& da, const int32_t* items,
+                        int32_t n_items) {
+  if (D == 128)
+    mixed_step_kernel<128, KEEP, FP8><<<grid, dim3(kPfThreads), 0, s>>>(pa, pf_wgs, qtiles, da,
+                                                                         items, n_items);
+  else
+    mixed_step_kernel<64, KEEP, FP8><<<grid, dim3(kPfThreads), 0, s>>>(pa, pf_wgs, qtiles, da,
+                                                                        items, n_items);
+}
+
+// Both pool types: k_pool / v_pool hold fp16 values or (fp8) E4M3 codes with
+// one scale per pool, as in the decode and prefill launches.
 static pa_status mixed_launch(const pa_decode_batch* dec, const pa_prefill_chunk* pf,
-                              const pa_kv_view& kv, int32_t num_q_heads, float scale,
-                              void* workspace, uint64_t workspace_bytes, uint32_t flags,
-                              void* stream) {
+                              const pa_kv_view& kv, bool fp8, float k_scale, float v_scale,
+                              int32_t num_q_heads, float scale, void* workspace,
+                              uint64_t workspace_bytes, uint32_t flags, void* stream) {
   if (dec == nullptr || pf == nullptr) return PA_ERR_INVALID;
+  if (fp8 && !(k_scale > 0.0f && k_scale <= 3.0e38f && v_scale > 0.0f && v_scale <= 3.0e38f))
+    return PA_ERR_INVALID;
   if ((flags & ~static_cast<uint32_t>(PA_DECODE_KEEP_KV)) != 0) return PA_ERR_INVALID;
   if (dec->batch > 0 && dec->n_items > 0 && dec->work_items == nullptr) return PA_ERR_INVALID;
   const PoolArgs pool{kv.k_pool, kv.v_pool, kv.num_blocks, kv.block_size, kv.num_kv_heads,
-                      kv.head_dim, false, 1.0f, 1.0f};
+                      kv.head_dim, fp8, fp8 ? k_scale : 1.0f, fp8 ? v_scale : 1.0f};
   const uint64_t dec_ws = mixed_decode_ws(*dec, num_q_heads, kv.head_dim);
   if (workspace_bytes < dec_ws) return PA_ERR_INVALID;
   DecodeArgs da{};
@@ -132,6 +148,15 @@ static pa_status mixed_launch(const pa_decode_batch* dec, const pa_prefill_chunk
   st = prefill_prepare(pf->out, pf->q, kv, pf->table, pf->table_len, pf->q_start, pf->chunk_len,
                        num_q_heads, scale, pf_ws, workspace_bytes - dec_ws, pa, pgrid);
   if (st != PA_OK) return st;
+  pa.v_scale = 1.0f;
+  if (fp8) {
+    pa.kp8 = reinterpret_cast<const uint8_t*>(kv.k_pool);
+    pa.vp8 = reinterpret_cast<const uint8_t*>(kv.v_pool);
+    pa.kp = pa.vp = nullptr;
+    // a score is scale * q . (code * k_scale): k_scale joins the exponent's factor
+    pa.scale_log2 *= k_scale;
+    pa.v_scale = v_scale;
+  }
   const int64_t pf_wgs =
       pf->chunk_len > 0 ? static_cast<int64_t>(pgrid.x) * pgrid.y * pgrid.z : 0;
   const int64_t dec_wgs =
@@ -144,20 +169,17 @@ static pa_status mixed_launch(const pa_decode_batch* dec, const pa_prefill_chunk
   const dim3 grid(static_cast<uint32_t>(pf_wgs + dec_wgs));
   const int32_t qtiles = static_cast<int32_t>(pgrid.y);
   const int32_t n_items = dec->batch > 0 ? dec->n_items : 0;
-  if (D == 128) {
+  const int32_t pw = static_cast<int32_t>(pf_wgs);
+  if (fp8) {
     if (keep)
-      mixed_step_kernel<128, true><<<grid, dim3(kPfThreads), 0, s>>>(
-          pa, static_cast<int32_t>(pf_wgs), qtiles, da, dec->work_items, n_items);
+      launch_step<true, true>(D, grid, s, pa, pw, qtiles, da, dec->work_items, n_items);
     else
-      mixed_step_kernel<128, false><<<grid, dim3(kPfThreads), 0, s>>>(
-          pa, static_cast<int32_t>(pf_wgs), qtiles, da, dec->work_items, n_items);
+      launch_step<false, true>(D, grid, s, pa, pw, qtiles, da, dec->work_items, n_items);
   } else {
     if (keep)
-      mixed_step_kernel<64, true><<<grid, dim3(kPfThreads), 0, s>>>(
-          pa, static_cast<int32_t>(pf_wgs), qtiles, da, dec->work_items, n_items);
+      launch_step<true, false>(D, grid, s, pa, pw, qtiles, da, dec->work_items, n_items);
     else
-      mixed_step_kernel<64, false><<<grid, dim3(kPfThreads), 0, s>>>(
-          pa, static_cast<int32_t>(pf_wgs), qtiles, da, dec->work_items, n_items);
+      launch_step<false, false>(D, grid, s, pa, pw, qtiles, da, dec->work_items, n_items);
   }
   if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   if (pf->chunk_len > 0 && pa.splits > 1) {
@@ -197,5 +219,17 @@ extern "C" pa_status pa_paged_attention_mixed(const pa_decode_batch* dec,
                                               int32_t num_q_heads, float scale, void* workspace,
                                               uint64_t workspace_bytes, uint32_t flags,
                                               void* stream) {
-  return mixed_launch(dec, pf, kv, num_q_heads, scale, workspace, workspace_bytes, flags, stream);
+  return mixed_launch(dec, pf, kv, false, 1.0f, 1.0f, num_q_heads, scale, workspace,
+                      workspace_bytes, flags, stream);
+}
+
+extern "C" pa_status pa_paged_attention_mixed_fp8(const pa_decode_batch* dec,
+                                                  const pa_prefill_chunk* pf, pa_kv_view_fp8 kv,
+                                                  int32_t num_q_heads, float scale,
+                                                  void* workspace, uint64_t workspace_bytes,
+                                                  uint32_t flags, void* stream) {
+  const pa_kv_view v{reinterpret_cast<pa_half*>(kv.k_pool), reinterpret_cast<pa_half*>(kv.v_pool),
+                     kv.num_blocks, kv.block_size, kv.num_kv_heads, kv.head_dim};
+  return mixed_launch(dec, pf, v, true, kv.k_scale, kv.v_scale, num_q_heads, scale, workspace,
+                      workspace_bytes, flags, stream);
 }

@@ -160,16 +160,13 @@ def test_fp8_decode_with_saturated_codes():
     assert_close(res["decode"], decode_reference(w, st), "fp8 saturated")
 
 
-def test_fp8_decode_is_placement_invariant_and_mixed_refuses_fp8_pools():
-    from pagedattention_block_paged_reshape_amd.cache import MixedPlan
+def test_fp8_decode_is_placement_invariant():
     w = make_tiny_workload(RAGGED, n_q=32, n_kv=8, d=128, seed=31, dist="normal")
     a = gpu_run(w, kv_dtype="fp8", k_scale=K_SCALE, v_scale=V_SCALE)
     w.free_order = np.random.default_rng(77).permutation(w.num_blocks).astype(np.int32)
     b = gpu_run(w, kv_dtype="fp8", k_scale=K_SCALE, v_scale=V_SCALE)
     torch.cuda.synchronize()
     assert torch.equal(a["decode"].view(torch.int16), b["decode"].view(torch.int16))
-    with pytest.raises(NotImplementedError):
-        MixedPlan(a["cache"], w.decode_ids, int(w.decode_ids[0]), 0, 1, w.n_q, w.scale)
 
 
 # --------------------------------------------------------------- prefill
@@ -207,3 +204,68 @@ def test_fp8_config5_prefill_chunk():
     err = assert_close(res["prefill"][rows], prefill_reference(w, st, rows=rows),
                        "fp8 config 5 prefill (sampled rows)")
     log(f"fp8 config 5 prefill: max err {err:.2e}")
+
+
+# ------------------------------------------------------------ mixed launch
+
+def _run_mixed_fp8(w, res, partition=512, keep_kv=None):
+    from pagedattention_block_paged_reshape_amd.cache import MixedPlan
+    pf = w.prefill
+    plan = MixedPlan(res["cache"], w.decode_ids, pf.seq_id, pf.q_start, pf.chunk_len, w.n_q,
+                     w.scale, partition, keep_kv=keep_kv)
+    dev = res["cache"].device
+    d_out, p_out = plan.run(torch.from_numpy(w.q).to(dev), torch.from_numpy(pf.q).to(dev))
+    torch.cuda.synchronize()
+    return plan, d_out.clone(), p_out.clone()
+
+
+@pytest.mark.parametrize("decode_lengths,q_start,chunk,n_q,n_kv,d,keep", [
+    ([5, 16, 17, 33], 0, 48, 4, 2, 128, False),        # tiny decode + whole causal prompt
+    ([1, 600, 1537, 2049], 37, 100, 32, 8, 128, False),  # multi-partition decode, ragged chunk
+    ([90, 1025], 333, 77, 64, 8, 128, False),          # G = 8
+    ([300, 45, 1100], 250, 130, 8, 2, 64, False),      # head_dim 64
+    ([4096, 3, 129], 4093, 512, 32, 8, 128, False),    # several key splits
+    ([40, 300], 200, 64, 32, 8, 128, True),            # KEEP decode loads
+])
+def test_fp8_mixed_equals_separate_launches_and_oracle(decode_lengths, q_start, chunk, n_q,
+                                                        n_kv, d, keep):
+    """pa_paged_attention_mixed_fp8: bitwise the FP8 decode and prefill
+    launches on the same pool, within tolerance of the oracle attending the
+    dequantised values."""
+    w = make_mixed_workload(decode_lengths, q_start, chunk, n_q=n_q, n_kv=n_kv, d=d,
+                            seed=3 * q_start + chunk + 1)
+    st = oracle_run(w, kv_dtype="fp8", k_scale=K_SCALE, v_scale=V_SCALE)
+    res = gpu_run(w, kv_dtype="fp8", k_scale=K_SCALE, v_scale=V_SCALE, keep_kv=keep or None)
+    _, d_out, p_out = _run_mixed_fp8(w, res, keep_kv=keep or None)
+    assert torch.equal(d_out.view(torch.int16), res["decode"].view(torch.int16))
+    assert torch.equal(p_out.view(torch.int16), res["prefill"].view(torch.int16))
+    err = assert_close(d_out, decode_reference(w, st), "fp8 mixed decode")
+    errp = assert_close(p_out, prefill_reference(w, st), "fp8 mixed prefill")
+    log(f"fp8 mixed {decode_lengths} q_start={q_start} chunk={chunk} d={d} keep={keep}: "
+        f"decode {err:.2e}, prefill {errp:.2e}")
+
+
+def test_fp8_config5_mixed_launch_and_scale_checks():
+    """The long-context step over FP8 pools at full size: bitwise the separate
+    FP8 launches; decode against the oracle in full, prefill on sampled rows.
+    Non-positive or non-finite scales are refused before any launch."""
+    import pagedattention_block_paged_reshape_amd as pa
+    from pagedattention_block_paged_reshape_amd import _lib as L
+    w = make_workload(5)
+    st = oracle_run(w, kv_dtype="fp8", k_scale=K_SCALE, v_scale=V_SCALE)
+    res = gpu_run(w, partition=512, kv_dtype="fp8", k_scale=K_SCALE, v_scale=V_SCALE)
+    plan, d_out, p_out = _run_mixed_fp8(w, res)
+    assert torch.equal(d_out.view(torch.int16), res["decode"].view(torch.int16))
+    assert torch.equal(p_out.view(torch.int16), res["prefill"].view(torch.int16))
+    err = assert_close(d_out, decode_reference(w, st), "fp8 config 5 mixed decode")
+    rows = [0, 31, 32, 383, 384, 511]
+    errp = assert_close(p_out[rows], prefill_reference(w, st, rows=rows),
+                        "fp8 config 5 mixed prefill (sampled rows)")
+    kv = res["cache"].kv
+    for ks, vs in [(0.0, 1.0), (1.0, -1.0), (float("inf"), 1.0), (1.0, float("nan"))]:
+        bad = L.pa_kv_view_fp8(kv.k_pool, kv.v_pool, kv.num_blocks, kv.block_size,
+                               kv.num_kv_heads, kv.head_dim, ks, vs)
+        with pytest.raises(pa.PaError):
+            pa.pa_paged_attention_mixed(plan.c_dec, plan.c_pf, bad, w.n_q, w.scale,
+                                        plan.workspace, plan.ws_bytes)
+    log(f"fp8 config 5 mixed: decode max err {err:.2e}, prefill max err {errp:.2e}")
