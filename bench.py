@@ -210,12 +210,13 @@ def bench_serve(args):
                 return step
 
     # clock warm-up on a small trace of the same shape (not timed)
-    warm = ServingLoop(cache, n_q, 1.0 / np.sqrt(d), budget, max_running, rows_fn=rows_fn)
+    warm = ServingLoop(cache, n_q, 1.0 / np.sqrt(d), budget, max_running, rows_fn=rows_fn,
+                       mixed=args.mixed)
     run(warm, make_trace(32, seed=1, arrive_over=4))
     warm.close()
     torch.cuda.synchronize()
     loop = ServingLoop(cache, n_q, 1.0 / np.sqrt(d), budget, max_running, rows_fn=rows_fn,
-                       swap=args.swap)
+                       swap=args.swap, mixed=args.mixed)
     t0 = time.perf_counter()
     steps = run(loop, tr)
     torch.cuda.synchronize()
@@ -245,6 +246,7 @@ def bench_serve(args):
             "prefill_tokens": st["prefill_tokens"], "decode_tokens": st["decode_tokens"],
             "preemptions": st["preempted"], "generated_tokens": out_tokens,
             "preemption_mode": "swap" if args.swap else "recompute",
+            "mixed_launches": bool(args.mixed),
             "swapped_out": st["swapped_out"], "swapped_in": st["swapped_in"],
         },
         "roofline": None,
@@ -493,7 +495,9 @@ def main():
                     help="time the causal prefill chunk of workload 5 instead of decode")
     ap.add_argument("--mixed", action="store_true",
                     help="time workload 5's decode batch and prefill chunk as one mixed "
-                         "launch (and as separate launches) instead of the decode step")
+                         "launch (and as separate launches) instead of the decode step; "
+                         "with --serve: run each step's decode batch and first prefill chunk "
+                         "as one mixed launch")
     ap.add_argument("--swap", action="store_true",
                     help="with --serve: preempt by swapping to host memory instead of "
                          "recomputing")

@@ -16,6 +16,9 @@ With swap=True the scheduler preempts by swapping ([lens] skeleton: move
 the request to CPU memory instead of recomputing it): before anything else
 in a step, this loop copies the K/V of requests swapped out to pinned host
 memory and writes those of resumed requests back into their new blocks.
+With mixed=True a step with both kinds of work runs its decode batch and its
+first prefill chunk in one pa_paged_attention_mixed launch (bitwise the same
+outputs as the two separate launches).
 This module only marshals arguments and launches; every step of the path
 runs in the library.
 """
@@ -33,7 +36,8 @@ from .cache import PagedKVCache
 class ServingLoop:
     def __init__(self, cache: PagedKVCache, num_q_heads: int, scale: float, token_budget: int,
                  max_running: int, partition: int = 512, row_fn=None,
-                 keep_outputs: bool = False, rows_fn=None, swap: bool = False):
+                 keep_outputs: bool = False, rows_fn=None, swap: bool = False,
+                 mixed: bool = False):
         """row_fn(req, pos, tag, width) -> fp16 rows on the cache's device
         (int64 device tensors in), or rows_fn(req, pos, width_kv, width_q) ->
         (k, v, q) rows in one call; keep_outputs stores every attention
@@ -51,13 +55,14 @@ class ServingLoop:
         self.outputs: Dict[Tuple[int, int], Tuple[torch.Tensor, str]] = {}
         self.sched = L.pa_sched_create(cache.pool, self.budget, self.max_running)
         self.swap = bool(swap)
+        self.mixed = bool(mixed)
         if self.swap:
             L.pa_sched_set_swap(self.sched, True)
         self.saved: Dict[int, Tuple[torch.Tensor, torch.Tensor]] = {}  # swapped-out K/V
         dev = cache.device
         self.d = cache.d
         self.stats = {"steps": 0, "decode_tokens": 0, "prefill_tokens": 0, "preempted": 0,
-                      "finished": 0, "swapped_out": 0, "swapped_in": 0}
+                      "finished": 0, "swapped_out": 0, "swapped_in": 0, "mixed_launches": 0}
         self._ws = torch.zeros(16, dtype=torch.uint8, device=dev)
         self._pws = torch.zeros(16, dtype=torch.uint8, device=dev)
         self.dev = dev
@@ -136,18 +141,26 @@ class ServingLoop:
                     q_dec = q[:len(dec)]
                 else:
                     q_dec = q[self._h2d(rows.astype(np.int64))]
-                self._decode([items[i] for i in dec], q_dec, stream)
+                first = None
+                if self.mixed and pre:
+                    first = pre[0]
+                    pre = pre[1:]
+                    r, s, n, _ = items[first]
+                    first = (r, s, n, q[offs[first]:offs[first] + n])
+                self._decode([items[i] for i in dec], q_dec, stream, chunk=first)
             for i in pre:
                 r, s, n, _ = items[i]
                 self._prefill(r, s, n, q[offs[i]:offs[i] + n], stream)
             self.stats["decode_tokens"] += len(dec)
-            self.stats["prefill_tokens"] += int(sum(items[i][2] for i in pre))
+            self.stats["prefill_tokens"] += int(sum(it[2] for it in items if not it[3]))
         done = L.pa_sched_commit(self.sched, self.max_running)
         self.stats["steps"] += 1
         self.stats["finished"] += len(done)
         return done
 
-    def _decode(self, items, q: torch.Tensor, stream):
+    def _decode(self, items, q: torch.Tensor, stream, chunk=None):
+        """Decode attention for the items; with chunk = (request, start,
+        length, query rows) that prefill chunk runs in the same launch."""
         ids = [r for r, _, _, _ in items]
         # each request's length after this step is known from its item
         max_blocks = max(-(-(s + 1) // L.BLOCK_SIZE) for _, s, _, _ in items)
@@ -162,9 +175,29 @@ class ServingLoop:
         d_len = self._h2d(ln)
         d_work = self._h2d(work)
         flags = L.PA_DECODE_KEEP_KV if self.cache.shares_blocks() else 0
-        self.cache.decode(out, q.contiguous(), d_tab, max_blocks, d_len, len(ids), self.n_q,
-                          self.scale, self.partition, max_len, d_work, len(work), ws, ws_bytes,
-                          stream, flags=flags)
+        if chunk is None:
+            self.cache.decode(out, q.contiguous(), d_tab, max_blocks, d_len, len(ids), self.n_q,
+                              self.scale, self.partition, max_len, d_work, len(work), ws,
+                              ws_bytes, stream, flags=flags)
+        else:
+            r, s, n, qc = chunk
+            pf_blocks = -(-(s + n) // L.BLOCK_SIZE)
+            ptab, pln = L.pa_block_tables(self.cache.pool, [r], pf_blocks)
+            assert int(pln[0]) == s + n
+            qc = qc.contiguous()
+            pout = torch.empty((n, self.n_q, self.d), dtype=torch.float16, device=self.dev)
+            c_dec = L.decode_batch(out, q.contiguous(), d_tab, max_blocks, d_len, len(ids),
+                                   self.partition, max_len, d_work, len(work))
+            d_ptab = self._h2d(ptab[0])
+            c_pf = L.prefill_chunk(pout, qc, d_ptab, pf_blocks, s, n)
+            mws_bytes = L.pa_mixed_workspace_bytes(c_dec, c_pf, self.n_q, self.d)
+            mws = self._workspace("_ws", max(mws_bytes, 16))
+            L.pa_paged_attention_mixed(c_dec, c_pf, self.cache.kv, self.n_q, self.scale, mws,
+                                       mws_bytes, stream, flags=flags)
+            self.stats["mixed_launches"] += 1
+            if self.keep:
+                for j in range(n):
+                    self.outputs[(r, s + j)] = (pout[j], "prefill")
         if self.keep:
             for j, (r, s, _, _) in enumerate(items):
                 self.outputs[(r, s)] = (out[j], "decode")

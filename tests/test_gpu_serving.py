@@ -39,7 +39,8 @@ def rows_kvq_dev(req, pos, width_kv, width_q):
     return token_rows_kvq(req, pos, width_kv, width_q, xp=torch)
 
 
-def serve(trace, num_blocks, budget, max_running, seed=0, fused_rows=False, swap=False):
+def serve(trace, num_blocks, budget, max_running, seed=0, fused_rows=False, swap=False,
+          mixed=False):
     from pagedattention_block_paged_reshape_amd.cache import PagedKVCache
     from pagedattention_block_paged_reshape_amd.serve import ServingLoop
     log(f"[serve] blocks={num_blocks} budget={budget} max_running={max_running}")
@@ -47,10 +48,10 @@ def serve(trace, num_blocks, budget, max_running, seed=0, fused_rows=False, swap
     cache = PagedKVCache(num_blocks, N_KV, D, order, "cuda:0")
     if fused_rows:
         loop = ServingLoop(cache, N_Q, SCALE, budget, max_running, rows_fn=rows_kvq_dev,
-                           keep_outputs=True, swap=swap)
+                           keep_outputs=True, swap=swap, mixed=mixed)
     else:
         loop = ServingLoop(cache, N_Q, SCALE, budget, max_running, row_fn=rows_dev,
-                           keep_outputs=True)
+                           keep_outputs=True, mixed=mixed)
     nxt = 0
     for step in range(20000):
         while nxt < len(trace.prompt) and trace.arrival[nxt] <= step:
@@ -139,3 +140,38 @@ def test_serving_with_swap_preemption_matches_oracle_and_unpressured_run():
         ref = oracle_row(r, p)
         got = small[(r, p)][0].astype(np.float64)
         assert np.isclose(got, ref, rtol=RTOL, atol=ATOL).all(), ((r, p), small[(r, p)][1])
+
+
+def test_serving_with_mixed_launches_matches_separate_launches():
+    """Requests arriving over 60 steps, so that many steps hold decode work
+    and a prompt chunk: with mixed=True those steps run the decode batch and
+    the first chunk in one pa_paged_attention_mixed launch.  The schedule is
+    the same, so every output (decode and prefill) equals the separate
+    launches' bitwise; sampled rows match the oracle.  The tight pool with
+    recompute preemption runs through the mixed launch too."""
+    tr = make_trace(24, seed=9, prompt_median=120.0, prompt_max=600, out_lo=16, out_hi=64,
+                    arrive_over=60)
+    need = [-(-(p + o) // 16) for p, o in zip(tr.prompt, tr.output)]
+    sep, s_sep, r_sep = serve(tr, sum(need) + 16, budget=256, max_running=32, fused_rows=True)
+    mix, s_mix, r_mix = serve(tr, sum(need) + 16, budget=256, max_running=32, fused_rows=True,
+                              mixed=True)
+    log(f"[serve] separate {s_sep}; mixed {s_mix}")
+    assert s_mix["mixed_launches"] >= 10
+    assert r_sep == r_mix and sorted(sep) == sorted(mix)
+    for k in sep:
+        assert sep[k][1] == mix[k][1], k
+        assert np.array_equal(sep[k][0].view(np.uint32), mix[k][0].view(np.uint32)), k
+    tight, s_t, r_t = serve(tr, max(need) + 8, budget=256, max_running=32, seed=1,
+                            fused_rows=True, mixed=True)
+    log(f"[serve] tight mixed {s_t}")
+    assert s_t["preempted"] >= 1 and s_t["mixed_launches"] >= 10
+    for r in range(len(tr.prompt)):
+        assert r_t[r][1] == tr.output[r]
+    rng = np.random.default_rng(5)
+    keys = list(tight)
+    for i in rng.choice(len(keys), size=min(60, len(keys)), replace=False):
+        r, p = keys[int(i)]
+        ref = oracle_row(r, p)
+        got = tight[(r, p)][0].astype(np.float64)
+        ok = np.isclose(got, ref, rtol=RTOL, atol=ATOL)
+        assert ok.all(), ((r, p), tight[(r, p)][1], np.abs(got - ref).max())
