@@ -40,12 +40,13 @@ def rows_kvq_dev(req, pos, width_kv, width_q):
 
 
 def serve(trace, num_blocks, budget, max_running, seed=0, fused_rows=False, swap=False,
-          mixed=False):
+          mixed=False, kv_dtype="fp16"):
     from pagedattention_block_paged_reshape_amd.cache import PagedKVCache
     from pagedattention_block_paged_reshape_amd.serve import ServingLoop
     log(f"[serve] blocks={num_blocks} budget={budget} max_running={max_running}")
     order = np.random.default_rng(seed).permutation(num_blocks).astype(np.int32)
-    cache = PagedKVCache(num_blocks, N_KV, D, order, "cuda:0")
+    cache = PagedKVCache(num_blocks, N_KV, D, order, "cuda:0", kv_dtype=kv_dtype,
+                         k_scale=1.0 / 448, v_scale=1.0 / 448)
     if fused_rows:
         loop = ServingLoop(cache, N_Q, SCALE, budget, max_running, rows_fn=rows_kvq_dev,
                            keep_outputs=True, swap=swap, mixed=mixed)
@@ -175,3 +176,23 @@ def test_serving_with_mixed_launches_matches_separate_launches():
         got = tight[(r, p)][0].astype(np.float64)
         ok = np.isclose(got, ref, rtol=RTOL, atol=ATOL)
         assert ok.all(), ((r, p), tight[(r, p)][1], np.abs(got - ref).max())
+
+
+def test_fp8_serving_with_mixed_launches_matches_separate_launches():
+    """The spread-arrival trace over an FP8 pool (scales 1/448: the rows lie
+    in [-1, 1)): the mixed launches (pa_paged_attention_mixed_fp8) give
+    bitwise the separate FP8 launches' outputs, in a tight pool with
+    recompute preemption."""
+    tr = make_trace(24, seed=9, prompt_median=120.0, prompt_max=600, out_lo=16, out_hi=64,
+                    arrive_over=60)
+    need = [-(-(p + o) // 16) for p, o in zip(tr.prompt, tr.output)]
+    sep, s_sep, r_sep = serve(tr, max(need) + 8, budget=256, max_running=32, seed=2,
+                              fused_rows=True, kv_dtype="fp8")
+    mix, s_mix, r_mix = serve(tr, max(need) + 8, budget=256, max_running=32, seed=2,
+                              fused_rows=True, mixed=True, kv_dtype="fp8")
+    log(f"[serve] fp8 separate {s_sep}; fp8 mixed {s_mix}")
+    assert s_mix["mixed_launches"] >= 10 and s_mix["preempted"] >= 1
+    assert r_sep == r_mix and sorted(sep) == sorted(mix)
+    for k in sep:
+        assert np.isfinite(sep[k][0]).all(), k
+        assert np.array_equal(sep[k][0].view(np.uint32), mix[k][0].view(np.uint32)), k
