@@ -43,6 +43,9 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["pagedattention_block_paged_reshape_amd/csrc/decode_core.h",
                   "pagedattention_block_paged_reshape_amd/csrc/decode.hip",
                   "pagedattention_block_paged_reshape_amd/csrc/pa_device.h"]
+PREFILL_SOURCES = ["pagedattention_block_paged_reshape_amd/csrc/prefill_tile.h",
+                   "pagedattention_block_paged_reshape_amd/csrc/prefill.hip",
+                   "pagedattention_block_paged_reshape_amd/csrc/pa_device.h"]
 TRAFFIC_FILES = {"fp16": os.path.join(PROFILES, "decode_llama3-70b_traffic.md"),
                  "fp8": os.path.join(PROFILES, "decode_llama3-70b_fp8_traffic.md")}
 # FP8 pools: one scale per pool, about max |x| / 448 for the N(0, 1) rows
@@ -53,9 +56,9 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -256,9 +259,12 @@ def bench_serve(args):
     loop.close()
 
 
-def bench_prefill(args):
-    """Causal chunked prefill over the paged cache: the 512-token chunk at
-    offset 49,488 of a 50,000-token prompt (32/8 heads, head_dim 128)."""
+def measure_prefill(args, kv_dtype: str):
+    """Time the causal prefill chunk of workload 5 (512 rows at offset 49,488
+    of a 50,000-token prompt, 32/8 heads, head_dim 128) after the clock
+    warm-up: ``args.prefill_steps`` launches, each bracketed by HIP events on
+    the stream it runs on.  Returns the launch times (ms), the wall time of
+    the timed launches, the algorithmic flops and the workload."""
     import torch
     from synth import make_workload
     from pagedattention_block_paged_reshape_amd.cache import (PagedKVCache, PrefillPlan,
@@ -268,7 +274,7 @@ def bench_prefill(args):
     log("[bench] generating workload 5")
     w = make_workload("5")
     pf = w.prefill
-    cache = PagedKVCache(w.num_blocks, w.n_kv, w.d, w.free_order, dev, kv_dtype=args.kv_dtype,
+    cache = PagedKVCache(w.num_blocks, w.n_kv, w.d, w.free_order, dev, kv_dtype=kv_dtype,
                          k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE)
     dk = torch.from_numpy(w.setup_k).to(dev)
     dv = torch.from_numpy(w.setup_v).to(dev)
@@ -280,12 +286,13 @@ def bench_prefill(args):
     q = torch.from_numpy(pf.q).to(dev)
     stream = torch.cuda.current_stream(dev)
     n_warm = clock_warmup(lambda: plan.run(q, stream), args.warm_ms)
-    log(f"[bench] clock warm-up: {n_warm} launches in ~{args.warm_ms:.0f} ms")
+    log(f"[bench] prefill clock warm-up: {n_warm} launches in ~{args.warm_ms:.0f} ms")
     for _ in range(args.warmup):
         plan.run(q, stream)
     torch.cuda.synchronize()
+    n = args.prefill_steps
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+          for _ in range(n)]
     t0 = time.perf_counter()
     for e in ev:
         e[0].record(stream)
@@ -295,48 +302,71 @@ def bench_prefill(args):
     wall = time.perf_counter() - t0
     ms = np.array([a.elapsed_time(b) for a, b in ev])
     flops = prefill_flops(pf.q_start, pf.chunk_len, w.n_q, w.d)
-    achieved = flops / (ms.mean() * 1e-3) / 1e12
     log(f"[bench] prefill launch mean {ms.mean() * 1e3:.1f} us (p50 {np.median(ms) * 1e3:.1f}); "
-        f"{flops / 1e9:.1f} GFLOP -> {achieved:.1f} TFLOP/s")
+        f"{flops / 1e9:.1f} GFLOP -> {flops / (ms.mean() * 1e-3) / 1e12:.1f} TFLOP/s")
+    del cache, plan, q
+    torch.cuda.empty_cache()
+    return ms, wall, flops, w
+
+
+def prefill_roofline(ms, flops, kv_dtype: str) -> dict:
+    achieved = flops / (ms.mean() * 1e-3) / 1e12
+    fp8 = kv_dtype == "fp8"
+    return {
+        "bound": "mfma",
+        "achieved": round(achieved, 2),
+        "peak": MFMA_F16_PEAK_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+        "traffic": None,
+        "kernel": f"pa_paged_attention_prefill{'_fp8' if fp8 else ''} "
+                  "(prefill_chunk_kernel + prefill_reduce_kernel)",
+        "algorithmic_flops_per_launch": flops,
+        "launch_us_mean": round(float(ms.mean()) * 1e3, 2),
+        "launch_us_p50": round(float(np.median(ms)) * 1e3, 2),
+        "launch_us_p99": round(float(np.percentile(ms, 99)) * 1e3, 2),
+        "kernel_source_sha256": kernel_source_hash(PREFILL_SOURCES),
+    }
+
+
+def prefill_workload_text(w) -> str:
+    pf = w.prefill
+    return (f"config 5 chunk ({w.name}): causal chunk of {pf.chunk_len} query rows at offset "
+            f"{pf.q_start} of a {pf.q_start + pf.chunk_len}-token prompt, {w.n_q}/{w.n_kv} "
+            f"heads, head_dim {w.d}, block 16, pool {w.num_blocks} blocks scattered")
+
+
+def bench_prefill(args):
+    """Causal chunked prefill over the paged cache: the 512-token chunk at
+    offset 49,488 of a 50,000-token prompt (32/8 heads, head_dim 128)."""
+    import torch
+    ms, wall, flops, w = measure_prefill(args, args.kv_dtype)
+    pf = w.prefill
+    n = len(ms)
     result = {
         "metric": "paged prefill chunk attention TFLOP/s (% of fp16 MFMA peak)",
-        "value": round(flops * args.steps / wall / 1e12, 2),
+        "value": round(flops * n / wall / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": n,
         "warmup": args.warmup,
-        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "ms_per_step": round(wall * 1e3 / n, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp16",
         "data": "synthetic",
         "config": {
-            "workload": f"config 5 chunk ({w.name}): causal chunk of {pf.chunk_len} query rows "
-                        f"at offset {pf.q_start} of a {pf.q_start + pf.chunk_len}-token prompt, "
-                        f"{w.n_q}/{w.n_kv} heads, head_dim {w.d}, block 16, pool "
-                        f"{w.num_blocks} blocks scattered",
+            "workload": prefill_workload_text(w),
             "chunk": pf.chunk_len,
             "q_start": pf.q_start,
             "kv_dtype": args.kv_dtype,
             "clock_warmup_ms": args.warm_ms,
         },
-        "roofline": {
-            "bound": "mfma",
-            "achieved": round(achieved, 2),
-            "peak": MFMA_F16_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
-            "traffic": None,
-            "kernel": "pa_paged_attention_prefill (prefill_chunk_kernel + prefill_reduce_kernel)",
-            "algorithmic_flops_per_launch": flops,
-            "launch_us_mean": round(float(ms.mean()) * 1e3, 2),
-            "launch_us_p50": round(float(np.median(ms)) * 1e3, 2),
-        },
+        "roofline": prefill_roofline(ms, flops, args.kv_dtype),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        del cache, plan
         torch.cuda.empty_cache()
         result["cpu_baseline"] = cpu_prefill_baseline(w, args.cpu_budget)
     print(json.dumps(result), flush=True)
@@ -493,6 +523,11 @@ def main():
     ap.add_argument("--copy-calibration-mb", type=int, default=0)
     ap.add_argument("--prefill", action="store_true",
                     help="time the causal prefill chunk of workload 5 instead of decode")
+    ap.add_argument("--prefill-steps", type=int, default=20,
+                    help="timed launches of the prefill chunk (its own line, or the prefill "
+                         "sub-object of the decode line)")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="leave the prefill sub-object out of the decode line")
     ap.add_argument("--mixed", action="store_true",
                     help="time workload 5's decode batch and prefill chunk as one mixed "
                          "launch (and as separate launches) instead of the decode step; "
@@ -643,10 +678,26 @@ def main():
         },
         "cpu_baseline": None,
     }
+    del cache, stepper
+    torch.cuda.empty_cache()
+    if not args.no_prefill:
+        # the chunked-prefill part of the path, on the long-context workload:
+        # compute-bound, so it is reported against the MFMA peak
+        pms, pwall, pflops, pw = measure_prefill(args, args.kv_dtype)
+        result["prefill"] = {
+            "metric": "paged prefill chunk attention TFLOP/s (% of fp16 MFMA peak)",
+            "value": round(pflops * len(pms) / pwall / 1e12, 2),
+            "unit": "TFLOP/s",
+            "steps": len(pms),
+            "workload": prefill_workload_text(pw),
+            "roofline": prefill_roofline(pms, pflops, args.kv_dtype),
+            "cpu_baseline": None,
+        }
     if not args.no_cpu_baseline:
-        del cache, stepper
-        torch.cuda.empty_cache()
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, total_steps, args.kv_dtype)
+        if not args.no_prefill:
+            del w
+            result["prefill"]["cpu_baseline"] = cpu_prefill_baseline(pw, args.cpu_budget)
     print(json.dumps(result), flush=True)
 
 

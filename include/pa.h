@@ -155,9 +155,6 @@ pa_status pa_seq_swap_out(pa_pool* pool, int64_t seq_id, int32_t* blocks, int32_
 pa_status pa_seq_swap_in(pa_pool* pool, int64_t seq_id, int32_t seq_len, int32_t* blocks,
                          int32_t cap, int32_t* n_blocks);
 
-/* Blocks pa_append_slots would take off the free list for the same arguments
- * (new blocks + copy-on-write targets).  Pure. */
-
 /* Prefix caching ([ngrok] "prefix caching": requests that begin with the same
  * tokens share the KV blocks of that prefix; only the same tokens at the same
  * positions count, one differing token ends the sharing, and a block is known
@@ -184,6 +181,9 @@ pa_status pa_seq_add_cached(pa_pool* pool, int64_t seq_id, const int32_t* tokens
                             int32_t n_tokens, int32_t* n_cached);
 pa_status pa_seq_register(pa_pool* pool, int64_t seq_id, const int32_t* tokens,
                           int32_t n_tokens, int32_t* n_registered);
+
+/* Blocks pa_append_slots would take off the free list for the same arguments
+ * (new blocks + copy-on-write targets).  Pure. */
 pa_status pa_can_append(const pa_pool* pool, int32_t n, const int64_t* seq_ids,
                         const int32_t* n_new, int32_t* blocks_needed);
 
@@ -411,12 +411,19 @@ uint64_t pa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t h
  *   computed by one workgroup, which writes the request's output directly if
  *   it has one partition and a partial softmax state otherwise; a second
  *   kernel merges the partitions by log-sum-exp.
+ *   scale: positive and finite (PA_ERR_INVALID otherwise).
  *   work_items / n_items: NULL / 0 launches one workgroup per unit (grid
  *   form).  Otherwise a device copy of the list pa_decode_work_items built
  *   from the same lengths (n_items <= 2^30): then as many workgroups as stay
  *   resident walk it, workgroup y of a kv head taking entries y, 2W-1-y,
- *   2W+y, ... of W such workgroups (work-list form); units the lengths do not
- *   contain are skipped.  Both forms give bitwise the same outputs.
+ *   2W+y, ... of W such workgroups (work-list form); entries naming a
+ *   request >= batch or a partition the lengths do not contain are skipped.
+ *   Both forms give bitwise the same outputs.  In the work-list form the two
+ *   wavefronts of a workgroup hand merge slots to each other through LDS
+ *   with a bounded wait; should a wait ever exceed its bound (it does not
+ *   in a normal run), the workgroup stops and writes NaN to every output
+ *   row (or partial) of the units it had not yet written, so the failure
+ *   shows in the output instead of leaving stale rows.
  *   workspace: device, 16-byte aligned, >= pa_decode_workspace_bytes(...);
  *   may be NULL when that is 0.  Calls sharing a workspace must not overlap.
  *   A table entry outside [0, num_blocks) or a length above max_blocks*16
@@ -510,7 +517,8 @@ uint64_t pa_prefill_workspace_bytes(int32_t chunk_len, int32_t num_q_heads, int3
  * `table` (device int32, >= ceil((q_start+chunk_len)/16) entries); the
  * chunk's own K/V must already be stored (pa_reshape_and_cache).
  *   out: device [chunk_len][n_q][D] fp16; q: device [chunk_len][n_q][D] fp16.
- *   head_dim 64 or 128; n_q/kv_heads <= 16 and divides 128.
+ *   head_dim 64 or 128; n_q/kv_heads <= 16 and divides 128; scale positive
+ *   and finite (PA_ERR_INVALID otherwise).
  *   workspace: device, >= pa_prefill_workspace_bytes(...). */
 pa_status pa_paged_attention_prefill(pa_half* out, const pa_half* q, pa_kv_view kv,
                                      const int32_t* table, int32_t table_len, int32_t q_start,

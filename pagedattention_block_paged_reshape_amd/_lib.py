@@ -16,7 +16,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 PA_DECODE_KEEP_KV = 1  # pa_paged_attention_decode flag: K/V tiles shared between requests
-LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
+# PA_LIBRARY selects another build of the same library (the sanitizer build
+# the CPU tests can run against); by default the in-tree libpagedattn.so
+LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(_HERE, "libpagedattn.so")
 
 PA_OK = 0
 PA_ERR_INVALID = 1

@@ -1,9 +1,21 @@
 """Build the C-ABI shared library (host block manager + gfx950 HIP kernels).
 
-    python pagedattention_block_paged_reshape_amd/build.py
+    python pagedattention_block_paged_reshape_amd/build.py [--sanitize]
 
 compiles every source under csrc/ with hipcc for gfx950 (the host block
 manager with g++) and links ``libpagedattn.so`` next to this file.
+
+``--sanitize`` builds ``libpagedattn_san.so`` instead, for the CPU tests: the
+host sources (block manager, scheduler, work-list planner) compiled by g++
+with AddressSanitizer and UndefinedBehaviorSanitizer, linked with the
+ordinary HIP objects.  Python is not instrumented, so a run preloads the
+sanitizer runtimes and points the binding at this file:
+
+    LD_PRELOAD="$(g++ -print-file-name=libasan.so) $(g++ -print-file-name=libubsan.so)" \
+    ASAN_OPTIONS=detect_leaks=0:halt_on_error=1 \
+    UBSAN_OPTIONS=halt_on_error=1:print_stacktrace=1 \
+    PA_LIBRARY=pagedattention_block_paged_reshape_amd/libpagedattn_san.so \
+    python -m pytest tests -m "not gpu"
 """
 from __future__ import annotations
 
@@ -31,6 +43,11 @@ HIPCC_FLAGS = [
     "-munsafe-fp-atomics",
 ]
 GXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
+# host code only (g++; no HIP source is compiled or linked with these)
+SAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fno-sanitize-recover=all",
+             "-fsanitize=address,undefined"]
+SAN_LIB = os.path.join(PKG, "libpagedattn_san.so")
+ROCM_LIB = "/opt/rocm/lib"
 # Per-file extras: the attention kernels keep their MFMA accumulators in
 # VGPRs, which they rescale with ordinary VALU ops (no AGPR round trips); for
 # the prefill kernel this also fits two wavefronts per SIMD.
@@ -55,31 +72,39 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, sanitize: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     hipcc = _hipcc()
     jobs = []
-    objs = []
+    hip_objs, host_objs = [], []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
-        objs.append(obj)
+        hip_objs.append(obj)
         jobs.append([hipcc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-I", INCLUDE, "-I", CSRC, "-c",
                      os.path.join(CSRC, src), "-o", obj])
     for src in HOST_SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
-        objs.append(obj)
-        jobs.append(["g++", *GXX_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj])
+        obj = os.path.join(BUILD, src + (".san.o" if sanitize else ".o"))
+        host_objs.append(obj)
+        flags = [*GXX_FLAGS, *SAN_FLAGS] if sanitize else GXX_FLAGS
+        jobs.append(["g++", *flags, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         outs = list(ex.map(_run, jobs))
     if verbose:
         for o in outs:
             if o.strip():
                 print(o)
+    if sanitize:
+        tmp = SAN_LIB + ".tmp"
+        link = ["g++", "-shared", "-fPIC", *SAN_FLAGS, "-o", tmp, *host_objs, *hip_objs,
+                "-L", ROCM_LIB, f"-Wl,-rpath,{ROCM_LIB}", "-lamdhip64"]
+        _run(link)
+        os.replace(tmp, SAN_LIB)
+        return SAN_LIB
     tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *hip_objs, *host_objs])
     os.replace(tmp, LIB)
     return LIB
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))

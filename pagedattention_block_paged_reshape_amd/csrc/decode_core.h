@@ -15,7 +15,8 @@
 //
 // Design (MI355X):
 //  * Work unit = (kv head, request, partition of `part_blocks` blocks), done
-//    by one workgroup of 4 wavefronts.  Two launch forms share the code:
+//    by one workgroup of kDecodeWaves (2) wavefronts.  Two launch forms
+//    share the code:
 //      - grid form: one workgroup per unit, grid (kv head, request,
 //        partition), empty units exit at once;
 //      - work-list form (persistent): as many workgroups as stay resident;
@@ -29,18 +30,19 @@
 //  * The G query heads that share a kv head are the 16 columns of a 16x16
 //    MFMA tile (padded when G < 16), so each K/V byte is read once per kv
 //    head, not once per query head.
-//  * Each wavefront takes every 4th block of the unit.  A block's K tile
-//    ([16 tokens][D], 16*D*2 bytes contiguous) is loaded straight into the
-//    MFMA A-operand registers: S^T = K . Q^T gives lane l the scores of 4
-//    tokens for query head l%16.  Those scores, after the online-softmax
-//    update, are already laid out as the B operand of O^T += V^T . P^T, whose
-//    A operand is the V tile ([D][16 tokens] contiguous).  Two register sets
-//    alternate so that one block's loads are in flight while the other is
-//    computed; no LDS round trip in the main loop.
+//  * Each wavefront takes every other block of the unit.  A block's K tile
+//    (16 tokens x D, 16*D*2 bytes contiguous, stored in MFMA operand order)
+//    is loaded straight into the MFMA A-operand registers: S^T = K . Q^T
+//    gives lane l the scores of 4 tokens for query head l%16.  Those scores,
+//    after the online-softmax update, are already laid out as the B operand
+//    of O^T += V^T . P^T, whose A operand is the V tile (also in operand
+//    order).  Two register sets alternate so that one block's loads are in
+//    flight while the other is computed; no LDS round trip in the main loop.
 //  * Softmax runs in fp32 in base 2 (scores pre-multiplied by scale*log2 e);
-//    the per-head running max is reduced across the 4 lane groups with two
-//    xor shuffles, the running sum is kept per lane and reduced at the end.
-//  * The 4 wavefronts merge through LDS with no closing barrier: each posts
+//    the per-head running max is reduced across the 4 lane groups with the
+//    gfx950 row-swap instructions, the running sum is kept per lane and
+//    reduced at the end.
+//  * The wavefronts merge through LDS with no closing barrier: each posts
 //    its state and counts itself in; the last to arrive merges in fixed wave
 //    order (deterministic) and stores.  A request that fits in one partition
 //    gets its fp16 output directly; longer ones store an fp16 normalised
@@ -48,6 +50,8 @@
 #pragma once
 
 #include <math.h>
+
+#include <stdlib.h>
 
 #include <algorithm>
 
@@ -68,7 +72,7 @@ constexpr int kDecodeWaves = PA_DECODE_WAVES;  // wavefronts per workgroup
 constexpr int kDecodeThreads = kDecodeWaves * kWave;
 constexpr int kMergeSlots = PA_MERGE_SLOTS;    // LDS merge slots of the work-list form
 constexpr int kMaxWaveBlocks = 128;            // block ids a wavefront holds (2 per lane)
-constexpr int kSpinLimit = 1 << 22;  // safety bound on the LDS slot wait
+constexpr int kSpinLimit = 1 << 22;  // default bound on the LDS slot wait (s_sleep rounds)
 constexpr size_t kResultRingBytes = 16384;  // LDS for buffered unit results (work-list form)
 
 struct DecodeArgs {
@@ -77,6 +81,8 @@ struct DecodeArgs {
   const f16* vp;
   const int32_t* tables;
   const int32_t* seq_lens;
+  int32_t batch;       // requests in the batch; work entries naming others are skipped
+  int32_t spin_limit;  // bound on the work-list kernel's LDS slot wait
   int32_t max_blocks;
   int32_t num_blocks;
   int32_t n_kv;
@@ -145,6 +151,22 @@ __device__ __forceinline__ Unit no_unit() {
   return u;
 }
 
+// Request b, partition p of a work entry (request << 16 | partition), or
+// false when the entry names no unit of these lengths (request >= batch, or
+// a partition the request does not have).  n_parts: the request's
+// partitions (clamped as make_unit clamps them).
+__device__ __forceinline__ bool entry_unit(const DecodeArgs& a, uint32_t packed, int& b, int& p,
+                                           int& n_parts) {
+  b = static_cast<int>(packed >> 16);
+  p = static_cast<int>(packed & 0xFFFFu);
+  if (b >= a.batch) return false;
+  bool bad = false;
+  const int L = clamp_len(a, b, bad);
+  const int part_tokens = a.part_blocks * kBlock;
+  n_parts = (L + part_tokens - 1) / part_tokens;
+  return L > 0 ? p < n_parts : p == 0;
+}
+
 __device__ __forceinline__ Unit make_unit(const DecodeArgs& a, int b, int p, int wave, int lane) {
   Unit u;
   u.b = b;
@@ -184,6 +206,17 @@ __device__ __forceinline__ Unit make_unit(const DecodeArgs& a, int b, int p, int
   return u;
 }
 
+
+// The unit of a work entry (request << 16 | partition).  An entry naming a
+// request outside the batch (a list built for other lengths) becomes
+// request 0's partition 65535, which no request has: an empty unit that is
+// not stored (the choice is made on the scalars, which costs no registers).
+__device__ __forceinline__ Unit make_entry_unit(const DecodeArgs& a, uint32_t packed, int wave,
+                                                int lane) {
+  const bool in_batch = static_cast<int>(packed >> 16) < a.batch;
+  return make_unit(a, in_batch ? static_cast<int>(packed >> 16) : 0,
+                   in_batch ? static_cast<int>(packed & 0xFFFFu) : 0xFFFF, wave, lane);
+}
 
 // Q^T as the B operand: lane holds query head lane%16 (zero when >= G), dims
 // kk*32 + 8*(lane/16) .. +8.
@@ -458,7 +491,8 @@ struct MergeSlot {
   int* bad;
 };
 
-// Post the wave's state; returns true for the last of the 4 to arrive.
+// Post the wave's state; returns true for the last of the kDecodeWaves
+// wavefronts to arrive.
 template <int D>
 __device__ __forceinline__ bool post_state(const MergeSlot<D>& ms, const WaveState<D>& st, int G,
                                            int wave, int lane, bool bad) {
@@ -787,6 +821,7 @@ void decode_worklist_kernel(DecodeArgs a, const int32_t* __restrict__ items, int
   __shared__ int sm_arrive[kMergeSlots];
   __shared__ int sm_bad[kMergeSlots];
   __shared__ int sm_merged[kMergeSlots];
+  __shared__ int sm_abandon;
   // dynamic LDS: [kMergeSlots][kDecodeWaves][G][D + 4] floats (merge states),
   // then the result ring: [ring] (request, partition, partitions, valid),
   // [ring][G][D] fp16 rows, [ring][G] max, [ring][G] sum
@@ -796,6 +831,7 @@ void decode_worklist_kernel(DecodeArgs a, const int32_t* __restrict__ items, int
     sm_bad[threadIdx.x] = 0;
     sm_merged[threadIdx.x] = 0;
   }
+  if (threadIdx.x == 0) sm_abandon = 0;
   __syncthreads();
   const int slot_floats = kDecodeWaves * G * OROW;
   int4* ring_info = reinterpret_cast<int4*>(reinterpret_cast<float*>(sm_o4) +
@@ -806,9 +842,31 @@ void decode_worklist_kernel(DecodeArgs a, const int32_t* __restrict__ items, int
 
   auto item = [&](int k) { return (k & 1) ? (k + 1) * wph - 1 - y : k * wph + y; };
   auto unit_at = [&](int t) {
-    const uint32_t packed = static_cast<uint32_t>(scalar_load(items, t));
-    return make_unit(a, static_cast<int>(packed >> 16), static_cast<int>(packed & 0xFFFFu), wave,
-                     lane);
+    return make_entry_unit(a, static_cast<uint32_t>(scalar_load(items, t)), wave, lane);
+  };
+  // Give up on this workgroup's remaining work: mark it abandoned for the
+  // other wavefront, then write NaN rows (and NaN max and sum) to the
+  // destination of every unit of the deal from entry index k0 on.  Units
+  // before k0 were flushed; the rest are in the LDS ring or not yet done,
+  // and which of those are whole cannot be told, so all of them read as
+  // bad.  Both wavefronts may do this; they write the same values.
+  auto abandon = [&](int k0) {
+    if (lane == 0)
+      __hip_atomic_store(&sm_abandon, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    const float nan = __builtin_nanf("");
+    const f16 hn = static_cast<f16>(nan);
+    const f16x8 nan8 = {hn, hn, hn, hn, hn, hn, hn, hn};
+    for (int t = k0; item(t) < n_items; ++t) {
+      int b, p, n_parts;
+      if (!entry_unit(a, static_cast<uint32_t>(scalar_load(items, item(t))), b, p, n_parts))
+        continue;
+      for (int idx = lane; idx < G * (D / 8); idx += kWave)
+        store_rows<D>(a, g, b, p, n_parts, idx / (D / 8), (idx % (D / 8)) * 8, nan8, nan, nan);
+    }
+  };
+  auto abandoned = [&]() {
+    return __hip_atomic_load(&sm_abandon, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
   };
   // both wavefronts: write ring slots 0 .. count-1 to their global rows
   auto flush = [&](int count) {
@@ -834,6 +892,7 @@ void decode_worklist_kernel(DecodeArgs a, const int32_t* __restrict__ items, int
   load_q<D>(a, g, u.b, lane, qf);
   if (u.cnt > 0) load_set<D, KEEP, FP8>(a, g, u, no_unit(), 0, true, lane, kA, vA);
 
+  int stop_k0 = 0;  // set when the loop is left early: the window to mark bad
   for (int k = 0;; ++k) {
     const bool more = item(k + 1) < n_items;
     const Unit nx = more ? unit_at(item(k + 1)) : no_unit();
@@ -842,12 +901,24 @@ void decode_worklist_kernel(DecodeArgs a, const int32_t* __restrict__ items, int
     if (more) load_q<D>(a, g, nx.b, lane, qf);  // in flight during the epilogue
 
     const int buf = k % kMergeSlots;
-    // slot `buf` was last used by unit k - kMergeSlots: wait until it has been merged
+    const int k0 = k - k % ring;  // first unit of the ring window not yet flushed
+    // slot `buf` was last used by unit k - kMergeSlots: wait until it has
+    // been merged.  The wait is bounded: past spin_limit rounds (or once the
+    // other wavefront has given up) the rest of the deal is written as NaN
+    // rather than left stale, and the wavefront ends.
     int spins = 0;
+    bool give_up = false;
     while (__hip_atomic_load(&sm_merged[buf], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) !=
            k / kMergeSlots) {
+      if (++spins > a.spin_limit || abandoned()) {
+        give_up = true;
+        break;
+      }
       __builtin_amdgcn_s_sleep(1);
-      if (++spins > kSpinLimit) return;
+    }
+    if (give_up) {
+      stop_k0 = k0;
+      break;
     }
     const MergeSlot<D> ms{sm_m[buf], sm_l[buf],
                           reinterpret_cast<float*>(sm_o4) + buf * slot_floats, &sm_arrive[buf],
@@ -873,13 +944,20 @@ void decode_worklist_kernel(DecodeArgs a, const int32_t* __restrict__ items, int
     }
     if (!more || rs == ring - 1) {
       // every unit in the ring has been merged once both wavefronts get here
+      // (a wavefront that gave up has ended, and the barrier waits only for
+      // the other one, which then writes the window as NaN instead)
       __syncthreads();
+      if (abandoned()) {
+        stop_k0 = k0;
+        break;
+      }
       flush(rs + 1);
       if (!more) return;
       __syncthreads();  // the ring is read out before the next unit reuses slot 0
     }
     u = nx;
   }
+  abandon(stop_k0);
 }
 
 // Both pool types: pools, geometry and (FP8) scales, then the shared checks
@@ -895,6 +973,17 @@ struct PoolArgs {
   float k_scale;
   float v_scale;
 };
+
+// Bound on the work-list kernel's LDS slot wait: kSpinLimit rounds, or the
+// value of the environment variable PA_DECODE_SPIN_LIMIT (>= 0), a test hook
+// that makes the give-up path run without anything hanging.
+inline int32_t decode_spin_limit() {
+  const char* e = getenv("PA_DECODE_SPIN_LIMIT");
+  if (e == nullptr || *e == 0) return kSpinLimit;
+  char* end = nullptr;
+  const long v = strtol(e, &end, 10);
+  return (end != e && v >= 0 && v <= kSpinLimit) ? static_cast<int32_t>(v) : kSpinLimit;
+}
 
 // Host checks of a decode batch's arguments, then its kernel arguments.  PA_OK
 // with batch == 0 means there is nothing to launch.
@@ -915,7 +1004,7 @@ static pa_status decode_prepare(pa_half* out, const pa_half* q, const PoolArgs& 
   if (partition_size <= 0 || partition_size % kBlock != 0 ||
       partition_size > kDecodeWaves * kMaxWaveBlocks * kBlock)
     return PA_ERR_INVALID;
-  if (!(scale == scale)) return PA_ERR_INVALID;
+  if (!scale_ok(scale)) return PA_ERR_INVALID;
   if (kv.fp8 && !(kv.k_scale > 0.0f && kv.k_scale <= 3.0e38f && kv.v_scale > 0.0f &&
                   kv.v_scale <= 3.0e38f))
     return PA_ERR_INVALID;
@@ -942,6 +1031,8 @@ static pa_status decode_prepare(pa_half* out, const pa_half* q, const PoolArgs& 
   a.vp = static_cast<const f16*>(kv.v_pool);
   a.tables = tables;
   a.seq_lens = seq_lens;
+  a.batch = batch;
+  a.spin_limit = decode_spin_limit();
   a.max_blocks = max_blocks;
   a.num_blocks = kv.num_blocks;
   a.n_kv = kv.num_kv_heads;

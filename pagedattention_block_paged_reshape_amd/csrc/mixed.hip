@@ -63,9 +63,7 @@ __global__ __launch_bounds__(kPfThreads) void mixed_step_kernel(PrefillArgs pa, 
   const int g = j % da.n_kv;
   const int t = 2 * (j / da.n_kv) + pair;
   if (t >= n_items) return;
-  const uint32_t packed = static_cast<uint32_t>(scalar_load(items, t));
-  const Unit u = make_unit(da, static_cast<int>(packed >> 16), static_cast<int>(packed & 0xFFFFu),
-                           wave, lane);
+  const Unit u = make_entry_unit(da, static_cast<uint32_t>(scalar_load(items, t)), wave, lane);
   const Unit nx = no_unit();
   typedef TileRegs<D, FP8> TR;
   f16x8 qf[D / 32];

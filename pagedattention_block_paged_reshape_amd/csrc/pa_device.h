@@ -91,4 +91,8 @@ inline pa_status launch_status() {
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Softmax scale accepted by the attention entry points: positive and finite
+// (the kernels take max(s * c) = c * max(s), which needs c > 0).
+inline bool scale_ok(float scale) { return scale > 0.0f && scale <= 3.4028234e38f; }
+
 }  // namespace pa

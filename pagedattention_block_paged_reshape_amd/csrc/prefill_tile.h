@@ -515,7 +515,7 @@ inline pa_status prefill_prepare(pa_half* out, const pa_half* q, const pa_kv_vie
   if (num_q_heads <= 0 || num_q_heads % kv.num_kv_heads != 0) return PA_ERR_INVALID;
   const int G = num_q_heads / kv.num_kv_heads;
   if (G > 16 || kPfMRows % G != 0) return PA_ERR_INVALID;
-  if (!(scale == scale)) return PA_ERR_INVALID;
+  if (!scale_ok(scale)) return PA_ERR_INVALID;
   if (chunk_len == 0) return PA_OK;
   if (static_cast<int64_t>(q_start) + chunk_len > static_cast<int64_t>(table_len) * kBlock)
     return PA_ERR_INVALID;

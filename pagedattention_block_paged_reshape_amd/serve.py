@@ -88,6 +88,16 @@ class ServingLoop:
             setattr(self, attr, ws)
         return ws
 
+    @staticmethod
+    def _hold(stream, *tensors):
+        """The launches only keep raw device addresses: tie each tensor to
+        the stream the kernels run on, so that the caching allocator does not
+        hand its memory out again before that stream's work so far is done
+        (the Python references are dropped when this step returns)."""
+        for t in tensors:
+            if t is not None and t.device.type == "cuda":
+                t.record_stream(stream)
+
     def _h2d(self, a: np.ndarray) -> torch.Tensor:
         """Host array to the device through a pinned staging copy, so the
         copy never waits for the GPU to drain the stream."""
@@ -95,8 +105,14 @@ class ServingLoop:
                                                                          non_blocking=True)
 
     def step(self, stream=None) -> List[int]:
-        """Plan and run one step; returns the requests that finished."""
+        """Plan and run one step; returns the requests that finished.  All of
+        the step's device work (row generation, host-to-device copies,
+        allocations and the library's launches) goes to `stream`."""
         stream = stream or torch.cuda.current_stream(self.dev)
+        with torch.cuda.stream(stream):
+            return self._step(stream)
+
+    def _step(self, stream) -> List[int]:
         plan = L.pa_sched_schedule(self.sched, self.budget, self.max_running)
         items = plan["items"]
         self.stats["preempted"] += len(plan["preempted"])
@@ -129,7 +145,9 @@ class ServingLoop:
             if len(plan["copies"]):
                 d_copies = self._h2d(plan["copies"])
                 self.cache.copy_blocks(d_copies, len(plan["copies"]), stream)
+                self._hold(stream, d_copies)
             self.cache.store(k, v, slots, len(req), stream)
+            self._hold(stream, k, v, slots)
             offs = np.cumsum([0] + [n for _, _, n, _ in items])
             dec = [i for i, it in enumerate(items) if it[3]]
             pre = [i for i, it in enumerate(items) if not it[3]]
@@ -175,10 +193,14 @@ class ServingLoop:
         d_len = self._h2d(ln)
         d_work = self._h2d(work)
         flags = L.PA_DECODE_KEEP_KV if self.cache.shares_blocks() else 0
+        # a contiguous copy of the queries (a slice of the step's fused rows
+        # is not): bound to a name so it outlives every launch that reads it
+        q_c = q.contiguous()
         if chunk is None:
-            self.cache.decode(out, q.contiguous(), d_tab, max_blocks, d_len, len(ids), self.n_q,
+            self.cache.decode(out, q_c, d_tab, max_blocks, d_len, len(ids), self.n_q,
                               self.scale, self.partition, max_len, d_work, len(work), ws,
                               ws_bytes, stream, flags=flags)
+            self._hold(stream, q_c, out, d_tab, d_len, d_work, ws)
         else:
             r, s, n, qc = chunk
             pf_blocks = -(-(s + n) // L.BLOCK_SIZE)
@@ -186,7 +208,7 @@ class ServingLoop:
             assert int(pln[0]) == s + n
             qc = qc.contiguous()
             pout = torch.empty((n, self.n_q, self.d), dtype=torch.float16, device=self.dev)
-            c_dec = L.decode_batch(out, q.contiguous(), d_tab, max_blocks, d_len, len(ids),
+            c_dec = L.decode_batch(out, q_c, d_tab, max_blocks, d_len, len(ids),
                                    self.partition, max_len, d_work, len(work))
             d_ptab = self._h2d(ptab[0])
             c_pf = L.prefill_chunk(pout, qc, d_ptab, pf_blocks, s, n)
@@ -194,13 +216,18 @@ class ServingLoop:
             mws = self._workspace("_ws", max(mws_bytes, 16))
             L.pa_paged_attention_mixed(c_dec, c_pf, self.cache.kv, self.n_q, self.scale, mws,
                                        mws_bytes, stream, flags=flags)
+            self._hold(stream, q_c, out, d_tab, d_len, d_work, qc, pout, d_ptab, mws)
             self.stats["mixed_launches"] += 1
             if self.keep:
+                kept = pout.clone()
                 for j in range(n):
-                    self.outputs[(r, s + j)] = (pout[j], "prefill")
+                    self.outputs[(r, s + j)] = (kept[j], "prefill")
         if self.keep:
+            # copies: the launch buffers go back to the allocator as they would
+            # without keep_outputs
+            kept = out.clone()
             for j, (r, s, _, _) in enumerate(items):
-                self.outputs[(r, s)] = (out[j], "decode")
+                self.outputs[(r, s)] = (kept[j], "decode")
 
     def _prefill(self, r: int, s: int, n: int, q: torch.Tensor, stream):
         max_blocks = -(-(s + n) // L.BLOCK_SIZE)
@@ -210,11 +237,14 @@ class ServingLoop:
         ws = self._workspace("_pws", max(ws_bytes, 16))
         out = torch.empty((n, self.n_q, self.d), dtype=torch.float16, device=self.dev)
         d_tab = self._h2d(tab[0])
-        L.pa_paged_attention_prefill(out, q.contiguous(), self.cache.kv, d_tab, max_blocks, s, n,
+        q_c = q.contiguous()
+        L.pa_paged_attention_prefill(out, q_c, self.cache.kv, d_tab, max_blocks, s, n,
                                      self.n_q, self.scale, ws, ws_bytes, stream)
+        self._hold(stream, q_c, out, d_tab, ws)
         if self.keep:
+            kept = out.clone()
             for j in range(n):
-                self.outputs[(r, s + j)] = (out[j], "prefill")
+                self.outputs[(r, s + j)] = (kept[j], "prefill")
 
     def request(self, req_id: int):
         """(computed input tokens, generated tokens, preemptions)."""

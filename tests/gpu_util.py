@@ -1,6 +1,7 @@
 """Helpers for the GPU parity tests: run a synthetic workload through the C
 ABI on cuda:0, run the same workload through the oracle, compare."""
 import sys
+import time
 
 import numpy as np
 import torch
@@ -60,6 +61,42 @@ def oracle_run(w, kv_dtype="fp16", k_scale=1.0, v_scale=1.0):
     st = run_setup(w, kv_dtype=kv_dtype, k_scale=k_scale, v_scale=v_scale)
     run_step(w, st)
     return st
+
+
+# Full-size workloads and their oracle results, computed once per process:
+# several test modules check the same long-context and Llama-3-70B-shaped
+# configs (callers must not modify what these return).
+_WORKLOADS = {}
+_STATES = {}
+_REFS = {}
+
+
+def shared_workload(cfg):
+    from synth import make_workload
+    key = str(cfg)
+    if key not in _WORKLOADS:
+        _WORKLOADS[key] = make_workload(key)
+    return _WORKLOADS[key]
+
+
+def shared_oracle(cfg, kv_dtype="fp16", k_scale=1.0, v_scale=1.0):
+    key = (str(cfg), kv_dtype, float(k_scale), float(v_scale))
+    if key not in _STATES:
+        _STATES[key] = oracle_run(shared_workload(cfg), kv_dtype, k_scale, v_scale)
+    return _STATES[key]
+
+
+def shared_reference(cfg, part, kv_dtype="fp16", k_scale=1.0, v_scale=1.0):
+    """The oracle's full output of a shared workload: part "decode" (every
+    request, head and dim) or "prefill" (every chunk row, head and dim)."""
+    key = (str(cfg), part, kv_dtype, float(k_scale), float(v_scale))
+    if key not in _REFS:
+        w = shared_workload(cfg)
+        st = shared_oracle(cfg, kv_dtype, k_scale, v_scale)
+        t0 = time.perf_counter()
+        _REFS[key] = decode_reference(w, st) if part == "decode" else prefill_reference(w, st)
+        log(f"[oracle] config {cfg} {part} ({kv_dtype}) in {time.perf_counter() - t0:.1f} s")
+    return _REFS[key]
 
 
 def assert_close(got, ref, what):

@@ -13,6 +13,7 @@ import pytest
 import torch
 
 from gpu_util import (FILL8, assert_close, assert_pools_bit_exact, gpu_run, log, oracle_run,
+                      shared_oracle, shared_reference, shared_workload,
                       pools8_to_logical)
 from oracle import decode_reference, prefill_reference
 from oracle.fp8 import decode_e4m3
@@ -100,18 +101,17 @@ def test_fp8_config_cache_and_decode(cfg):
 
 def test_fp8_config3_full_size_decode():
     """The FP8 decode workload the benchmark times (the Llama-3-70B-shaped
-    batch): every stored code, and every 4th request's outputs (all heads and
-    dims) against the oracle; the grid form, KEEP loads and a second launch
-    give bitwise the same result.  Also logs the distance to the unquantised
-    fp16 result."""
+    batch): every stored code, and every output element (all 256 requests,
+    heads and dims) against the oracle; the grid form, KEEP loads and a second
+    launch give bitwise the same result.  Also logs the distance to the
+    unquantised fp16 result."""
     from pagedattention_block_paged_reshape_amd.cache import DecodePlan
-    w = make_workload(3)
-    st = oracle_run(w, "fp8", K_SCALE, V_SCALE)
+    w = shared_workload(3)
+    st = shared_oracle(3, "fp8", K_SCALE, V_SCALE)
     res = gpu_run(w, partition=512, kv_dtype="fp8", k_scale=K_SCALE, v_scale=V_SCALE)
     n = assert_pools_bit_exact(res["cache"], st)
-    sample = list(range(0, w.batch, 4))
-    ref = decode_reference(w, st, seq_index=sample)
-    err = assert_close(res["decode"][sample], ref, "fp8 config 3 decode (every 4th request)")
+    ref = shared_reference(3, "decode", "fp8", K_SCALE, V_SCALE)
+    err = assert_close(res["decode"], ref, "fp8 config 3 decode (all 256 requests)")
     grid = DecodePlan(res["cache"], w.decode_ids, w.n_q, w.scale, 512, worklist=False)
     keep = DecodePlan(res["cache"], w.decode_ids, w.n_q, w.scale, 512, keep_kv=True)
     g_out = grid.run(res["q"]).clone()
@@ -120,8 +120,7 @@ def test_fp8_config3_full_size_decode():
     torch.cuda.synchronize()
     for other in (g_out, k_out, again):
         assert torch.equal(other.view(torch.int16), res["decode"].view(torch.int16))
-    st16 = oracle_run(w)
-    exact = decode_reference(w, st16, seq_index=range(0, w.batch, 16))
+    exact = decode_reference(w, shared_oracle(3), seq_index=range(0, w.batch, 16))
     got = res["decode"].float().cpu().numpy()[::16]
     log(f"fp8 config 3: {n} live slots code-exact, max err vs oracle {err:.2e}; vs unquantised "
         f"fp16 K/V: max {np.abs(got - exact).max():.3e}, mean {np.abs(got - exact).mean():.3e}")
@@ -196,13 +195,11 @@ def test_fp8_prefill_chunk_parity(decode_lengths, q_start, chunk, n_q, n_kv, d):
 
 def test_fp8_config5_prefill_chunk():
     """The long-context chunk (512 rows at 49,488) over FP8 pools, in the
-    launch the fp16 bench times; sampled rows, all heads."""
-    w = make_workload(5)
-    st = oracle_run(w, kv_dtype="fp8", k_scale=K_SCALE, v_scale=V_SCALE)
+    launch the fp16 bench times; every row, head and dim."""
+    w = shared_workload(5)
     res = gpu_run(w, kv_dtype="fp8", k_scale=K_SCALE, v_scale=V_SCALE, decode=False)
-    rows = [0, 5, 31, 32, 255, 256, 400, 511]
-    err = assert_close(res["prefill"][rows], prefill_reference(w, st, rows=rows),
-                       "fp8 config 5 prefill (sampled rows)")
+    err = assert_close(res["prefill"], shared_reference(5, "prefill", "fp8", K_SCALE, V_SCALE),
+                       "fp8 config 5 prefill (all 512 rows x 32 heads)")
     log(f"fp8 config 5 prefill: max err {err:.2e}")
 
 
@@ -247,20 +244,19 @@ def test_fp8_mixed_equals_separate_launches_and_oracle(decode_lengths, q_start, 
 
 def test_fp8_config5_mixed_launch_and_scale_checks():
     """The long-context step over FP8 pools at full size: bitwise the separate
-    FP8 launches; decode against the oracle in full, prefill on sampled rows.
-    Non-positive or non-finite scales are refused before any launch."""
+    FP8 launches; both outputs against the oracle in full.  Non-positive or
+    non-finite scales are refused before any launch."""
     import pagedattention_block_paged_reshape_amd as pa
     from pagedattention_block_paged_reshape_amd import _lib as L
-    w = make_workload(5)
-    st = oracle_run(w, kv_dtype="fp8", k_scale=K_SCALE, v_scale=V_SCALE)
+    w = shared_workload(5)
     res = gpu_run(w, partition=512, kv_dtype="fp8", k_scale=K_SCALE, v_scale=V_SCALE)
     plan, d_out, p_out = _run_mixed_fp8(w, res)
     assert torch.equal(d_out.view(torch.int16), res["decode"].view(torch.int16))
     assert torch.equal(p_out.view(torch.int16), res["prefill"].view(torch.int16))
-    err = assert_close(d_out, decode_reference(w, st), "fp8 config 5 mixed decode")
-    rows = [0, 31, 32, 383, 384, 511]
-    errp = assert_close(p_out[rows], prefill_reference(w, st, rows=rows),
-                        "fp8 config 5 mixed prefill (sampled rows)")
+    err = assert_close(d_out, shared_reference(5, "decode", "fp8", K_SCALE, V_SCALE),
+                       "fp8 config 5 mixed decode")
+    errp = assert_close(p_out, shared_reference(5, "prefill", "fp8", K_SCALE, V_SCALE),
+                        "fp8 config 5 mixed prefill (all 512 rows x 32 heads)")
     kv = res["cache"].kv
     for ks, vs in [(0.0, 1.0), (1.0, -1.0), (float("inf"), 1.0), (1.0, float("nan"))]:
         bad = L.pa_kv_view_fp8(kv.k_pool, kv.v_pool, kv.num_blocks, kv.block_size,

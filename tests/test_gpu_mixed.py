@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import assert_close, gpu_run, log, oracle_run
+from gpu_util import assert_close, gpu_run, log, oracle_run, shared_reference, shared_workload
 from oracle import decode_reference, prefill_reference
 from synth import make_mixed_workload, make_workload
 
@@ -68,18 +68,16 @@ def test_mixed_equals_separate_launches_and_oracle(decode_lengths, q_start, chun
 def test_config5_mixed_launch():
     """The long-context step at full size: 8 decode requests at 32,768 tokens
     and the 512-row chunk at offset 49,488, in the launch configuration the
-    mixed bench times.  Bitwise equal to the separate launches; decode checked
-    against the oracle in full, prefill on sampled rows."""
-    w = make_workload(5)
-    st = oracle_run(w)
+    mixed bench times.  Bitwise equal to the separate launches; both outputs
+    against the oracle in full (every request, chunk row, head and dim)."""
+    w = shared_workload(5)
     res = gpu_run(w, partition=512)
     plan, d_out, p_out = run_mixed(w, res)
     assert bitwise_equal(d_out, res["decode"])
     assert bitwise_equal(p_out, res["prefill"])
-    err = assert_close(d_out, decode_reference(w, st), "config 5 mixed decode")
-    rows = [0, 7, 31, 32, 200, 383, 384, 508, 511]
-    errp = assert_close(p_out[rows], prefill_reference(w, st, rows=rows),
-                        "config 5 mixed prefill (sampled rows)")
+    err = assert_close(d_out, shared_reference(5, "decode"), "config 5 mixed decode")
+    errp = assert_close(p_out, shared_reference(5, "prefill"),
+                        "config 5 mixed prefill (all 512 rows x 32 heads)")
     # repeated launches on one workspace give the same bits
     q = torch.from_numpy(w.q).to(res["cache"].device)
     qc = torch.from_numpy(w.prefill.q).to(res["cache"].device)

@@ -9,8 +9,8 @@ import pytest
 import torch
 
 from gpu_util import (ATOL, FILL, RTOL, assert_close, assert_pools_bit_exact, gpu_run, log,
-                      pools_to_logical,
-                      oracle_run)
+                      oracle_run, pools_to_logical, shared_oracle, shared_reference,
+                      shared_workload)
 from oracle import decode_attention_one, decode_reference, prefill_reference
 from synth import make_mixed_workload, make_tiny_workload, make_workload
 from synth.workloads import Workload
@@ -48,11 +48,11 @@ def test_config3_full_size_decode():
     """The decode workload the benchmark times (split-K 512 + merge, work-list
     form), every output element against the oracle; the grid form and a
     second launch must give bitwise the same result."""
-    w = make_workload(3)
-    st = oracle_run(w)
+    w = shared_workload(3)
+    st = shared_oracle(3)
     res = gpu_run(w, partition=512)
     n = assert_pools_bit_exact(res["cache"], st)
-    err = assert_close(res["decode"], decode_reference(w, st), "config 3 decode")
+    err = assert_close(res["decode"], shared_reference(3, "decode"), "config 3 decode")
     log(f"config 3: {n} live slots bit-exact, decode max err {err:.2e}")
     from pagedattention_block_paged_reshape_amd.cache import DecodePlan
     grid = DecodePlan(res["cache"], w.decode_ids, w.n_q, w.scale, 512, worklist=False)
@@ -65,16 +65,15 @@ def test_config3_full_size_decode():
 
 def test_config5_mixed_step():
     """8 decode requests at 32,768 tokens (64 partitions each) and the
-    512-token prefill chunk at offset 49,488 over one pool; decode checked in
-    full, prefill on sampled rows and all heads."""
-    w = make_workload(5)
-    st = oracle_run(w)
+    512-token prefill chunk at offset 49,488 over one pool, as two launches;
+    every element of both outputs against the oracle."""
+    w = shared_workload(5)
+    st = shared_oracle(5)
     res = gpu_run(w, partition=512)
     assert_pools_bit_exact(res["cache"], st)
-    err = assert_close(res["decode"], decode_reference(w, st), "config 5 decode")
-    rows = [0, 1, 15, 16, 127, 128, 255, 300, 447, 510, 511]
-    ref = prefill_reference(w, st, rows=rows)
-    errp = assert_close(res["prefill"][rows], ref, "config 5 prefill (sampled rows)")
+    err = assert_close(res["decode"], shared_reference(5, "decode"), "config 5 decode")
+    errp = assert_close(res["prefill"], shared_reference(5, "prefill"),
+                        "config 5 prefill (all 512 rows x 32 heads)")
     log(f"config 5: decode max err {err:.2e}, prefill max err {errp:.2e}")
 
 
@@ -347,3 +346,63 @@ def test_decode_empty_batch_is_a_noop():
                                  plan.workspace, plan.ws_bytes)
     torch.cuda.synchronize()
     assert (sentinel.float() == 3.0).all()
+
+
+@pytest.mark.parametrize("worklist_extra", ["other requests", "other partitions"])
+def test_decode_work_list_entries_outside_the_batch_are_skipped(worklist_extra):
+    """A work list built for other lengths (two requests the batch does not
+    have, or longer requests with partitions the batch lacks) runs its extra
+    entries as empty units: the outputs are bitwise those of the batch's own
+    list, and no row outside the batch is written."""
+    import pagedattention_block_paged_reshape_amd as pa
+    w = make_tiny_workload([40, 700, 1300], n_q=16, n_kv=4, d=128, seed=61, dist="normal")
+    res = gpu_run(w, partition=256)
+    plan, good = res["plan"], res["decode"]
+    lens = plan.lens.cpu().numpy().tolist()
+    other = lens + [3000, 2500] if worklist_extra == "other requests" else [x + 900 for x in lens]
+    items = pa.pa_decode_work_items(other, 256)
+    assert len(items) > plan.n_items
+    plan.items = torch.from_numpy(items.copy()).to("cuda:0")
+    plan.n_items = len(items)
+    # the output has room for two more requests, which must stay untouched
+    big = torch.full((w.batch + 2, w.n_q, w.d), 5.0, dtype=torch.float16, device="cuda:0")
+    plan.out = big[:w.batch]
+    plan.run(res["q"])
+    torch.cuda.synchronize()
+    assert torch.equal(big[:w.batch].view(torch.int16), good.view(torch.int16))
+    assert (big[w.batch:].float() == 5.0).all()
+
+
+@pytest.mark.parametrize("case", ["config 2", "ragged, partition 32"])
+def test_decode_worklist_give_up_writes_nan_not_stale_rows(case, monkeypatch):
+    """The work-list kernel's LDS slot wait is bounded.  With the bound
+    forced to 0 rounds from the host (a test hook; every wait still ends),
+    a wavefront that finds a slot still busy gives up and the rest of its
+    workgroup's units must come out NaN: every output row is either NaN or
+    bitwise the normal run's, and the launch completes."""
+    from pagedattention_block_paged_reshape_amd.cache import DecodePlan
+    if case == "config 2":
+        w, part = make_workload(2), 512
+    else:
+        w, part = make_tiny_workload(RAGGED * 3, n_q=32, n_kv=8, d=128, seed=71,
+                                     dist="normal"), 32
+    res = gpu_run(w, partition=part)
+    good = res["decode"].float().cpu().numpy()
+    plan = DecodePlan(res["cache"], w.decode_ids, w.n_q, w.scale, part)
+    plan.out.fill_(3.0)                     # stale contents the give-up must not leave
+    plan.workspace.fill_(0)
+    monkeypatch.setenv("PA_DECODE_SPIN_LIMIT", "0")
+    nan_rows = 0
+    for rep in range(5):
+        out = plan.run(res["q"]).clone()
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy()
+        is_nan = np.isnan(got).all(axis=-1)
+        same = (got.view(np.uint32) == good.view(np.uint32)).all(axis=-1)
+        assert (is_nan | same).all(), f"{case}: a row is neither NaN nor the normal result"
+        nan_rows += int(is_nan.sum())
+    monkeypatch.delenv("PA_DECODE_SPIN_LIMIT")
+    again = plan.run(res["q"]).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(again.view(torch.int16), res["decode"].view(torch.int16))
+    log(f"give-up ({case}): {nan_rows} of {5 * good.shape[0] * good.shape[1]} rows NaN over 5 runs")

@@ -40,7 +40,7 @@ def rows_kvq_dev(req, pos, width_kv, width_q):
 
 
 def serve(trace, num_blocks, budget, max_running, seed=0, fused_rows=False, swap=False,
-          mixed=False, kv_dtype="fp16"):
+          mixed=False, kv_dtype="fp16", side_stream=False):
     from pagedattention_block_paged_reshape_amd.cache import PagedKVCache
     from pagedattention_block_paged_reshape_amd.serve import ServingLoop
     log(f"[serve] blocks={num_blocks} budget={budget} max_running={max_running}")
@@ -53,12 +53,13 @@ def serve(trace, num_blocks, budget, max_running, seed=0, fused_rows=False, swap
     else:
         loop = ServingLoop(cache, N_Q, SCALE, budget, max_running, row_fn=rows_dev,
                            keep_outputs=True, mixed=mixed)
+    stream = torch.cuda.Stream() if side_stream else None   # default priority
     nxt = 0
     for step in range(20000):
         while nxt < len(trace.prompt) and trace.arrival[nxt] <= step:
             loop.add(nxt, trace.prompt[nxt], trace.output[nxt])
             nxt += 1
-        loop.step()
+        loop.step(stream)
         st = loop.sched_stats()
         if (nxt == len(trace.prompt) and st["n_waiting"] == 0 and st["n_running"] == 0
                 and st["n_swapped"] == 0):
@@ -196,3 +197,26 @@ def test_fp8_serving_with_mixed_launches_matches_separate_launches():
     for k in sep:
         assert np.isfinite(sep[k][0]).all(), k
         assert np.array_equal(sep[k][0].view(np.uint32), mix[k][0].view(np.uint32)), k
+
+
+def test_mixed_serving_on_a_side_stream_equals_the_default_stream():
+    """Regression for launch operands freed too early: the mixed launch gets
+    raw addresses of the step's contiguous queries, tables and work list.
+    Kept outputs are copies, so the step's buffers go back to the caching
+    allocator each step and are handed out again at once; run on a stream
+    other than the current one, where the step's own allocations, copies and
+    launches must still be ordered.  Every output must equal the
+    default-stream run's bitwise."""
+    tr = make_trace(24, seed=9, prompt_median=120.0, prompt_max=600, out_lo=16, out_hi=64,
+                    arrive_over=60)
+    need = [-(-(p + o) // 16) for p, o in zip(tr.prompt, tr.output)]
+    base, s_base, r_base = serve(tr, max(need) + 8, budget=256, max_running=32, seed=3,
+                                 fused_rows=True, mixed=True)
+    side, s_side, r_side = serve(tr, max(need) + 8, budget=256, max_running=32, seed=3,
+                                 fused_rows=True, mixed=True, side_stream=True)
+    log(f"[serve] default stream {s_base}; side stream {s_side}")
+    assert s_side["mixed_launches"] >= 10 and s_side["preempted"] >= 1
+    assert r_base == r_side and sorted(base) == sorted(side)
+    for k in base:
+        assert np.isfinite(base[k][0]).all(), k
+        assert np.array_equal(base[k][0].view(np.uint32), side[k][0].view(np.uint32)), k

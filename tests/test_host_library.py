@@ -386,6 +386,40 @@ def test_decode_rejects_unknown_flags_before_any_launch():
     pa.pa_paged_attention_decode(**args, flags=0)
 
 
+def test_attention_calls_reject_bad_scales_before_any_launch():
+    """The softmax scale must be positive and finite for decode, prefill and
+    the mixed launch (the kernels take max(c * s) = c * max(s)); the check
+    comes before the early returns of empty calls.  Dummy addresses, never
+    dereferenced."""
+    kv = pa.kv_view(None, None, 64, 8, 128)
+    kv.k_pool = kv.v_pool = 1 << 20
+    dec = pa.decode_batch(1 << 21, 1 << 22, 1 << 23, 256, 1 << 24, 4, 512, 4096, 1 << 25, 32)
+    pf = pa.prefill_chunk(1 << 26, 1 << 27, 1 << 28, 3125, 49488, 512)
+    empty_dec = pa.decode_batch(1 << 21, 1 << 22, 1 << 23, 256, 1 << 24, 0, 512, 4096, None, 0)
+    empty_pf = pa.prefill_chunk(1 << 26, 1 << 27, 1 << 28, 3125, 49488, 0)
+    big = 1 << 40
+    for scale in (0.0, -0.088, float("inf"), float("-inf"), float("nan")):
+        for batch in (4, 0):
+            with pytest.raises(pa.PaError):
+                pa.pa_paged_attention_decode(1 << 21, 1 << 22, kv, 1 << 23, 256, 1 << 24, batch,
+                                             32, scale, 512, 4096, 1 << 25, 32, 1 << 29, big)
+        for chunk in (512, 0):
+            with pytest.raises(pa.PaError):
+                pa.pa_paged_attention_prefill(1 << 26, 1 << 27, kv, 1 << 28, 3125, 49488, chunk,
+                                              32, scale, 1 << 29, big)
+        for d, p in ((dec, pf), (empty_dec, empty_pf)):
+            with pytest.raises(pa.PaError):
+                pa.pa_paged_attention_mixed(d, p, kv, 32, scale, 1 << 29, big)
+    # the smallest positive and the largest finite scale are accepted (empty
+    # calls: nothing is launched)
+    for scale in (1e-30, 3.4028234e38):
+        pa.pa_paged_attention_decode(1 << 21, 1 << 22, kv, 1 << 23, 256, 1 << 24, 0, 32, scale,
+                                     512, 4096, None, 0, None, 0)
+        pa.pa_paged_attention_prefill(1 << 26, 1 << 27, kv, 1 << 28, 3125, 49488, 0, 32, scale,
+                                      None, 0)
+        pa.pa_paged_attention_mixed(empty_dec, empty_pf, kv, 32, scale, None, 0)
+
+
 def test_mixed_checks_run_before_any_launch():
     # dummy addresses, never dereferenced: every call below fails or returns
     # on the host
