@@ -443,6 +443,33 @@ pa_status pa_paged_attention_decode(pa_half* out, const pa_half* q, pa_kv_view k
                                     void* workspace, uint64_t workspace_bytes, uint32_t flags,
                                     void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * pa_paged_attention_decode with the partials kept in a scratch array that
+ * the library's code object holds on each GPU, PA_DECODE_SCRATCH_BYTES
+ * (64 MiB) per GPU, held until the process ends.  Same arguments, outputs
+ * (bitwise) and checks as pa_paged_attention_decode, without workspace.
+ *   - Calls no hipMalloc / hipFree or other allocating routine.  The first
+ *     call on a device looks the array's address up (hipGetSymbolAddress)
+ *     with that device current; `stream` (NULL = the null stream) must
+ *     belong to the current device (PA_ERR_INVALID otherwise).
+ *   - PA_ERR_CAPACITY, before anything else, when the partials
+ *     (pa_decode_workspace_bytes of the same arguments) exceed
+ *     PA_DECODE_SCRATCH_BYTES: e.g. 256 requests x 64 query heads at
+ *     head_dim 128 fit up to 7,680 tokens with 512-token partitions.
+ *   - Every call on one GPU uses the same array, and nothing in it needs
+ *     to start at zero (each partial is written before it is read).  Two
+ *     calls in flight on one GPU at once (e.g. on different streams) race
+ *     on it: the caller orders them. */
+#define PA_DECODE_SCRATCH_BYTES (64ull << 20)
+pa_status pa_paged_attention_decode_noalloc(pa_half* out, const pa_half* q, pa_kv_view kv,
+                                            const int32_t* tables, int32_t max_blocks,
+                                            const int32_t* seq_lens, int32_t batch,
+                                            int32_t num_q_heads, float scale,
+                                            int32_t partition_size, int32_t max_seq_len,
+                                            const int32_t* work_items, int32_t n_items,
+                                            uint32_t flags, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* FP8 KV cache                                                              */
 /* ------------------------------------------------------------------------ */

@@ -16,6 +16,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 PA_DECODE_KEEP_KV = 1  # pa_paged_attention_decode flag: K/V tiles shared between requests
+PA_DECODE_SCRATCH_BYTES = 64 << 20  # partials pa_paged_attention_decode_noalloc can hold
 # PA_LIBRARY selects another build of the same library (the sanitizer build
 # the CPU tests can run against); by default the in-tree libpagedattn.so
 LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(_HERE, "libpagedattn.so")
@@ -137,6 +138,9 @@ _SIGS = {
     "pa_paged_attention_decode": (C.c_int, [_P, _P, pa_kv_view, _P, _I32, _P, _I32, _I32,
                                             C.c_float, _I32, _I32, _P, _I32, _P, _U64, C.c_uint32,
                                             _P]),
+    "pa_paged_attention_decode_noalloc": (C.c_int, [_P, _P, pa_kv_view, _P, _I32, _P, _I32,
+                                                    _I32, C.c_float, _I32, _I32, _P, _I32,
+                                                    C.c_uint32, _P]),
     "pa_reshape_and_cache_fp8": (C.c_int, [_P, _P, _P, _I32, pa_kv_view_fp8, _P]),
     "pa_copy_blocks_fp8": (C.c_int, [_P, _I32, pa_kv_view_fp8, _P]),
     "pa_paged_attention_decode_fp8": (C.c_int, [_P, _P, pa_kv_view_fp8, _P, _I32, _P, _I32, _I32,
@@ -506,6 +510,17 @@ def pa_paged_attention_decode(out, q, kv: pa_kv_view, tables, max_blocks: int, s
                                          _dptr(work_items), int(n_items), _dptr(workspace),
                                          int(workspace_bytes), int(flags), _stream(stream)),
            "pa_paged_attention_decode")
+
+
+def pa_paged_attention_decode_noalloc(out, q, kv: pa_kv_view, tables, max_blocks: int, seq_lens,
+                                      batch: int, num_q_heads: int, scale: float,
+                                      partition_size: int, max_seq_len: int, work_items,
+                                      n_items: int, stream=None, flags: int = 0) -> None:
+    _check(LIB.pa_paged_attention_decode_noalloc(
+        _dptr(out), _dptr(q), kv, _dptr(tables), int(max_blocks), _dptr(seq_lens), int(batch),
+        int(num_q_heads), float(scale), int(partition_size), int(max_seq_len),
+        _dptr(work_items), int(n_items), int(flags), _stream(stream)),
+        "pa_paged_attention_decode_noalloc")
 
 
 def pa_paged_attention_decode_fp8(out, q, kv: pa_kv_view_fp8, tables, max_blocks: int, seq_lens,

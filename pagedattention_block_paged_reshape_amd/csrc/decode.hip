@@ -1,10 +1,42 @@
 // Paged decode attention on gfx950: the decode launch and its C entry points.
 // The kernels and their design are in decode_core.h.
 #include <algorithm>
+#include <mutex>
 
 #include "decode_core.h"
 
+// Partials of pa_paged_attention_decode_noalloc, for callers that cannot
+// allocate: a device array of the library's code object, one per GPU,
+// created when the code is loaded on that GPU and held until the process
+// ends.  Host code never uses this name as an address (on the host it is a
+// stand-in, not device memory); it uses the address hipGetSymbolAddress
+// gives for each device.
+static __device__ __align__(256) unsigned char scratch[PA_DECODE_SCRATCH_BYTES];
+
 namespace pa {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device, once looked up
+}  // namespace
+
+// The scratch array's device address on the current device (looked up on
+// the first call for that device, with it current).
+static pa_status scratch_on_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return PA_ERR_INVALID;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return PA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PA_OK;
+}
 
 // The kernels of one (head_dim, KEEP, FP8) choice.
 struct DecodeKernels {
@@ -144,4 +176,34 @@ extern "C" pa_status pa_paged_attention_decode_fp8(
   return decode_launch(out, q, pk, tables, max_blocks, seq_lens, batch, num_q_heads, scale,
                        partition_size, max_seq_len, work_items, n_items, workspace,
                        workspace_bytes, flags, stream);
+}
+
+extern "C" pa_status pa_paged_attention_decode_noalloc(
+    pa_half* out, const pa_half* q, pa_kv_view kv, const int32_t* tables, int32_t max_blocks,
+    const int32_t* seq_lens, int32_t batch, int32_t num_q_heads, float scale,
+    int32_t partition_size, int32_t max_seq_len, const int32_t* work_items, int32_t n_items,
+    uint32_t flags, void* stream) {
+  // the partials must fit the scratch array: refused before anything else
+  const uint64_t need = pa_decode_workspace_bytes(batch, num_q_heads, kv.head_dim, max_seq_len,
+                                                  partition_size);
+  if (need > PA_DECODE_SCRATCH_BYTES) return PA_ERR_CAPACITY;
+  // the launch goes to the stream's device, which must be the current one
+  // (the scratch address is per device)
+  if (stream != nullptr) {
+    int cur = 0;
+    hipDevice_t sdev = 0;
+    if (hipGetDevice(&cur) != hipSuccess ||
+        hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess)
+      return PA_ERR_HIP;
+    if (sdev != cur) return PA_ERR_INVALID;
+  }
+  void* ws = nullptr;
+  if (need > 0) {
+    const pa_status st = scratch_on_current_device(&ws);
+    if (st != PA_OK) return st;
+  }
+  const PoolArgs pk{kv.k_pool, kv.v_pool, kv.num_blocks, kv.block_size, kv.num_kv_heads,
+                    kv.head_dim, false, 1.0f, 1.0f};
+  return decode_launch(out, q, pk, tables, max_blocks, seq_lens, batch, num_q_heads, scale,
+                       partition_size, max_seq_len, work_items, n_items, ws, need, flags, stream);
 }
