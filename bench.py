@@ -320,7 +320,8 @@ def prefill_roofline(ms, flops, kv_dtype: str) -> dict:
         "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
         "traffic": None,
         "kernel": f"pa_paged_attention_prefill{'_fp8' if fp8 else ''} "
-                  "(prefill_chunk_kernel + prefill_reduce_kernel)",
+                  f"({'prefill_chunk_kernel' if fp8 else 'prefill_chunk_pp_kernel'} + "
+                  "prefill_reduce_kernel)",
         "algorithmic_flops_per_launch": flops,
         "launch_us_mean": round(float(ms.mean()) * 1e3, 2),
         "launch_us_p50": round(float(np.median(ms)) * 1e3, 2),

@@ -12,17 +12,21 @@
 // compute-bound).
 //
 // Design (MI355X):
-//  * Workgroup = 4 wavefronts over 128 "M-rows" = (128/G query rows) x (G
-//    query heads of one kv head); wavefront w owns M-rows 32w..32w+31 as two
-//    16-wide MFMA tiles.  Grid = (kv head, query tile, key split);
-//    blockIdx.x = kv head puts each head on one XCD so that every query tile
-//    and split of that head shares one L2 for the same K/V blocks.
-//  * Keys advance 64 at a time (4 blocks).  The 4 K tiles and 4 V tiles are
-//    gathered through the table with lane-contiguous 16-byte loads into
-//    registers one step ahead, then stored to LDS in logical order (K as
-//    [key][D], V^T as [D][key] with each 32-key half in the score
-//    accumulators' key order, rows padded so the MFMA operand reads are
-//    bank-conflict free) and shared by the 4 wavefronts.
+//  * "M-rows" = query rows x the G query heads of one kv head; a wavefront
+//    owns 32 M-rows as two 16-wide MFMA tiles.  Grid = (kv head, query tile,
+//    key split); blockIdx.x = kv head puts each head on one XCD so that every
+//    query tile and split of that head shares one L2 for the same K/V blocks.
+//  * Keys advance 64 at a time (4 blocks).  fp16 pools (prefill_tile_pp): 8
+//    wavefronts over 256 M-rows, in two groups that alternate between matrix
+//    products and softmax at every phase (ping-pong), so that each SIMD's
+//    matrix core is fed by one group while the other computes its
+//    exponentials; the 4 K and 4 V tiles of a step are copied from HBM
+//    straight into LDS (global -> LDS loads) in the pool's tile order, two
+//    phases ahead of their first reader.  FP8 pools (prefill_tile): 4
+//    wavefronts over 128 M-rows; the tiles are gathered into registers one
+//    step ahead, converted, and stored to LDS in logical order (K as [key][D],
+//    V^T as [D][key] in the score accumulators' key order, rows padded so the
+//    MFMA operand reads are bank-conflict free).
 //  * S^T = K . Q^T (keys x M-rows, 16x16x32 f16 MFMA); online softmax in fp32
 //    base 2 per M-row; P^T goes straight from the score accumulators into the
 //    B operand of O^T += V^T . P^T.  Only the steps that cross the causal
@@ -46,6 +50,13 @@ template <int D, bool FP8>
 __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a) {
   __shared__ PrefillLds<D> lds;
   prefill_tile<D, kPfPrio, FP8>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds);
+}
+
+// fp16 pools: the ping-pong tile, one 8-wavefront workgroup per 256 M-rows.
+template <int D>
+__global__ __launch_bounds__(kPfPPThreads) void prefill_chunk_pp_kernel(PrefillArgs a) {
+  __shared__ PrefillLdsPP<D> lds;
+  prefill_tile_pp<D>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds);
 }
 
 // Merge the key splits of each (row, head) by log-sum-exp.
@@ -89,16 +100,19 @@ static pa_status prefill_launch(pa_half* out, const pa_half* q, const pa_kv_view
   float* ws_l = a.ws_l;
   f16* oo = a.out;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // the fp16 tile covers 256 M-rows: half as many query tiles
+  dim3 grid_pp = grid;
+  grid_pp.y = static_cast<uint32_t>((chunk_len + kPfPPMRows / a.G - 1) / (kPfPPMRows / a.G));
   if (D == 128) {
     if (fp8)
       prefill_chunk_kernel<128, true><<<grid, dim3(kPfThreads), 0, s>>>(a);
     else
-      prefill_chunk_kernel<128, false><<<grid, dim3(kPfThreads), 0, s>>>(a);
+      prefill_chunk_pp_kernel<128><<<grid_pp, dim3(kPfPPThreads), 0, s>>>(a);
   } else {
     if (fp8)
       prefill_chunk_kernel<64, true><<<grid, dim3(kPfThreads), 0, s>>>(a);
     else
-      prefill_chunk_kernel<64, false><<<grid, dim3(kPfThreads), 0, s>>>(a);
+      prefill_chunk_pp_kernel<64><<<grid_pp, dim3(kPfPPThreads), 0, s>>>(a);
   }
   if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   if (splits > 1) {
