@@ -3,55 +3,70 @@
 // Mixed step: the decode units of a batch and the tiles of one prefill chunk
 // in one launch over one pool (a scheduler step runs both kinds of work in
 // one forward pass: ta-paperlens "scheduler skeleton"; techfeed.io ngrok
-// summary, "the scheduler").  Workgroups of 4 wavefronts; the first pf_wgs
-// take prefill tiles (kv head fastest, then query tile, then key split, as
-// the prefill launch's grid), the rest decode units, two per workgroup, one
-// per wavefront pair, each as in the grid form.  The prefill tiles, being the
+// summary, "the scheduler").  Workgroups of the prefill launch's size (8
+// wavefronts with fp16 pools, 4 with FP8 ones); the first pf_wgs take prefill
+// tiles (kv head fastest, then query tile, then key split, as the prefill
+// launch's grid), the rest decode units, one per wavefront pair (so 4 or 2
+// per workgroup), each as in the grid form.  The prefill tiles, being the
 // long work, start first; decode units fill the CUs as tiles retire, so the
 // chunk's ragged end and the launch gap between the two kinds of work
 // overlap with memory-bound decode.  Decode unit t of kv head g is entry t
-// of the work list; the workgroup that holds entries 2j and 2j+1 of kv head g
-// is number pf_wgs + j*n_kv + g, so with 8 kv heads and pf_wgs a multiple of 8
-// each head's decode units land on one XCD, as in the decode launch.
+// of the work list; the workgroup that holds entries P*j .. P*j + P - 1 of kv
+// head g (P pairs) is number pf_wgs + j*n_kv + g, so with 8 kv heads and
+// pf_wgs a multiple of 8 each head's decode units land on one XCD, as in the
+// decode launch.
+#include <type_traits>
+
 #include "decode_core.h"
 #include "prefill_tile.h"
 
 namespace pa {
 
-// LDS of a mixed workgroup: one prefill tile's, or two decode units' merge
+// Threads of a mixed workgroup: the prefill launch's workgroup size.
+template <bool FP8>
+constexpr int mixed_threads() {
+  return FP8 ? kPfThreads : kPfPPThreads;
+}
+
+// LDS of a mixed workgroup: one prefill tile's, or P decode units' merge
 // states ([pair][wave][16] max and sum, [pair][wave][G <= 16][D + 4] O^T rows).
-template <int D>
+template <int D, int P>
 struct MixedDecodeLds {
-  __attribute__((aligned(16))) float o[2][kDecodeWaves * 16 * (D + 4)];
-  float m[2][kDecodeWaves * 16];
-  float l[2][kDecodeWaves * 16];
-  int arrive[2];
-  int bad[2];
+  __attribute__((aligned(16))) float o[P][kDecodeWaves * 16 * (D + 4)];
+  float m[P][kDecodeWaves * 16];
+  float l[P][kDecodeWaves * 16];
+  int arrive[P];
+  int bad[P];
 };
 
-template <int D>
+template <int D, bool FP8>
 union MixedLds {
-  PrefillLds<D> pf;
-  MixedDecodeLds<D> dec;
+  static constexpr int P = mixed_threads<FP8>() / (kDecodeWaves * kWave);  // decode units
+  typename std::conditional<FP8, PrefillLds<D>, PrefillLdsPP<D>>::type pf;
+  MixedDecodeLds<D, P> dec;
 };
 
 template <int D, bool KEEP, bool FP8>
-__global__ __launch_bounds__(kPfThreads) void mixed_step_kernel(PrefillArgs pa, int32_t pf_wgs,
-                                                                 int32_t pf_qtiles, DecodeArgs da,
-                                                                 const int32_t* __restrict__ items,
-                                                                 int32_t n_items) {
-  __shared__ MixedLds<D> lds;
+__global__ __launch_bounds__(mixed_threads<FP8>()) void mixed_step_kernel(
+    PrefillArgs pa, int32_t pf_wgs, int32_t pf_qtiles, DecodeArgs da,
+    const int32_t* __restrict__ items, int32_t n_items) {
+  __shared__ MixedLds<D, FP8> lds;
+  constexpr int P = MixedLds<D, FP8>::P;
   const int wg = blockIdx.x;
   if (wg < pf_wgs) {
     const int rest = wg / pa.n_kv;
-    // no raised wave priority here, unlike the prefill launch: tiles that
-    // share CUs with decode units starved them (measured on the
+    // FP8: no raised wave priority here, unlike the prefill launch: tiles
+    // that share CUs with decode units starved them (measured on the
     // long-context step: 650 us with the prefill launch's priorities, also
-    // when decode units ran at a higher priority, vs 607 us without)
-    prefill_tile<D, 0, FP8>(pa, wg % pa.n_kv, rest % pf_qtiles, rest / pf_qtiles, lds.pf);
+    // when decode units ran at a higher priority, vs 607 us without).  The
+    // fp16 tile fills its CU alone (two wavefronts per SIMD at ~211 VGPRs).
+    if constexpr (FP8)
+      prefill_tile<D, 0, FP8>(pa, wg % pa.n_kv, rest % pf_qtiles, rest / pf_qtiles, lds.pf);
+    else
+      prefill_tile_pp<D>(pa, wg % pa.n_kv, rest % pf_qtiles, rest / pf_qtiles, lds.pf);
     return;
   }
-  if (threadIdx.x < 2) {
+  if (threadIdx.x < P) {
     lds.dec.arrive[threadIdx.x] = 0;
     lds.dec.bad[threadIdx.x] = 0;
   }
@@ -61,7 +76,7 @@ __global__ __launch_bounds__(kPfThreads) void mixed_step_kernel(PrefillArgs pa, 
   const int wave = uniform((threadIdx.x >> 6) & 1);
   const int lane = threadIdx.x & 63;
   const int g = j % da.n_kv;
-  const int t = 2 * (j / da.n_kv) + pair;
+  const int t = P * (j / da.n_kv) + pair;
   if (t >= n_items) return;
   const Unit u = make_entry_unit(da, static_cast<uint32_t>(scalar_load(items, t)), wave, lane);
   const Unit nx = no_unit();
@@ -111,12 +126,13 @@ template <bool KEEP, bool FP8>
 static void launch_step(int D, dim3 grid, hipStream_t s, const PrefillArgs& pa, int32_t pf_wgs,
                         int32_t qtiles, const DecodeArgs& da, const int32_t* items,
                         int32_t n_items) {
+  const dim3 block(mixed_threads<FP8>());
   if (D == 128)
-    mixed_step_kernel<128, KEEP, FP8><<<grid, dim3(kPfThreads), 0, s>>>(pa, pf_wgs, qtiles, da,
-                                                                         items, n_items);
+    mixed_step_kernel<128, KEEP, FP8><<<grid, block, 0, s>>>(pa, pf_wgs, qtiles, da, items,
+                                                             n_items);
   else
-    mixed_step_kernel<64, KEEP, FP8><<<grid, dim3(kPfThreads), 0, s>>>(pa, pf_wgs, qtiles, da,
-                                                                        items, n_items);
+    mixed_step_kernel<64, KEEP, FP8><<<grid, block, 0, s>>>(pa, pf_wgs, qtiles, da, items,
+                                                            n_items);
 }
 
 // Both pool types: k_pool / v_pool hold fp16 values or (fp8) E4M3 codes with
@@ -155,10 +171,15 @@ static pa_status mixed_launch(const pa_decode_batch* dec, const pa_prefill_chunk
     pa.scale_log2 *= k_scale;
     pa.v_scale = v_scale;
   }
+  // fp16: the prefill launch's 256-M-row tiles (half as many query tiles)
+  if (!fp8 && pf->chunk_len > 0)
+    pgrid.y = static_cast<uint32_t>((pf->chunk_len + kPfPPMRows / pa.G - 1) / (kPfPPMRows / pa.G));
   const int64_t pf_wgs =
       pf->chunk_len > 0 ? static_cast<int64_t>(pgrid.x) * pgrid.y * pgrid.z : 0;
+  // decode units per workgroup: one per wavefront pair
+  const int P = (fp8 ? mixed_threads<true>() : mixed_threads<false>()) / (kDecodeWaves * kWave);
   const int64_t dec_wgs =
-      dec->batch > 0 ? static_cast<int64_t>(kv.num_kv_heads) * ((dec->n_items + 1) / 2) : 0;
+      dec->batch > 0 ? static_cast<int64_t>(kv.num_kv_heads) * ((dec->n_items + P - 1) / P) : 0;
   if (pf_wgs + dec_wgs > 0x7FFFFFFF) return PA_ERR_INVALID;
   if (pf_wgs + dec_wgs == 0) return PA_OK;
   const bool keep = (flags & PA_DECODE_KEEP_KV) != 0;
