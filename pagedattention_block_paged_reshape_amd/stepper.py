@@ -2,12 +2,15 @@
 
 Each step reserves one slot per request (``pa_append_slots``, host), stores
 the step's new K/V (``pa_reshape_and_cache``, or its FP8 form for FP8
-pools), refreshes the device block tables (``pa_block_tables`` + one async
-host-to-device copy) and attends (``pa_paged_attention_decode`` / ``_fp8``),
-all enqueued on one stream.  Host staging
-buffers are pinned and used round-robin, so the host prepares step i+1 while
-the GPU still runs step i (the scheduler loop of ta-paperlens: blocks are
-reserved for every running request before the step's forward pass).
+pools), refreshes the device block tables (``pa_block_tables``) and attends
+(``pa_paged_attention_decode`` / ``_fp8``), all enqueued on one stream.  The
+step's slots, tables, lengths and work list sit in one pinned host buffer
+and go to the device in one asynchronous copy on the step's stream (a copy
+on a second stream, waited for by events, made the step slower: 392 vs
+286 us per config-3 step).  Host staging buffers are used round-robin, so
+the host prepares step i+1 while the GPU still runs step i (the scheduler
+loop of ta-paperlens: blocks are reserved for every running request before
+the step's forward pass).
 """
 from __future__ import annotations
 
@@ -32,18 +35,23 @@ class DecodeStepper:
         self.max_blocks = -(-self.max_len_cap // L.BLOCK_SIZE)
         dev = cache.device
         self.depth = depth
-        self.h_slots = [torch.empty(self.B, dtype=torch.int32, pin_memory=True) for _ in range(depth)]
-        self.h_tab = [torch.empty((self.B, self.max_blocks), dtype=torch.int32, pin_memory=True)
-                      for _ in range(depth)]
-        self.h_len = [torch.empty(self.B, dtype=torch.int32, pin_memory=True) for _ in range(depth)]
-        self.d_slots = [torch.empty(self.B, dtype=torch.int32, device=dev) for _ in range(depth)]
-        self.d_tab = torch.empty((self.B, self.max_blocks), dtype=torch.int32, device=dev)
-        self.d_len = torch.empty(self.B, dtype=torch.int32, device=dev)
+        # one int32 staging layout, host and device: slots, tables, lengths,
+        # work list (each section starting on a 64-byte boundary; the work
+        # list last, so a step copies only the entries it uses)
         p_cap = -(-self.max_len_cap // self.partition)
-        self.h_items = [torch.empty(self.B * p_cap, dtype=torch.int32, pin_memory=True)
-                        for _ in range(depth)]
-        self.d_items = torch.empty(self.B * p_cap, dtype=torch.int32, device=dev)
-        self.done = [None] * depth
+        up = lambda n: -(-n // 16) * 16
+        self.o_tab = up(self.B)
+        self.o_len = self.o_tab + up(self.B * self.max_blocks)
+        self.o_items = self.o_len + up(self.B)
+        total = self.o_items + self.B * p_cap
+        self.h_buf = [torch.empty(total, dtype=torch.int32, pin_memory=True) for _ in range(depth)]
+        self.d_buf = torch.empty(total, dtype=torch.int32, device=dev)
+        self.d_slots = self.d_buf[:self.B]
+        self.d_tab = self.d_buf[self.o_tab:self.o_tab + self.B * self.max_blocks].view(
+            self.B, self.max_blocks)
+        self.d_len = self.d_buf[self.o_len:self.o_len + self.B]
+        self.d_items = self.d_buf[self.o_items:]
+        self.done = [None] * depth  # copy of slot r finished (host buffer r free)
         self.ws_bytes = L.pa_decode_workspace_bytes(self.B, self.n_q, cache.d, self.max_len_cap,
                                                     self.partition)
         self.workspace = torch.zeros(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev)
@@ -59,20 +67,20 @@ class DecodeStepper:
         r = self.i % self.depth
         if self.done[r] is not None:
             self.done[r].synchronize()          # the pinned buffers of slot r are free
-        slots_np = self.h_slots[r].numpy()
+        h = self.h_buf[r].numpy()
+        slots_np = h[:self.B]
         _, copies = L.pa_append_slots(self.cache.pool, self.ids, self.ones, slots_out=slots_np)
-        tab_np, len_np = self.h_tab[r].numpy(), self.h_len[r].numpy()
+        tab_np = h[self.o_tab:self.o_tab + self.B * self.max_blocks].reshape(self.B, self.max_blocks)
+        len_np = h[self.o_len:self.o_len + self.B]
         L.pa_block_tables(self.cache.pool, self.ids, self.max_blocks, tables=tab_np, lens=len_np)
         max_len = int(len_np.max())
         if max_len > self.max_len_cap:
             raise ValueError("a request outgrew the stepper's max_len_cap")
         self.last_lens = len_np.copy()
-        n_items = len(L.pa_decode_work_items(len_np, self.partition, out=self.h_items[r].numpy()))
+        n_items = len(L.pa_decode_work_items(len_np, self.partition, out=h[self.o_items:]))
+        used = self.o_items + n_items
         with torch.cuda.stream(stream):
-            self.d_slots[r].copy_(self.h_slots[r], non_blocking=True)
-            self.d_tab.copy_(self.h_tab[r], non_blocking=True)
-            self.d_len.copy_(self.h_len[r], non_blocking=True)
-            self.d_items[:n_items].copy_(self.h_items[r][:n_items], non_blocking=True)
+            self.d_buf[:used].copy_(self.h_buf[r][:used], non_blocking=True)
             ev = torch.cuda.Event()
             ev.record(stream)
             self.done[r] = ev
@@ -81,7 +89,7 @@ class DecodeStepper:
             if len(copies):
                 d_copies = torch.from_numpy(np.ascontiguousarray(copies)).to(self.cache.device)
                 self.cache.copy_blocks(d_copies, len(copies), stream)
-            self.cache.store(k_new, v_new, self.d_slots[r], self.B, stream)
+            self.cache.store(k_new, v_new, self.d_slots, self.B, stream)
             if events is not None:
                 events["cache"][1].record(stream)
                 events["decode"][0].record(stream)

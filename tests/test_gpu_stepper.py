@@ -1,0 +1,64 @@
+"""The decode step the benchmark times, as its stepper runs it: slots
+reserved on the host, the step's K/V stored, tables, lengths and work list
+uploaded in one copy, then the work-list decode (ta-paperlens "LLM serving
+from scratch", scheduler skeleton: blocks are reserved for every running
+request before the forward pass; "fragmentation and PagedAttention": the
+kernel reads K/V through the block table).
+
+The first step must equal the fp64 oracle's decode of the same workload
+step; later steps (the pool grown by one token per request each time) must
+equal, bitwise, a decode planned from scratch on the same pool.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import assert_close, log, oracle_run, shared_reference, shared_workload
+from oracle import decode_reference
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("cfg", ["2", "3"])
+def test_decode_stepper_matches_oracle_then_fresh_plans(cfg):
+    from pagedattention_block_paged_reshape_amd.cache import (DecodePlan, PagedKVCache,
+                                                              run_program)
+    from pagedattention_block_paged_reshape_amd.stepper import DecodeStepper
+    w = shared_workload(cfg)
+    assert list(w.step_ids) == list(w.decode_ids) and set(np.asarray(w.step_n_new)) == {1}
+    dev = torch.device("cuda:0")
+    steps = 3
+    extra = w.batch * (steps // 16 + 2)
+    free_order = np.concatenate([np.arange(w.num_blocks, w.num_blocks + extra, dtype=np.int32),
+                                 np.asarray(w.free_order, dtype=np.int32)])
+    cache = PagedKVCache(w.num_blocks + extra, w.n_kv, w.d, free_order, dev)
+    dk = torch.from_numpy(w.setup_k).to(dev)
+    dv = torch.from_numpy(w.setup_v).to(dev)
+    run_program(cache, w.setup, dk, dv)
+    del dk, dv
+    sk = torch.from_numpy(w.step_k[:w.batch]).to(dev)
+    sv = torch.from_numpy(w.step_v[:w.batch]).to(dev)
+    q = torch.from_numpy(w.q).to(dev)
+    cap = max(cache.seq_len(int(s)) for s in w.decode_ids) + steps
+    stepper = DecodeStepper(cache, w.decode_ids, w.n_q, w.scale, cap, 512)
+    log(f"[stepper] config {cfg}: B={w.batch}, cap {cap}")
+
+    out = stepper.step(q, sk, sv).clone()
+    torch.cuda.synchronize()
+    if cfg == "3":
+        ref = shared_reference(3, "decode")
+    else:
+        ref = decode_reference(w, oracle_run(w))
+    err = assert_close(out, ref, f"config {cfg} stepper decode")
+    log(f"[stepper] config {cfg} step 1: max err {err:.2e}")
+
+    for i in range(2, steps + 1):
+        out = stepper.step(q, sk, sv).clone()
+        torch.cuda.synchronize()
+        lens = stepper.last_lens
+        assert (lens == np.asarray([cache.seq_len(int(s)) for s in w.decode_ids])).all()
+        plan = DecodePlan(cache, w.decode_ids, w.n_q, w.scale, 512)
+        fresh = plan.run(q).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), fresh.view(torch.int16)), f"step {i}"
+        log(f"[stepper] config {cfg} step {i}: bitwise equal to a fresh plan")
