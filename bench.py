@@ -48,6 +48,7 @@ PREFILL_SOURCES = ["pagedattention_block_paged_reshape_amd/csrc/prefill_tile.h",
                    "pagedattention_block_paged_reshape_amd/csrc/pa_device.h"]
 TRAFFIC_FILES = {"fp16": os.path.join(PROFILES, "decode_llama3-70b_traffic.md"),
                  "fp8": os.path.join(PROFILES, "decode_llama3-70b_fp8_traffic.md")}
+PREFILL_TRAFFIC_FILES = {"fp16": os.path.join(PROFILES, "prefill_long-context-chunk_traffic.md")}
 # FP8 pools: one scale per pool, about max |x| / 448 for the N(0, 1) rows
 FP8_K_SCALE, FP8_V_SCALE = 5.5 / 448, 4.75 / 448
 
@@ -64,16 +65,17 @@ def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(kv_dtype: str = "fp16"):
-    """HBM bytes per decode launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel sources."""
-    path = TRAFFIC_FILES[kv_dtype]
-    if not os.path.exists(path):
+def recorded_traffic(kv_dtype: str = "fp16", prefill: bool = False):
+    """HBM bytes per decode (or prefill) launch from the committed rocprofv3
+    counter summary, if it was taken on the current kernel sources."""
+    path = (PREFILL_TRAFFIC_FILES if prefill else TRAFFIC_FILES).get(kv_dtype)
+    if path is None or not os.path.exists(path):
         return None
     text = open(path).read()
     m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
     m_bytes = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+    sources = PREFILL_SOURCES if prefill else KERNEL_SOURCES
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash(sources):
         return None
     return float(m_bytes.group(1))
 
@@ -318,7 +320,7 @@ def prefill_roofline(ms, flops, kv_dtype: str) -> dict:
         "peak": MFMA_F16_PEAK_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
-        "traffic": None,
+        "traffic": recorded_traffic(kv_dtype, prefill=True),
         "kernel": f"pa_paged_attention_prefill{'_fp8' if fp8 else ''} "
                   f"({'prefill_chunk_kernel' if fp8 else 'prefill_chunk_pp_kernel'} + "
                   "prefill_reduce_kernel)",
