@@ -680,29 +680,42 @@ __device__ __forceinline__ void prefill_tile_pp(const PrefillArgs& a, int g, int
   typedef f16x8 Probs[2][2];
   // S^T[key][M-row] = K . Q^T over the 4 blocks in K buffer `buf`.  Lane
   // (col, lg) reads K[slot col][dims 32kk + 8lg ..] of block mt, 16 bytes of
-  // the tile order [D/8][16][8]: 1 KiB per wavefront and read.  Block mt + 1's
-  // reads are requested before block mt's products, which then wait for block
-  // mt's reads only (the scheduling fences keep that order).
+  // the tile order [D/8][16][8]: 1 KiB per wavefront and read.  Blocks go in
+  // pairs: pair pr + 1's reads are requested before pair pr's products, which
+  // then wait for pair pr's reads only (the scheduling fences keep that
+  // order), and the two blocks' products interleave as four independent
+  // accumulation chains (each still summing over kk in order).
   auto scores = [&](int buf, Scores& s) {
     const f16* const sk = lds.kv[buf][0] + lane * 8;
-    f16x8 kb[2][KS];
-    auto kload = [&](int mt, f16x8 (&dst)[KS]) {
+    f16x8 kb[2][2][KS];
+    auto kload = [&](int pr, f16x8 (&dst)[2][KS]) {
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk)
-        dst[kk] = *reinterpret_cast<const f16x8*>(sk + mt * TILE + kk * 512);
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+          dst[e][kk] = *reinterpret_cast<const f16x8*>(sk + (2 * pr + e) * TILE + kk * 512);
     };
     kload(0, kb[0]);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      if (mt + 1 < 4) kload(mt + 1, kb[(mt + 1) & 1]);
+    for (int pr = 0; pr < 2; ++pr) {
+      if (pr + 1 < 2) kload(pr + 1, kb[(pr + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
-      f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      f32x4 acc[2][2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) acc[e][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) acc[nt] = mfma16x16x32(kb[mt & 1][kk], qf[nt][kk], acc[nt]);
-      s[mt][0] = acc[0];
-      s[mt][1] = acc[1];
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+            acc[e][nt] = mfma16x16x32(kb[pr & 1][e][kk], qf[nt][kk], acc[e][nt]);
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) s[2 * pr + e][nt] = acc[e][nt];
       __builtin_amdgcn_sched_barrier(0);
     }
   };
