@@ -365,6 +365,29 @@ pa_status pa_reshape_and_cache(const pa_half* k, const pa_half* v, const int32_t
  * pa_reshape_and_cache of the same step (same stream). */
 pa_status pa_copy_blocks(const pa_copy* copies, int32_t n, pa_kv_view kv, void* stream);
 
+/* Device address of pinned host memory (allocated with hipHostMalloc, e.g. a
+ * torch pin_memory tensor), so that kernels can read per-step metadata in
+ * place instead of from a device copy: the slot mapping, block tables,
+ * lengths and work list that the scheduler rebuilds every step ([lens]
+ * scheduler skeleton: blocks are reserved for the running requests before
+ * each forward pass).  host: a pointer into such an allocation; *device
+ * receives the matching device address.  Reads through it cross the host
+ * link, so it suits data that a launch reads a few times.  The caller keeps
+ * the memory unchanged until every launch that reads it has completed.
+ * PA_ERR_INVALID for a null argument or memory the runtime does not hold as
+ * pinned. */
+pa_status pa_host_device_pointer(const void* host, void** device);
+
+/* Copy `bytes` from src to dst with one kernel launch on `stream`, for
+ * moving a step's metadata (slot mapping, block tables, lengths, work list:
+ * [lens] scheduler skeleton) from pinned host memory, through its device
+ * address (pa_host_device_pointer), into device memory.  The runtime's own
+ * copy from host memory runs as several launches; this is one.  src, dst:
+ * device addresses, 16-byte aligned, non-overlapping; bytes: a multiple of
+ * 16 (0 does nothing).  PA_ERR_INVALID on a null pointer, misalignment or a
+ * size that is not a multiple of 16.  Async on `stream`. */
+pa_status pa_stage_copy(const void* src, void* dst, uint64_t bytes, void* stream);
+
 /* Swap transfers: whole K and V tiles (all kv heads) of n blocks between the
  * pools and contiguous buffers [n][num_kv_heads][16*D] fp16 in the pools'
  * tile order (a bit copy; the caller moves the buffers to and from host

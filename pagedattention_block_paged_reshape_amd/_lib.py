@@ -153,6 +153,8 @@ _SIGS = {
                                                  _I32, C.c_float, _P, _U64, _P]),
     "pa_seq_swap_out": (C.c_int, [_P, _I64, _P, _I32, C.POINTER(_I32), C.POINTER(_I32)]),
     "pa_seq_swap_in": (C.c_int, [_P, _I64, _I32, _P, _I32, C.POINTER(_I32)]),
+    "pa_host_device_pointer": (C.c_int, [_P, C.POINTER(C.c_void_p)]),
+    "pa_stage_copy": (C.c_int, [_P, _P, C.c_uint64, _P]),
     "pa_gather_blocks": (C.c_int, [_P, _I32, pa_kv_view, _P, _P, _P]),
     "pa_scatter_blocks": (C.c_int, [_P, _I32, pa_kv_view, _P, _P, _P]),
     "pa_gather_blocks_fp8": (C.c_int, [_P, _I32, pa_kv_view_fp8, _P, _P, _P]),
@@ -604,6 +606,20 @@ def pa_seq_swap_in(pool: int, seq_id: int, seq_len: int) -> np.ndarray:
     _check(LIB.pa_seq_swap_in(pool, int(seq_id), int(seq_len), out.ctypes.data, out.size,
                               C.byref(n)), "pa_seq_swap_in")
     return out[:n.value]
+
+
+def pa_host_device_pointer(host) -> int:
+    """Device address of pinned host memory (a pin_memory tensor or an int
+    host address)."""
+    addr = host if isinstance(host, int) else host.data_ptr()
+    out = C.c_void_p()
+    _check(LIB.pa_host_device_pointer(addr, C.byref(out)), "pa_host_device_pointer")
+    return int(out.value)
+
+
+def pa_stage_copy(src, dst, nbytes: int, stream=None) -> None:
+    _check(LIB.pa_stage_copy(_dptr(src), _dptr(dst), int(nbytes), _stream(stream)),
+           "pa_stage_copy")
 
 
 def pa_gather_blocks(blocks, n: int, kv, k_out, v_out, stream=None) -> None:

@@ -12,6 +12,9 @@
 //
 // FP8 pools (ta-paperlens "in practice": a smaller KV data type as a serving
 // setting) store OCP E4M3 codes with one scale per pool.
+//
+// Also here: the one-launch staging copy of a step's metadata from pinned
+// host memory (pa_stage_copy).
 #include "pa_device.h"
 
 namespace pa {
@@ -331,4 +334,41 @@ extern "C" pa_status pa_scatter_blocks_fp8(const int32_t* blocks, int32_t n, pa_
   return block_transfer(false, blocks, n, kv.k_pool, kv.v_pool, kv.num_blocks, kv.block_size,
                         kv.num_kv_heads, kv.head_dim, 1, const_cast<uint8_t*>(k_in),
                         const_cast<uint8_t*>(v_in), stream);
+}
+
+extern "C" pa_status pa_host_device_pointer(const void* host, void** device) {
+  if (host == nullptr || device == nullptr) return PA_ERR_INVALID;
+  void* d = nullptr;
+  if (hipHostGetDevicePointer(&d, const_cast<void*>(host), 0) != hipSuccess || d == nullptr) {
+    (void)hipGetLastError();  // not pinned: clear the runtime's sticky error
+    return PA_ERR_INVALID;
+  }
+  *device = d;
+  return PA_OK;
+}
+
+namespace pa {
+
+// 16-byte chunks, grid-stride; the source is usually pinned host memory read
+// across the host link once, hence the non-temporal loads
+__global__ __launch_bounds__(256) void stage_copy_kernel(const u32x4* __restrict__ src,
+                                                         u32x4* __restrict__ dst, int64_t n) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
+    dst[i] = __builtin_nontemporal_load(src + i);
+}
+
+}  // namespace pa
+
+extern "C" pa_status pa_stage_copy(const void* src, void* dst, uint64_t bytes, void* stream) {
+  if (src == nullptr || dst == nullptr) return PA_ERR_INVALID;
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst) | bytes) & 15u)
+    return PA_ERR_INVALID;
+  const int64_t n = static_cast<int64_t>(bytes / 16);
+  if (n == 0) return PA_OK;
+  const int64_t wgs = n < 256 * 256 ? (n + 255) / 256 : 256;
+  pa::stage_copy_kernel<<<dim3(static_cast<uint32_t>(wgs)), dim3(256), 0,
+                          static_cast<hipStream_t>(stream)>>>(
+      reinterpret_cast<const pa::u32x4*>(src), reinterpret_cast<pa::u32x4*>(dst), n);
+  return pa::launch_status();
 }

@@ -3,14 +3,16 @@
 Each step reserves one slot per request (``pa_append_slots``, host), stores
 the step's new K/V (``pa_reshape_and_cache``, or its FP8 form for FP8
 pools), refreshes the device block tables (``pa_block_tables``) and attends
-(``pa_paged_attention_decode`` / ``_fp8``), all enqueued on one stream.  The
-step's slots, tables, lengths and work list sit in one pinned host buffer
-and go to the device in one asynchronous copy on the step's stream (a copy
-on a second stream, waited for by events, made the step slower: 392 vs
-286 us per config-3 step).  Host staging buffers are used round-robin, so
-the host prepares step i+1 while the GPU still runs step i (the scheduler
-loop of ta-paperlens: blocks are reserved for every running request before
-the step's forward pass).
+(``pa_paged_attention_decode`` / ``_fp8``), all enqueued on one stream (the
+scheduler loop of ta-paperlens: blocks are reserved for every running
+request before the step's forward pass).  The step's slots, tables, lengths
+and work list sit in one pinned host buffer and go to device memory in one
+``pa_stage_copy`` launch on the step's stream.  Measured per config-3 step:
+the runtime's copy from pinned memory (several launches) 262 us, this copy
+250 us, the kernels reading the pinned buffer in place 249 us but with the
+decode kernel itself ~10 us slower (its table reads cross the host link),
+and a copy on a second stream waited for by events 392 us.  Host buffers are
+used round-robin: the host fills buffer i+1 while the GPU still runs step i.
 """
 from __future__ import annotations
 
@@ -25,7 +27,7 @@ from .cache import DEFAULT_PARTITION, PagedKVCache
 
 class DecodeStepper:
     def __init__(self, cache: PagedKVCache, seq_ids, num_q_heads: int, scale: float,
-                 max_len_cap: int, partition: int = DEFAULT_PARTITION, depth: int = 2):
+                 max_len_cap: int, partition: int = DEFAULT_PARTITION, depth: int = 3):
         self.cache = cache
         self.ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
         self.B = len(self.ids)
@@ -43,15 +45,18 @@ class DecodeStepper:
         self.o_tab = up(self.B)
         self.o_len = self.o_tab + up(self.B * self.max_blocks)
         self.o_items = self.o_len + up(self.B)
-        total = self.o_items + self.B * p_cap
+        total = up(self.o_items + self.B * p_cap)
         self.h_buf = [torch.empty(total, dtype=torch.int32, pin_memory=True) for _ in range(depth)]
+        self.h_dev = [L.pa_host_device_pointer(b) for b in self.h_buf]
         self.d_buf = torch.empty(total, dtype=torch.int32, device=dev)
         self.d_slots = self.d_buf[:self.B]
         self.d_tab = self.d_buf[self.o_tab:self.o_tab + self.B * self.max_blocks].view(
             self.B, self.max_blocks)
         self.d_len = self.d_buf[self.o_len:self.o_len + self.B]
         self.d_items = self.d_buf[self.o_items:]
-        self.done = [None] * depth  # copy of slot r finished (host buffer r free)
+        # event r: the copy out of host buffer r has completed
+        self.done = [torch.cuda.Event() for _ in range(depth)]
+        self.used = [False] * depth
         self.ws_bytes = L.pa_decode_workspace_bytes(self.B, self.n_q, cache.d, self.max_len_cap,
                                                     self.partition)
         self.workspace = torch.zeros(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev)
@@ -65,8 +70,8 @@ class DecodeStepper:
         pairs named 'cache' and 'decode' recorded around those launches."""
         stream = stream or torch.cuda.current_stream(self.cache.device)
         r = self.i % self.depth
-        if self.done[r] is not None:
-            self.done[r].synchronize()          # the pinned buffers of slot r are free
+        if self.used[r]:
+            self.done[r].synchronize()          # host buffer r has been copied out
         h = self.h_buf[r].numpy()
         slots_np = h[:self.B]
         _, copies = L.pa_append_slots(self.cache.pool, self.ids, self.ones, slots_out=slots_np)
@@ -78,12 +83,11 @@ class DecodeStepper:
             raise ValueError("a request outgrew the stepper's max_len_cap")
         self.last_lens = len_np.copy()
         n_items = len(L.pa_decode_work_items(len_np, self.partition, out=h[self.o_items:]))
-        used = self.o_items + n_items
+        nbytes = -(-(self.o_items + n_items) // 4) * 16  # whole 16-byte chunks
         with torch.cuda.stream(stream):
-            self.d_buf[:used].copy_(self.h_buf[r][:used], non_blocking=True)
-            ev = torch.cuda.Event()
-            ev.record(stream)
-            self.done[r] = ev
+            L.pa_stage_copy(self.h_dev[r], self.d_buf, nbytes, stream)
+            self.done[r].record(stream)
+            self.used[r] = True
             if events is not None:
                 events["cache"][0].record(stream)
             if len(copies):

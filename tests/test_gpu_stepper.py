@@ -1,6 +1,7 @@
 """The decode step the benchmark times, as its stepper runs it: slots
-reserved on the host, the step's K/V stored, tables, lengths and work list
-uploaded in one copy, then the work-list decode (ta-paperlens "LLM serving
+reserved on the host, tables, lengths and work list moved from pinned host
+memory by one pa_stage_copy launch, the step's K/V stored, then the
+work-list decode (ta-paperlens "LLM serving
 from scratch", scheduler skeleton: blocks are reserved for every running
 request before the forward pass; "fragmentation and PagedAttention": the
 kernel reads K/V through the block table).
@@ -62,3 +63,29 @@ def test_decode_stepper_matches_oracle_then_fresh_plans(cfg):
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), fresh.view(torch.int16)), f"step {i}"
         log(f"[stepper] config {cfg} step {i}: bitwise equal to a fresh plan")
+
+
+def test_stage_copy_moves_pinned_host_bytes_exactly():
+    """pa_stage_copy: whole 16-byte chunks from pinned host memory (through
+    pa_host_device_pointer) into device memory, bit for bit, and nothing past
+    the requested size."""
+    import pagedattention_block_paged_reshape_amd as pa
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(7)
+    n_int = (1 << 20) + 64
+    host = torch.empty(n_int, dtype=torch.int32, pin_memory=True)
+    host.numpy()[:] = rng.integers(-2**31, 2**31 - 1, n_int, dtype=np.int64).astype(np.int32)
+    src = pa.pa_host_device_pointer(host)
+    assert src != 0
+    stream = torch.cuda.current_stream(dev)
+    for nbytes in (16, 48, 4096, 65536 + 16, 4 * n_int):
+        dst = torch.full((n_int,), -7, dtype=torch.int32, device=dev)
+        pa.pa_stage_copy(src, dst, nbytes, stream)
+        torch.cuda.synchronize()
+        got = dst.cpu().numpy()
+        k = nbytes // 4
+        log(f"stage copy {nbytes} bytes")
+        assert np.array_equal(got[:k], host.numpy()[:k])
+        assert (got[k:] == -7).all()
+    # an interior pointer of the pinned allocation maps to the same offset
+    assert pa.pa_host_device_pointer(host.data_ptr() + 4096) == src + 4096

@@ -35,6 +35,21 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(_lib.EXPORTED)
 
 
+def test_staging_helpers_reject_bad_arguments_before_any_device_call():
+    import ctypes as C
+    out = C.c_void_p()
+    assert _lib.LIB.pa_host_device_pointer(None, C.byref(out)) == _lib.PA_ERR_INVALID
+    assert _lib.LIB.pa_host_device_pointer(16, None) == _lib.PA_ERR_INVALID
+    # null, misaligned, or not whole 16-byte chunks
+    assert _lib.LIB.pa_stage_copy(None, 256, 16, None) == _lib.PA_ERR_INVALID
+    assert _lib.LIB.pa_stage_copy(256, None, 16, None) == _lib.PA_ERR_INVALID
+    assert _lib.LIB.pa_stage_copy(256 + 4, 512, 16, None) == _lib.PA_ERR_INVALID
+    assert _lib.LIB.pa_stage_copy(256, 512 + 8, 16, None) == _lib.PA_ERR_INVALID
+    assert _lib.LIB.pa_stage_copy(256, 512, 20, None) == _lib.PA_ERR_INVALID
+    # nothing to copy: no launch
+    assert _lib.LIB.pa_stage_copy(256, 512, 0, None) == _lib.PA_OK
+
+
 def test_status_strings_and_kv_bytes():
     assert pa.status_string(0) == "ok"
     assert "out of blocks" in pa.status_string(2)
