@@ -19,6 +19,9 @@ memory and writes those of resumed requests back into their new blocks.
 With mixed=True a step with both kinds of work runs its decode batch and its
 first prefill chunk in one pa_paged_attention_mixed launch (bitwise the same
 outputs as the two separate launches).
+A step's host-built arrays (request ids and positions of its rows, slots,
+copy-on-write list, block tables, lengths, work lists) are packed into one
+pinned staging buffer and moved to the device by one pa_stage_copy launch.
 This module only marshals arguments and launches; every step of the path
 runs in the library.
 """
@@ -31,6 +34,64 @@ import torch
 
 from . import _lib as L
 from .cache import PagedKVCache
+
+
+class _Staging:
+    """A ring of pinned host buffers and one device buffer: a step's arrays
+    are packed into the next host buffer (16-byte aligned sections) and moved
+    by one pa_stage_copy launch; the host waits for a buffer's copy before
+    packing it again."""
+
+    def __init__(self, dev, nbytes: int = 1 << 16, depth: int = 3):
+        self.dev = dev
+        self.depth = depth
+        self.host = [self._pinned(nbytes) for _ in range(depth)]
+        self.done = [torch.cuda.Event() for _ in range(depth)]
+        self.used = [False] * depth
+        self.d_buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.r = -1
+        self.off = 0
+        self.secs: List[Tuple[int, int, np.dtype]] = []
+
+    @staticmethod
+    def _pinned(nbytes: int):
+        buf = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+        return buf, L.pa_host_device_pointer(buf)
+
+    def begin(self) -> None:
+        self.r = (self.r + 1) % self.depth
+        if self.used[self.r]:
+            self.done[self.r].synchronize()
+        self.off = 0
+        self.secs = []
+
+    def add(self, a: np.ndarray) -> int:
+        """Pack `a`; returns its section index."""
+        a = np.ascontiguousarray(a)
+        n = a.nbytes
+        buf, _ = self.host[self.r]
+        if self.off + n > buf.numel():
+            grown = self._pinned(max(2 * buf.numel(), -(-(self.off + n) // 4096) * 4096 * 2))
+            grown[0][:self.off].copy_(buf[:self.off])
+            self.host[self.r] = grown
+            buf = grown[0]
+        if n:
+            buf.numpy()[self.off:self.off + n] = a.view(np.uint8).reshape(-1)
+        self.secs.append((self.off, a.size, a.dtype))
+        self.off += -(-n // 16) * 16
+        return len(self.secs) - 1
+
+    def upload(self, stream) -> List[torch.Tensor]:
+        """One copy of the packed sections; returns their device views."""
+        if self.d_buf.numel() < self.off:
+            self.d_buf = torch.empty(2 * self.off, dtype=torch.uint8, device=self.dev)
+        if self.off:
+            L.pa_stage_copy(self.host[self.r][1], self.d_buf, self.off, stream)
+        self.done[self.r].record(stream)
+        self.used[self.r] = True
+        tdt = {np.dtype(np.int32): torch.int32, np.dtype(np.int64): torch.int64}
+        return [self.d_buf[o:o + n * np.dtype(dt).itemsize].view(tdt[np.dtype(dt)])
+                for o, n, dt in self.secs]
 
 
 class ServingLoop:
@@ -66,6 +127,7 @@ class ServingLoop:
         self._ws = torch.zeros(16, dtype=torch.uint8, device=dev)
         self._pws = torch.zeros(16, dtype=torch.uint8, device=dev)
         self.dev = dev
+        self.stage = _Staging(dev)
 
     def close(self):
         if self.sched:
@@ -98,12 +160,6 @@ class ServingLoop:
             if t is not None and t.device.type == "cuda":
                 t.record_stream(stream)
 
-    def _h2d(self, a: np.ndarray) -> torch.Tensor:
-        """Host array to the device through a pinned staging copy, so the
-        copy never waits for the GPU to drain the stream."""
-        return torch.from_numpy(np.ascontiguousarray(a)).pin_memory().to(self.dev,
-                                                                         non_blocking=True)
-
     def step(self, stream=None) -> List[int]:
         """Plan and run one step; returns the requests that finished.  All of
         the step's device work (row generation, host-to-device copies,
@@ -129,8 +185,29 @@ class ServingLoop:
         if items:
             req = np.concatenate([np.full(n, r, dtype=np.int64) for r, _, n, _ in items])
             pos = np.concatenate([np.arange(s, s + n, dtype=np.int64) for _, s, n, _ in items])
-            d_req = self._h2d(req)
-            d_pos = self._h2d(pos)
+            offs = np.cumsum([0] + [n for _, _, n, _ in items])
+            dec = [i for i, it in enumerate(items) if it[3]]
+            pre = [i for i, it in enumerate(items) if not it[3]]
+            first = None
+            if self.mixed and dec and pre:
+                first, pre = pre[0], pre[1:]
+            # every array the step's launches read, packed and moved at once
+            st = self.stage
+            st.begin()
+            i_req, i_pos = st.add(req), st.add(pos)
+            i_slots = st.add(plan["slots"])
+            i_copies = st.add(plan["copies"]) if len(plan["copies"]) else None
+            dec_host = self._decode_host([items[i] for i in dec]) if dec else None
+            rows = offs[dec] if dec else None
+            lead = dec and np.array_equal(rows, np.arange(len(dec)))
+            i_rows = st.add(rows.astype(np.int64)) if dec and not lead else None
+            i_dec = [st.add(a) for a in dec_host[:3]] if dec else None
+            pf_host = {i: self._prefill_host(*items[i][:3]) for i in ([first] if first is not None
+                                                                      else []) + pre}
+            i_pf = {i: st.add(h[0]) for i, h in pf_host.items()}
+            dv = st.upload(stream)
+
+            d_req, d_pos = dv[i_req], dv[i_pos]
             width = self.cache.n_kv * self.d
             if self.rows_fn is not None:
                 k, v, q = self.rows_fn(d_req, d_pos, width, self.n_q * self.d)
@@ -141,34 +218,24 @@ class ServingLoop:
                 k = self.row_fn(d_req, d_pos, 0, width).view(-1, self.cache.n_kv, self.d)
                 v = self.row_fn(d_req, d_pos, 1, width).view(-1, self.cache.n_kv, self.d)
                 q = self.row_fn(d_req, d_pos, 2, self.n_q * self.d).view(-1, self.n_q, self.d)
-            slots = self._h2d(plan["slots"])
-            if len(plan["copies"]):
-                d_copies = self._h2d(plan["copies"])
-                self.cache.copy_blocks(d_copies, len(plan["copies"]), stream)
-                self._hold(stream, d_copies)
-            self.cache.store(k, v, slots, len(req), stream)
-            self._hold(stream, k, v, slots)
-            offs = np.cumsum([0] + [n for _, _, n, _ in items])
-            dec = [i for i, it in enumerate(items) if it[3]]
-            pre = [i for i, it in enumerate(items) if not it[3]]
+            if i_copies is not None:
+                self.cache.copy_blocks(dv[i_copies], len(plan["copies"]), stream)
+            self.cache.store(k, v, dv[i_slots], len(req), stream)
+            self._hold(stream, k, v)
             if dec:
-                rows = offs[dec]
                 # decode items come first (one token each), so their query
                 # rows are usually a leading slice
-                if np.array_equal(rows, np.arange(len(dec))):
-                    q_dec = q[:len(dec)]
-                else:
-                    q_dec = q[self._h2d(rows.astype(np.int64))]
-                first = None
-                if self.mixed and pre:
-                    first = pre[0]
-                    pre = pre[1:]
+                q_dec = q[:len(dec)] if lead else q[dv[i_rows]]
+                chunk = None
+                if first is not None:
                     r, s, n, _ = items[first]
-                    first = (r, s, n, q[offs[first]:offs[first] + n])
-                self._decode([items[i] for i in dec], q_dec, stream, chunk=first)
+                    chunk = (r, s, n, q[offs[first]:offs[first] + n], pf_host[first],
+                             dv[i_pf[first]])
+                self._decode([items[i] for i in dec], q_dec, stream, dec_host,
+                             [dv[j] for j in i_dec], chunk=chunk)
             for i in pre:
                 r, s, n, _ = items[i]
-                self._prefill(r, s, n, q[offs[i]:offs[i] + n], stream)
+                self._prefill(r, s, n, q[offs[i]:offs[i] + n], stream, pf_host[i], dv[i_pf[i]])
             self.stats["decode_tokens"] += len(dec)
             self.stats["prefill_tokens"] += int(sum(it[2] for it in items if not it[3]))
         done = L.pa_sched_commit(self.sched, self.max_running)
@@ -176,47 +243,56 @@ class ServingLoop:
         self.stats["finished"] += len(done)
         return done
 
-    def _decode(self, items, q: torch.Tensor, stream, chunk=None):
-        """Decode attention for the items; with chunk = (request, start,
-        length, query rows) that prefill chunk runs in the same launch."""
+    def _decode_host(self, items):
+        """Host arrays of a decode batch: tables, lengths, work list, and the
+        table width and longest length."""
         ids = [r for r, _, _, _ in items]
         # each request's length after this step is known from its item
         max_blocks = max(-(-(s + 1) // L.BLOCK_SIZE) for _, s, _, _ in items)
         tab, ln = L.pa_block_tables(self.cache.pool, ids, max_blocks)
         assert [int(x) for x in ln] == [s + 1 for _, s, _, _ in items]
-        max_len = int(ln.max())
         work = L.pa_decode_work_items(ln, self.partition)
-        ws_bytes = L.pa_decode_workspace_bytes(len(ids), self.n_q, self.d, max_len, self.partition)
+        return tab, ln, work, max_blocks, int(ln.max())
+
+    def _prefill_host(self, r: int, s: int, n: int):
+        """Host table of a prefill chunk and its width."""
+        max_blocks = -(-(s + n) // L.BLOCK_SIZE)
+        tab, ln = L.pa_block_tables(self.cache.pool, [r], max_blocks)
+        assert int(ln[0]) == s + n
+        return tab[0], max_blocks
+
+    def _decode(self, items, q: torch.Tensor, stream, host, dev, chunk=None):
+        """Decode attention for the items (host: _decode_host's arrays, dev:
+        device copies of its tables, lengths and work list); with chunk =
+        (request, start, length, query rows, prefill host data, prefill
+        device table) that prefill chunk runs in the same launch."""
+        _, _, work, max_blocks, max_len = host
+        d_tab, d_len, d_work = dev
+        n_dec = len(items)
+        ws_bytes = L.pa_decode_workspace_bytes(n_dec, self.n_q, self.d, max_len, self.partition)
         ws = self._workspace("_ws", max(ws_bytes, 16))
-        out = torch.empty((len(ids), self.n_q, self.d), dtype=torch.float16, device=self.dev)
-        d_tab = self._h2d(tab)
-        d_len = self._h2d(ln)
-        d_work = self._h2d(work)
+        out = torch.empty((n_dec, self.n_q, self.d), dtype=torch.float16, device=self.dev)
         flags = L.PA_DECODE_KEEP_KV if self.cache.shares_blocks() else 0
         # a contiguous copy of the queries (a slice of the step's fused rows
         # is not): bound to a name so it outlives every launch that reads it
         q_c = q.contiguous()
         if chunk is None:
-            self.cache.decode(out, q_c, d_tab, max_blocks, d_len, len(ids), self.n_q,
+            self.cache.decode(out, q_c, d_tab, max_blocks, d_len, n_dec, self.n_q,
                               self.scale, self.partition, max_len, d_work, len(work), ws,
                               ws_bytes, stream, flags=flags)
-            self._hold(stream, q_c, out, d_tab, d_len, d_work, ws)
+            self._hold(stream, q_c, out, ws)
         else:
-            r, s, n, qc = chunk
-            pf_blocks = -(-(s + n) // L.BLOCK_SIZE)
-            ptab, pln = L.pa_block_tables(self.cache.pool, [r], pf_blocks)
-            assert int(pln[0]) == s + n
+            r, s, n, qc, (_, pf_blocks), d_ptab = chunk
             qc = qc.contiguous()
             pout = torch.empty((n, self.n_q, self.d), dtype=torch.float16, device=self.dev)
-            c_dec = L.decode_batch(out, q_c, d_tab, max_blocks, d_len, len(ids),
+            c_dec = L.decode_batch(out, q_c, d_tab, max_blocks, d_len, n_dec,
                                    self.partition, max_len, d_work, len(work))
-            d_ptab = self._h2d(ptab[0])
             c_pf = L.prefill_chunk(pout, qc, d_ptab, pf_blocks, s, n)
             mws_bytes = L.pa_mixed_workspace_bytes(c_dec, c_pf, self.n_q, self.d)
             mws = self._workspace("_ws", max(mws_bytes, 16))
             L.pa_paged_attention_mixed(c_dec, c_pf, self.cache.kv, self.n_q, self.scale, mws,
                                        mws_bytes, stream, flags=flags)
-            self._hold(stream, q_c, out, d_tab, d_len, d_work, qc, pout, d_ptab, mws)
+            self._hold(stream, q_c, out, qc, pout, mws)
             self.stats["mixed_launches"] += 1
             if self.keep:
                 kept = pout.clone()
@@ -229,18 +305,15 @@ class ServingLoop:
             for j, (r, s, _, _) in enumerate(items):
                 self.outputs[(r, s)] = (kept[j], "decode")
 
-    def _prefill(self, r: int, s: int, n: int, q: torch.Tensor, stream):
-        max_blocks = -(-(s + n) // L.BLOCK_SIZE)
-        tab, ln = L.pa_block_tables(self.cache.pool, [r], max_blocks)
-        assert int(ln[0]) == s + n
+    def _prefill(self, r: int, s: int, n: int, q: torch.Tensor, stream, host, d_tab):
+        _, max_blocks = host
         ws_bytes = L.pa_prefill_workspace_bytes(n, self.n_q, self.d, s)
         ws = self._workspace("_pws", max(ws_bytes, 16))
         out = torch.empty((n, self.n_q, self.d), dtype=torch.float16, device=self.dev)
-        d_tab = self._h2d(tab[0])
         q_c = q.contiguous()
         L.pa_paged_attention_prefill(out, q_c, self.cache.kv, d_tab, max_blocks, s, n,
                                      self.n_q, self.scale, ws, ws_bytes, stream)
-        self._hold(stream, q_c, out, d_tab, ws)
+        self._hold(stream, q_c, out, ws)
         if self.keep:
             kept = out.clone()
             for j in range(n):
