@@ -10,9 +10,10 @@ and work list sit in one pinned host buffer and go to device memory in one
 ``pa_stage_copy`` launch on the step's stream.  Measured per config-3 step:
 the runtime's copy from pinned memory (several launches) 262 us, this copy
 250 us, the kernels reading the pinned buffer in place 249 us but with the
-decode kernel itself ~10 us slower (its table reads cross the host link),
-and a copy on a second stream waited for by events 392 us.  Host buffers are
-used round-robin: the host fills buffer i+1 while the GPU still runs step i.
+decode kernel itself ~10 us slower (its table reads cross the host link);
+this copy on a second stream, overlapping the previous step and waited for
+by events, 253 vs 249 us serial.  Host buffers are used round-robin: the
+host fills buffer i+1 while the GPU still runs step i.
 """
 from __future__ import annotations
 
