@@ -865,26 +865,49 @@ __device__ __forceinline__ void prefill_reduce_row(int32_t chunk_len, int32_t n_
                                                    const float* __restrict__ ws_l,
                                                    f16* __restrict__ out, int head, int row) {
   constexpr int PER = D / 64;
+  constexpr int GRP = 4;  // splits whose partial rows are requested together
+  const int lane = threadIdx.x;
   const int64_t qh = static_cast<int64_t>(row) * n_q + head;
   const int64_t stride = static_cast<int64_t>(chunk_len) * n_q;
+  // split z's max and sum in lane z (splits <= 64), all requested at once
+  // (lanes past the splits read split 0's and ignore it)
+  const bool has = lane < splits;
+  const int64_t zl = (has ? lane : 0) * stride + qh;
+  const float m_in = ws_m[zl], l_in = ws_l[zl];
+  const float mz = has ? m_in : -INFINITY;
+  const float lz = has ? l_in : 0.0f;
   float M = -INFINITY;
-  for (int z = 0; z < splits; ++z) M = fmaxf(M, ws_m[z * stride + qh]);
+  for (int z = 0; z < splits; ++z)
+    M = fmaxf(M, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mz), z)));
   float wsum = 0.0f, acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
-  for (int z = 0; z < splits; ++z) {
-    const float l = ws_l[z * stride + qh];
-    if (!(l > 0.0f) && !(ws_m[z * stride + qh] != ws_m[z * stride + qh])) continue;
-    const float w = l * exp2f(ws_m[z * stride + qh] - M);
-    wsum += w;
-    const float* op = ws_o + (z * stride + qh) * D;
+  for (int z0 = 0; z0 < splits; z0 += GRP) {
+    float o[GRP][PER];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] += w * op[threadIdx.x + 64 * e];
+    for (int i = 0; i < GRP; ++i) {
+      const int z = min(z0 + i, splits - 1);  // past the splits: the last one again, unused
+      const float* op = ws_o + (z * stride + qh) * D;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) o[i][e] = op[lane + 64 * e];
+    }
+#pragma unroll
+    for (int i = 0; i < GRP; ++i) {
+      const int z = z0 + i;
+      if (z >= splits) break;
+      const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mz), z));
+      const float l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lz), z));
+      if (!(l > 0.0f) && !(m != m)) continue;
+      const float w = l * exp2f(m - M);
+      wsum += w;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] += w * o[i][e];
+    }
   }
   const float inv = 1.0f / wsum;
   f16* orow = out + qh * D;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) orow[threadIdx.x + 64 * e] = static_cast<f16>(acc[e] * inv);
+  for (int e = 0; e < PER; ++e) orow[lane + 64 * e] = static_cast<f16>(acc[e] * inv);
 }
 
 
