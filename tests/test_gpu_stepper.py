@@ -89,3 +89,40 @@ def test_stage_copy_moves_pinned_host_bytes_exactly():
         assert (got[k:] == -7).all()
     # an interior pointer of the pinned allocation maps to the same offset
     assert pa.pa_host_device_pointer(host.data_ptr() + 4096) == src + 4096
+
+
+def test_host_device_pointer_rejects_pageable_memory_and_the_runtime_stays_usable():
+    """Memory the runtime does not hold as pinned gets PA_ERR_INVALID (its
+    sticky runtime error cleared), and later launches still run."""
+    import pagedattention_block_paged_reshape_amd as pa
+    import pagedattention_block_paged_reshape_amd._lib as L
+    pageable = np.zeros(4096, dtype=np.int32)
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_host_device_pointer(pageable.ctypes.data)
+    assert e.value.status == L.PA_ERR_INVALID
+    host = torch.arange(1024, dtype=torch.int32).pin_memory()
+    dst = torch.zeros(1024, dtype=torch.int32, device="cuda:0")
+    pa.pa_stage_copy(pa.pa_host_device_pointer(host), dst, 4096, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert torch.equal(dst.cpu(), host)
+
+
+def test_serving_staging_ring_grows_and_moves_every_section():
+    """The serving loop's staging: sections of both int widths, a buffer
+    that has to grow mid-step, and three steps around the ring; every
+    device view equals its host array."""
+    from pagedattention_block_paged_reshape_amd.serve import _Staging
+    dev = torch.device("cuda:0")
+    st = _Staging(dev, nbytes=256, depth=2)
+    rng = np.random.default_rng(11)
+    stream = torch.cuda.current_stream(dev)
+    for step in range(3):
+        arrays = [rng.integers(-2**31, 2**31 - 1, n).astype(dt)
+                  for n, dt in ((5, np.int64), (3, np.int32), (4000, np.int32), (1, np.int64),
+                                (0, np.int32), (777 + step, np.int64))]
+        st.begin()
+        idx = [st.add(a) for a in arrays]
+        views = st.upload(stream)
+        torch.cuda.synchronize()
+        for i, a in zip(idx, arrays):
+            assert np.array_equal(views[i].cpu().numpy(), a), (step, i)
