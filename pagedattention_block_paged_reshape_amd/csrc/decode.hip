@@ -104,10 +104,9 @@ static pa_status decode_launch(pa_half* out, const pa_half* q, const PoolArgs& k
   if (worklist) {
     if (n_items > 0) {
       // result ring: as many unit slots as fit in ~16 KiB (at least 2)
-      const size_t ring_slot = static_cast<size_t>(G) * D * 2 + 2 * G * sizeof(float) + 16;
+      const size_t ring_slot = walk_ring_slot_bytes(G, D);
       const int ring = static_cast<int>(std::max<size_t>(2, kResultRingBytes / ring_slot));
-      const size_t lds = static_cast<size_t>(kMergeSlots) * kDecodeWaves * G * (D + 4) * sizeof(float) +
-                         static_cast<size_t>(ring) * ring_slot;
+      const size_t lds = walk_merge_bytes(G, D) + static_cast<size_t>(ring) * ring_slot;
       int wph = worklist_resident_wgs(D, keep, kv.fp8, G, lds) / kv.num_kv_heads;
       if (wph < 1) wph = 1;
       if (wph > n_items) wph = n_items;

@@ -788,76 +788,122 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(Decode
     merge_store<D, FP8>(a, ms, g, b, p, u.L, n_parts, lane);
 }
 
-// Work-list form: gridDim.y resident workgroups per kv head walk `items`
-// ((request << 16) | partition, largest first) in a snake deal: in round r
-// workgroup y takes entry r*wph + y, reversed on odd rounds, which gives every
-// workgroup a near-equal share of blocks and leaves the smallest units for
-// last.  While a unit is computed the next unit's block ids are already
-// loaded, and its first block and query rows are in flight during the unit's
-// epilogue.  LDS merge slots rotate over consecutive units so that a fast
-// wavefront can post the next unit while the last one of an earlier unit
-// still merges.
+// LDS of one wavefront pair's work-list walk: kMergeSlots merge slots (per
+// wavefront and head the running max and sum, and the O^T rows), their
+// arrival, bad and merged counters, the pair's give-up flag, and the result
+// ring of `ring` units: (request, partition, partitions, valid), the fp16
+// rows, and each row's max and sum.
+struct WalkLds {
+  float* m;          // [kMergeSlots][kDecodeWaves * 16]
+  float* l;          // [kMergeSlots][kDecodeWaves * 16]
+  int* arrive;       // [kMergeSlots]
+  int* bad;          // [kMergeSlots]
+  int* merged;       // [kMergeSlots]
+  int* abandon;      // one flag
+  float* o;          // [kMergeSlots][kDecodeWaves][G][D + 4]
+  int4* ring_info;   // [ring]
+  f16* ring_o;       // [ring][G][D]
+  float* ring_m;     // [ring][G]
+  float* ring_l;     // [ring][G]
+};
+
+// Bytes of the merge states and of one result-ring unit, for G query heads.
+__host__ __device__ constexpr size_t walk_merge_bytes(int G, int D) {
+  return static_cast<size_t>(kMergeSlots) * kDecodeWaves * G * (D + 4) * sizeof(float);
+}
+__host__ __device__ constexpr size_t walk_ring_slot_bytes(int G, int D) {
+  return static_cast<size_t>(G) * D * 2 + 2 * G * sizeof(float) + 16;
+}
+// One pair's whole LDS as walk_carve lays it out, a multiple of 16 bytes.
+__host__ __device__ constexpr size_t walk_pair_bytes(int G, int D, int ring) {
+  return (walk_merge_bytes(G, D) + 2 * kMergeSlots * kDecodeWaves * 16 * sizeof(float) +
+          16 * ((3 * kMergeSlots + 1 + 3) / 4) + ring * walk_ring_slot_bytes(G, D) + 15) /
+         16 * 16;
+}
+
+// A pair's WalkLds carved from `base` (16-byte aligned), in walk_pair_bytes'
+// layout: merge rows, max, sum, counters, ring info, ring rows, ring max, sum.
+template <int D>
+__device__ __forceinline__ WalkLds walk_carve(char* base, int G, int ring) {
+  WalkLds w;
+  char* p = base;
+  w.o = reinterpret_cast<float*>(p);
+  p += walk_merge_bytes(G, D);
+  w.m = reinterpret_cast<float*>(p);
+  p += kMergeSlots * kDecodeWaves * 16 * sizeof(float);
+  w.l = reinterpret_cast<float*>(p);
+  p += kMergeSlots * kDecodeWaves * 16 * sizeof(float);
+  w.arrive = reinterpret_cast<int*>(p);
+  w.bad = w.arrive + kMergeSlots;
+  w.merged = w.bad + kMergeSlots;
+  w.abandon = w.merged + kMergeSlots;
+  p += 16 * ((3 * kMergeSlots + 1 + 3) / 4);
+  w.ring_info = reinterpret_cast<int4*>(p);
+  w.ring_o = reinterpret_cast<f16*>(w.ring_info + ring);
+  w.ring_m = reinterpret_cast<float*>(w.ring_o + ring * G * D);
+  w.ring_l = w.ring_m + ring * G;
+  return w;
+}
+
+// Units of the snake deal that pair y of wph gets from a list of n_items:
+// every full round, and the last, partial one if it reaches y.
+__device__ __forceinline__ int walk_units(int n_items, int wph, int y) {
+  const int R = n_items / wph;
+  const int rem = n_items % wph;
+  const bool part = rem > 0 && ((R & 1) ? (wph - 1 - y) < rem : y < rem);
+  return R + (part ? 1 : 0);
+}
+
+// The work-list walk of one wavefront pair: pair y of the wph pairs of kv
+// head g walks `items` ((request << 16) | partition, largest first) in a
+// snake deal: in round r pair y takes entry r*wph + y, reversed on odd
+// rounds, which gives every pair a near-equal share of blocks and leaves the
+// smallest units for last.  While a unit is computed the next unit's block
+// ids are already loaded, and its first block and query rows are in flight
+// during the unit's epilogue.  LDS merge slots rotate over consecutive units
+// so that a fast wavefront can post the next unit while the last one of an
+// earlier unit still merges.
 //
 // Merged results are not stored when a unit ends: they go to an LDS ring of
 // `ring` unit slots, written to HBM when the ring is full and when the
-// workgroup's work is done.  On this GPU a wavefront's stores and loads
-// retire in order, so a store issued at a unit's end would make the next
-// unit's first wait also wait for the store's acknowledgement; measured on
-// the Llama-3-70B-shaped layer that cost ~8 % of the launch.
-template <int D, bool KEEP, bool FP8>
-__global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(PA_WL_WAVES_PER_EU)))
-void decode_worklist_kernel(DecodeArgs a, const int32_t* __restrict__ items, int32_t n_items,
-                            int32_t ring) {
-  constexpr int OROW = D + 4;
-  const int g = blockIdx.x;
-  const int wph = gridDim.y;
-  const int y = blockIdx.y;
+// walk is done.  On this GPU a wavefront's stores and loads retire in order,
+// so a store issued at a unit's end would make the next unit's first wait
+// also wait for the store's acknowledgement; measured on the
+// Llama-3-70B-shaped layer that cost ~8 % of the launch.
+//
+// With several pairs in a workgroup (MULTI), every pair runs k_end
+// iterations (the most units any of them has; a pair past its own units runs
+// empty ones), so the ring windows end at the same iterations everywhere and
+// their barriers are the workgroup's; with one pair, k_end is unused and the
+// walk ends with the pair's last unit.  The LDS counters must be zero on
+// entry, behind a barrier.
+template <int D, bool KEEP, bool FP8, bool MULTI>
+__device__ __forceinline__ void worklist_walk(const DecodeArgs& a,
+                                              const int32_t* __restrict__ items,
+                                              int32_t n_items, int32_t ring, int g, int y,
+                                              int wph, int k_end, int wave, int lane,
+                                              const WalkLds& w) {
   const int G = a.G;
-  const int wave = uniform(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-
-  __shared__ float sm_m[kMergeSlots][kDecodeWaves * 16];
-  __shared__ float sm_l[kMergeSlots][kDecodeWaves * 16];
-  __shared__ int sm_arrive[kMergeSlots];
-  __shared__ int sm_bad[kMergeSlots];
-  __shared__ int sm_merged[kMergeSlots];
-  __shared__ int sm_abandon;
-  // dynamic LDS: [kMergeSlots][kDecodeWaves][G][D + 4] floats (merge states),
-  // then the result ring: [ring] (request, partition, partitions, valid),
-  // [ring][G][D] fp16 rows, [ring][G] max, [ring][G] sum
-  extern __shared__ f32x4 sm_o4[];
-  if (threadIdx.x < kMergeSlots) {
-    sm_arrive[threadIdx.x] = 0;
-    sm_bad[threadIdx.x] = 0;
-    sm_merged[threadIdx.x] = 0;
-  }
-  if (threadIdx.x == 0) sm_abandon = 0;
-  __syncthreads();
-  const int slot_floats = kDecodeWaves * G * OROW;
-  int4* ring_info = reinterpret_cast<int4*>(reinterpret_cast<float*>(sm_o4) +
-                                           kMergeSlots * slot_floats);  // 16-byte aligned
-  f16* ring_o = reinterpret_cast<f16*>(ring_info + ring);
-  float* ring_m = reinterpret_cast<float*>(ring_o + ring * G * D);
-  float* ring_l = ring_m + ring * G;
-
+  const int slot_floats = kDecodeWaves * G * (D + 4);
   auto item = [&](int k) { return (k & 1) ? (k + 1) * wph - 1 - y : k * wph + y; };
+  auto has = [&](int k) { return (!MULTI || k < k_end) && item(k) < n_items; };
   auto unit_at = [&](int t) {
     return make_entry_unit(a, static_cast<uint32_t>(scalar_load(items, t)), wave, lane);
   };
-  // Give up on this workgroup's remaining work: mark it abandoned for the
-  // other wavefront, then write NaN rows (and NaN max and sum) to the
-  // destination of every unit of the deal from entry index k0 on.  Units
-  // before k0 were flushed; the rest are in the LDS ring or not yet done,
-  // and which of those are whole cannot be told, so all of them read as
-  // bad.  Both wavefronts may do this; they write the same values.
+  // Give up on this pair's remaining work: mark it abandoned for the other
+  // wavefront, then write NaN rows (and NaN max and sum) to the destination
+  // of every unit of the deal from entry index k0 on.  Units before k0 were
+  // flushed; the rest are in the LDS ring or not yet done, and which of
+  // those are whole cannot be told, so all of them read as bad.  Both
+  // wavefronts may do this; they write the same values.
   auto abandon = [&](int k0) {
     if (lane == 0)
-      __hip_atomic_store(&sm_abandon, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_store(w.abandon, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     const float nan = __builtin_nanf("");
     const f16 hn = static_cast<f16>(nan);
     const f16x8 nan8 = {hn, hn, hn, hn, hn, hn, hn, hn};
-    for (int t = k0; item(t) < n_items; ++t) {
+    for (int t = k0; has(t); ++t) {
       int b, p, n_parts;
       if (!entry_unit(a, static_cast<uint32_t>(scalar_load(items, item(t))), b, p, n_parts))
         continue;
@@ -866,35 +912,36 @@ void decode_worklist_kernel(DecodeArgs a, const int32_t* __restrict__ items, int
     }
   };
   auto abandoned = [&]() {
-    return __hip_atomic_load(&sm_abandon, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
+    return __hip_atomic_load(w.abandon, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
   };
   // both wavefronts: write ring slots 0 .. count-1 to their global rows
   auto flush = [&](int count) {
     for (int j = wave; j < count; j += kDecodeWaves) {
-      const int4 info = ring_info[j];  // request, partition, partitions, valid
+      const int4 info = w.ring_info[j];  // request, partition, partitions, valid
       if (info.w == 0) continue;
       for (int idx = lane; idx < G * (D / 8); idx += kWave) {
         const int h = idx / (D / 8);
         const int d0 = (idx % (D / 8)) * 8;
-        const f16x8 r = *reinterpret_cast<const f16x8*>(ring_o + (j * G + h) * D + d0);
-        store_rows<D>(a, g, info.x, info.y, info.z, h, d0, r, ring_m[j * G + h],
-                      ring_l[j * G + h]);
+        const f16x8 r = *reinterpret_cast<const f16x8*>(w.ring_o + (j * G + h) * D + d0);
+        store_rows<D>(a, g, info.x, info.y, info.z, h, d0, r, w.ring_m[j * G + h],
+                      w.ring_l[j * G + h]);
       }
     }
   };
 
-  if (item(0) >= n_items) return;
-  Unit u = unit_at(item(0));
+  if (MULTI ? k_end <= 0 : !has(0)) return;
+  Unit u = has(0) ? unit_at(item(0)) : no_unit();
   typedef TileRegs<D, FP8> TR;
   f16x8 qf[D / 32];
   typename TR::K kA[TR::NB * TR::NK], kB[TR::NB * TR::NK];
   typename TR::V vA[TR::NB * TR::NV], vB[TR::NB * TR::NV];
-  load_q<D>(a, g, u.b, lane, qf);
+  if (has(0)) load_q<D>(a, g, u.b, lane, qf);
   if (u.cnt > 0) load_set<D, KEEP, FP8>(a, g, u, no_unit(), 0, true, lane, kA, vA);
 
   int stop_k0 = 0;  // set when the loop is left early: the window to mark bad
   for (int k = 0;; ++k) {
-    const bool more = item(k + 1) < n_items;
+    const bool more = has(k + 1);
+    const bool last = MULTI ? k + 1 == k_end : !more;
     const Unit nx = more ? unit_at(item(k + 1)) : no_unit();
     WaveState<D> st;
     run_unit<D, KEEP, FP8>(a, g, wave, lane, u, nx, qf, kA, vA, kB, vB, st);
@@ -908,7 +955,7 @@ void decode_worklist_kernel(DecodeArgs a, const int32_t* __restrict__ items, int
     // rather than left stale, and the wavefront ends.
     int spins = 0;
     bool give_up = false;
-    while (__hip_atomic_load(&sm_merged[buf], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) !=
+    while (__hip_atomic_load(&w.merged[buf], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) !=
            k / kMergeSlots) {
       if (++spins > a.spin_limit || abandoned()) {
         give_up = true;
@@ -920,29 +967,28 @@ void decode_worklist_kernel(DecodeArgs a, const int32_t* __restrict__ items, int
       stop_k0 = k0;
       break;
     }
-    const MergeSlot<D> ms{sm_m[buf], sm_l[buf],
-                          reinterpret_cast<float*>(sm_o4) + buf * slot_floats, &sm_arrive[buf],
-                          &sm_bad[buf]};
+    const MergeSlot<D> ms{w.m + buf * kDecodeWaves * 16, w.l + buf * kDecodeWaves * 16,
+                          w.o + buf * slot_floats, &w.arrive[buf], &w.bad[buf]};
     const int rs = k % ring;  // this unit's result slot
     if (post_state<D>(ms, st, G, wave, lane, u.bad)) {
       if (u.ok) {
         merge_unit<D, FP8>(ms, G, u.L, lane, a.v_scale,
                            [&](int h, int d0, f16x8 r, float m, float l) {
-          *reinterpret_cast<f16x8*>(ring_o + (rs * G + h) * D + d0) = r;
+          *reinterpret_cast<f16x8*>(w.ring_o + (rs * G + h) * D + d0) = r;
           if (d0 == 0) {
-            ring_m[rs * G + h] = m;
-            ring_l[rs * G + h] = l;
+            w.ring_m[rs * G + h] = m;
+            w.ring_l[rs * G + h] = l;
           }
         });
       }
       if (lane == 0) {
-        ring_info[rs] = int4{u.b, u.p, u.n_parts, u.ok ? 1 : 0};
-        sm_arrive[buf] = 0;
-        sm_bad[buf] = 0;
-        __hip_atomic_fetch_add(&sm_merged[buf], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        w.ring_info[rs] = int4{u.b, u.p, u.n_parts, u.ok ? 1 : 0};
+        w.arrive[buf] = 0;
+        w.bad[buf] = 0;
+        __hip_atomic_fetch_add(&w.merged[buf], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
     }
-    if (!more || rs == ring - 1) {
+    if (last || rs == ring - 1) {
       // every unit in the ring has been merged once both wavefronts get here
       // (a wavefront that gave up has ended, and the barrier waits only for
       // the other one, which then writes the window as NaN instead)
@@ -952,12 +998,51 @@ void decode_worklist_kernel(DecodeArgs a, const int32_t* __restrict__ items, int
         break;
       }
       flush(rs + 1);
-      if (!more) return;
+      if (last) return;
       __syncthreads();  // the ring is read out before the next unit reuses slot 0
     }
     u = nx;
   }
   abandon(stop_k0);
+}
+
+// Work-list form: gridDim.y resident workgroups of one wavefront pair each
+// per kv head; workgroup (g, y) is pair y of kv head g's walk.
+template <int D, bool KEEP, bool FP8>
+__global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(PA_WL_WAVES_PER_EU)))
+void decode_worklist_kernel(DecodeArgs a, const int32_t* __restrict__ items, int32_t n_items,
+                            int32_t ring) {
+  __shared__ float sm_m[kMergeSlots * kDecodeWaves * 16];
+  __shared__ float sm_l[kMergeSlots * kDecodeWaves * 16];
+  __shared__ int sm_arrive[kMergeSlots];
+  __shared__ int sm_bad[kMergeSlots];
+  __shared__ int sm_merged[kMergeSlots];
+  __shared__ int sm_abandon;
+  // dynamic LDS: the merge rows, then the result ring
+  extern __shared__ f32x4 sm_o4[];
+  if (threadIdx.x < kMergeSlots) {
+    sm_arrive[threadIdx.x] = 0;
+    sm_bad[threadIdx.x] = 0;
+    sm_merged[threadIdx.x] = 0;
+  }
+  if (threadIdx.x == 0) sm_abandon = 0;
+  __syncthreads();
+  const int G = a.G;
+  WalkLds w;
+  w.m = sm_m;
+  w.l = sm_l;
+  w.arrive = sm_arrive;
+  w.bad = sm_bad;
+  w.merged = sm_merged;
+  w.abandon = &sm_abandon;
+  w.o = reinterpret_cast<float*>(sm_o4);
+  w.ring_info = reinterpret_cast<int4*>(w.o + kMergeSlots * kDecodeWaves * G * (D + 4));
+  w.ring_o = reinterpret_cast<f16*>(w.ring_info + ring);
+  w.ring_m = reinterpret_cast<float*>(w.ring_o + ring * G * D);
+  w.ring_l = w.ring_m + ring * G;
+  worklist_walk<D, KEEP, FP8, false>(a, items, n_items, ring, blockIdx.x, blockIdx.y,
+                                     gridDim.y, 0, uniform(threadIdx.x >> 6), threadIdx.x & 63,
+                                     w);
 }
 
 // Both pool types: pools, geometry and (FP8) scales, then the shared checks

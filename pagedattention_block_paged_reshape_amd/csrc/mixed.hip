@@ -6,15 +6,17 @@
 // summary, "the scheduler").  Workgroups of the prefill launch's size (8
 // wavefronts with fp16 pools, 4 with FP8 ones); the first pf_wgs take prefill
 // tiles (kv head fastest, then query tile, then key split, as the prefill
-// launch's grid), the rest decode units, one per wavefront pair (so 4 or 2
-// per workgroup), each as in the grid form.  The prefill tiles, being the
-// long work, start first; decode units fill the CUs as tiles retire, so the
-// chunk's ragged end and the launch gap between the two kinds of work
-// overlap with memory-bound decode.  Decode unit t of kv head g is entry t
-// of the work list; the workgroup that holds entries P*j .. P*j + P - 1 of kv
-// head g (P pairs) is number pf_wgs + j*n_kv + g, so with 8 kv heads and
-// pf_wgs a multiple of 8 each head's decode units land on one XCD, as in the
-// decode launch.
+// launch's grid), the rest walk the decode work list as the decode launch's
+// work-list form does, one walk per wavefront pair (up to 4 or 2 per
+// workgroup): as many decode workgroups as stay resident, so that once the
+// tiles retire every CU streams K/V with the next unit's loads in flight
+// during each unit's epilogue and merged rows buffered in an LDS ring.  The
+// prefill tiles, being the long work, start first; decode workgroups fill
+// the CUs as tiles retire, so the chunk's ragged end and the launch gap
+// between the two kinds of work overlap with memory-bound decode.  Decode
+// workgroup j (after the tiles) holds pairs pairs*(j / n_kv) .. of kv head
+// j % n_kv, so with 8 kv heads and pf_wgs a multiple of 8 each head's decode
+// units land on one XCD, as in the decode launch.
 #include <type_traits>
 
 #include "decode_core.h"
@@ -28,30 +30,18 @@ constexpr int mixed_threads() {
   return FP8 ? kPfThreads : kPfPPThreads;
 }
 
-// LDS of a mixed workgroup: one prefill tile's, or P decode units' merge
-// states ([pair][wave][16] max and sum, [pair][wave][G <= 16][D + 4] O^T rows).
-template <int D, int P>
-struct MixedDecodeLds {
-  __attribute__((aligned(16))) float o[P][kDecodeWaves * 16 * (D + 4)];
-  float m[P][kDecodeWaves * 16];
-  float l[P][kDecodeWaves * 16];
-  int arrive[P];
-  int bad[P];
-};
-
+// LDS of a mixed workgroup (dynamic): one prefill tile's, or the walk state
+// of its decode pairs (walk_pair_bytes each), whichever is larger.
 template <int D, bool FP8>
-union MixedLds {
-  static constexpr int P = mixed_threads<FP8>() / (kDecodeWaves * kWave);  // decode units
-  typename std::conditional<FP8, PrefillLds<D>, PrefillLdsPP<D>>::type pf;
-  MixedDecodeLds<D, P> dec;
-};
+constexpr size_t mixed_tile_lds() {
+  return FP8 ? sizeof(PrefillLds<D>) : sizeof(PrefillLdsPP<D>);
+}
 
 template <int D, bool KEEP, bool FP8>
 __global__ __launch_bounds__(mixed_threads<FP8>()) void mixed_step_kernel(
     PrefillArgs pa, int32_t pf_wgs, int32_t pf_qtiles, DecodeArgs da,
-    const int32_t* __restrict__ items, int32_t n_items) {
-  __shared__ MixedLds<D, FP8> lds;
-  constexpr int P = MixedLds<D, FP8>::P;
+    const int32_t* __restrict__ items, int32_t n_items, int32_t pairs, int32_t ring) {
+  extern __shared__ f32x4 mixed_lds[];
   const int wg = blockIdx.x;
   if (wg < pf_wgs) {
     const int rest = wg / pa.n_kv;
@@ -61,39 +51,39 @@ __global__ __launch_bounds__(mixed_threads<FP8>()) void mixed_step_kernel(
     // when decode units ran at a higher priority, vs 607 us without).  The
     // fp16 tile fills its CU alone (two wavefronts per SIMD at ~211 VGPRs).
     if constexpr (FP8)
-      prefill_tile<D, 0, FP8>(pa, wg % pa.n_kv, rest % pf_qtiles, rest / pf_qtiles, lds.pf);
+      prefill_tile<D, 0, FP8>(pa, wg % pa.n_kv, rest % pf_qtiles, rest / pf_qtiles,
+                              *reinterpret_cast<PrefillLds<D>*>(mixed_lds));
     else
-      prefill_tile_pp<D>(pa, wg % pa.n_kv, rest % pf_qtiles, rest / pf_qtiles, lds.pf);
+      prefill_tile_pp<D>(pa, wg % pa.n_kv, rest % pf_qtiles, rest / pf_qtiles,
+                         *reinterpret_cast<PrefillLdsPP<D>*>(mixed_lds));
     return;
   }
-  if (threadIdx.x < P) {
-    lds.dec.arrive[threadIdx.x] = 0;
-    lds.dec.bad[threadIdx.x] = 0;
+  const int G = da.G;
+  char* const base = reinterpret_cast<char*>(mixed_lds);
+  const size_t pair_bytes = walk_pair_bytes(G, D, ring);
+  if (static_cast<int>(threadIdx.x) < pairs) {
+    const WalkLds w = walk_carve<D>(base + threadIdx.x * pair_bytes, G, ring);
+#pragma unroll
+    for (int i = 0; i < kMergeSlots; ++i) {
+      w.arrive[i] = 0;
+      w.bad[i] = 0;
+      w.merged[i] = 0;
+    }
+    *w.abandon = 0;
   }
   __syncthreads();
-  const int j = wg - pf_wgs;
   const int pair = uniform(threadIdx.x >> 7);
-  const int wave = uniform((threadIdx.x >> 6) & 1);
-  const int lane = threadIdx.x & 63;
-  const int g = j % da.n_kv;
-  const int t = P * (j / da.n_kv) + pair;
-  if (t >= n_items) return;
-  const Unit u = make_entry_unit(da, static_cast<uint32_t>(scalar_load(items, t)), wave, lane);
-  const Unit nx = no_unit();
-  typedef TileRegs<D, FP8> TR;
-  f16x8 qf[D / 32];
-  typename TR::K kA[TR::NB * TR::NK], kB[TR::NB * TR::NK];
-  typename TR::V vA[TR::NB * TR::NV], vB[TR::NB * TR::NV];
-  if (u.cnt > 0) {
-    load_q<D>(da, g, u.b, lane, qf);
-    load_set<D, KEEP, FP8>(da, g, u, nx, 0, true, lane, kA, vA);
-  }
-  WaveState<D> st;
-  run_unit<D, KEEP, FP8>(da, g, wave, lane, u, nx, qf, kA, vA, kB, vB, st);
-  const MergeSlot<D> ms{lds.dec.m[pair], lds.dec.l[pair], lds.dec.o[pair], &lds.dec.arrive[pair],
-                        &lds.dec.bad[pair]};
-  if (post_state<D>(ms, st, da.G, wave, lane, u.bad) && u.ok)
-    merge_store<D, FP8>(da, ms, g, u.b, u.p, u.L, u.n_parts, lane);
+  if (pair >= pairs) return;
+  const int j = wg - pf_wgs;
+  const int n_kv = da.n_kv;
+  const int g = j % n_kv;
+  const int wph = (static_cast<int>(gridDim.x) - pf_wgs) / n_kv * pairs;  // pairs per kv head
+  const int y0 = (j / n_kv) * pairs;
+  int k_end = 0;  // the most units any pair of this workgroup has
+  for (int p = 0; p < pairs; ++p) k_end = max(k_end, walk_units(n_items, wph, y0 + p));
+  worklist_walk<D, KEEP, FP8, true>(da, items, n_items, ring, g, y0 + pair, wph, k_end,
+                              uniform((threadIdx.x >> 6) & 1), threadIdx.x & 63,
+                              walk_carve<D>(base + pair * pair_bytes, G, ring));
 }
 
 // Merges after the mixed step's kernel: the prefill (row, head) pairs whose
@@ -122,17 +112,67 @@ static uint64_t mixed_decode_ws(const pa_decode_batch& d, int32_t num_q_heads, i
   return (b + kMixedWsAlign - 1) / kMixedWsAlign * kMixedWsAlign;
 }
 
+template <int D, bool KEEP, bool FP8>
+static const void* step_kernel() {
+  return reinterpret_cast<const void*>(&mixed_step_kernel<D, KEEP, FP8>);
+}
+
+static const void* pick_step_kernel(int D, bool keep, bool fp8) {
+  if (D == 128) {
+    if (fp8) return keep ? step_kernel<128, true, true>() : step_kernel<128, false, true>();
+    return keep ? step_kernel<128, true, false>() : step_kernel<128, false, false>();
+  }
+  if (fp8) return keep ? step_kernel<64, true, true>() : step_kernel<64, false, true>();
+  return keep ? step_kernel<64, true, false>() : step_kernel<64, false, false>();
+}
+
 template <bool KEEP, bool FP8>
-static void launch_step(int D, dim3 grid, hipStream_t s, const PrefillArgs& pa, int32_t pf_wgs,
-                        int32_t qtiles, const DecodeArgs& da, const int32_t* items,
-                        int32_t n_items) {
+static void launch_step(int D, dim3 grid, size_t lds, hipStream_t s, const PrefillArgs& pa,
+                        int32_t pf_wgs, int32_t qtiles, const DecodeArgs& da,
+                        const int32_t* items, int32_t n_items, int32_t pairs, int32_t ring) {
   const dim3 block(mixed_threads<FP8>());
   if (D == 128)
-    mixed_step_kernel<128, KEEP, FP8><<<grid, block, 0, s>>>(pa, pf_wgs, qtiles, da, items,
-                                                             n_items);
+    mixed_step_kernel<128, KEEP, FP8><<<grid, block, lds, s>>>(pa, pf_wgs, qtiles, da, items,
+                                                               n_items, pairs, ring);
   else
-    mixed_step_kernel<64, KEEP, FP8><<<grid, block, 0, s>>>(pa, pf_wgs, qtiles, da, items,
-                                                            n_items);
+    mixed_step_kernel<64, KEEP, FP8><<<grid, block, lds, s>>>(pa, pf_wgs, qtiles, da, items,
+                                                              n_items, pairs, ring);
+}
+
+// LDS that a mixed workgroup may take: all of a CU's for fp16 pools (the
+// tile holds its CU alone), half of it for FP8 ones (two tiles per CU).
+constexpr size_t kMixedLdsFp16 = 160 * 1024;
+constexpr size_t kMixedLdsFp8 = 80 * 1024;
+
+// Resident mixed workgroups on the current device at this LDS size (CUs
+// times the kernel's occupancy), after allowing the kernel that much dynamic
+// LDS; both are asked of the runtime once per (device, kernel, LDS size) and
+// thread.  0 when the runtime refuses.
+static int mixed_resident_wgs(const void* fn, int threads, size_t lds) {
+  struct Entry {
+    const void* fn;
+    size_t lds;
+    int dev;
+    int wgs;
+  };
+  thread_local Entry cache[16] = {};
+  thread_local int next = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  for (const Entry& e : cache)
+    if (e.fn == fn && e.lds == lds && e.dev == dev) return e.wgs;
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          static_cast<int>(lds)) != hipSuccess)
+    return 0;
+  int n = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, threads, lds) != hipSuccess || n < 1)
+    n = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    cus = 1;
+  cache[next] = Entry{fn, lds, dev, n * cus};
+  next = (next + 1) % 16;
+  return n * cus;
 }
 
 // Both pool types: k_pool / v_pool hold fp16 values or (fp8) E4M3 codes with
@@ -176,29 +216,55 @@ static pa_status mixed_launch(const pa_decode_batch* dec, const pa_prefill_chunk
     pgrid.y = static_cast<uint32_t>((pf->chunk_len + kPfPPMRows / pa.G - 1) / (kPfPPMRows / pa.G));
   const int64_t pf_wgs =
       pf->chunk_len > 0 ? static_cast<int64_t>(pgrid.x) * pgrid.y * pgrid.z : 0;
-  // decode units per workgroup: one per wavefront pair
-  const int P = (fp8 ? mixed_threads<true>() : mixed_threads<false>()) / (kDecodeWaves * kWave);
-  const int64_t dec_wgs =
-      dec->batch > 0 ? static_cast<int64_t>(kv.num_kv_heads) * ((dec->n_items + P - 1) / P) : 0;
-  if (pf_wgs + dec_wgs > 0x7FFFFFFF) return PA_ERR_INVALID;
-  if (pf_wgs + dec_wgs == 0) return PA_OK;
   const bool keep = (flags & PA_DECODE_KEEP_KV) != 0;
   const int D = kv.head_dim;
+  const int threads = fp8 ? mixed_threads<true>() : mixed_threads<false>();
+  const size_t tile_lds = fp8 ? (D == 128 ? mixed_tile_lds<128, true>() : mixed_tile_lds<64, true>())
+                              : (D == 128 ? mixed_tile_lds<128, false>() : mixed_tile_lds<64, false>());
+  // decode walks: one per wavefront pair, with as large a result ring (up to
+  // ~16 KiB, at least 2 units) and as many pairs as the LDS allows
+  const int32_t n_items = dec->batch > 0 ? dec->n_items : 0;
+  int pairs = threads / (kDecodeWaves * kWave);
+  const size_t slot = walk_ring_slot_bytes(da.G, D);
+  int ring = static_cast<int>(std::max<size_t>(2, kResultRingBytes / slot));
+  const size_t budget = fp8 ? kMixedLdsFp8 : kMixedLdsFp16;
+  while (ring > 2 && pairs * walk_pair_bytes(da.G, D, ring) > budget) --ring;
+  while (pairs > 1 && pairs * walk_pair_bytes(da.G, D, ring) > budget) --pairs;
+  const size_t lds =
+      std::max(tile_lds, n_items > 0 ? pairs * walk_pair_bytes(da.G, D, ring) : size_t{0});
+  if (lds > budget) return PA_ERR_INVALID;  // not reached for G <= 16, D <= 128
+  if (pf_wgs == 0 && n_items == 0) return PA_OK;  // nothing to launch
+  const int resident = mixed_resident_wgs(pick_step_kernel(D, keep, fp8), threads, lds);
+  if (resident < 1) return PA_ERR_HIP;
+  // as many decode workgroups as stay resident, a multiple of n_kv, each kv
+  // head's pairs no more than its units
+  int64_t dec_wgs = 0;
+  if (n_items > 0) {
+    int64_t per_head = resident / kv.num_kv_heads;
+    per_head = std::min<int64_t>(per_head, (n_items + pairs - 1) / pairs);
+    per_head = std::max<int64_t>(per_head, 1);
+    dec_wgs = per_head * kv.num_kv_heads;
+  }
+  if (pf_wgs + dec_wgs > 0x7FFFFFFF) return PA_ERR_INVALID;
+  if (pf_wgs + dec_wgs == 0) return PA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid(static_cast<uint32_t>(pf_wgs + dec_wgs));
   const int32_t qtiles = static_cast<int32_t>(pgrid.y);
-  const int32_t n_items = dec->batch > 0 ? dec->n_items : 0;
   const int32_t pw = static_cast<int32_t>(pf_wgs);
   if (fp8) {
     if (keep)
-      launch_step<true, true>(D, grid, s, pa, pw, qtiles, da, dec->work_items, n_items);
+      launch_step<true, true>(D, grid, lds, s, pa, pw, qtiles, da, dec->work_items, n_items,
+                              pairs, ring);
     else
-      launch_step<false, true>(D, grid, s, pa, pw, qtiles, da, dec->work_items, n_items);
+      launch_step<false, true>(D, grid, lds, s, pa, pw, qtiles, da, dec->work_items, n_items,
+                               pairs, ring);
   } else {
     if (keep)
-      launch_step<true, false>(D, grid, s, pa, pw, qtiles, da, dec->work_items, n_items);
+      launch_step<true, false>(D, grid, lds, s, pa, pw, qtiles, da, dec->work_items, n_items,
+                               pairs, ring);
     else
-      launch_step<false, false>(D, grid, s, pa, pw, qtiles, da, dec->work_items, n_items);
+      launch_step<false, false>(D, grid, lds, s, pa, pw, qtiles, da, dec->work_items, n_items,
+                                pairs, ring);
   }
   if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   if (pf->chunk_len > 0 && pa.splits > 1) {

@@ -242,6 +242,22 @@ def test_fp8_mixed_equals_separate_launches_and_oracle(decode_lengths, q_start, 
         f"decode {err:.2e}, prefill {errp:.2e}")
 
 
+def test_fp8_mixed_many_units_per_walk():
+    """One-block partitions: several decode units per wavefront pair in the
+    FP8 mixed launch (two pairs per workgroup, pairs of one workgroup with
+    different unit counts), bitwise the separate FP8 launches."""
+    w = make_mixed_workload([8000, 6000, 3000, 900, 40, 2], 300, 64, n_q=32, n_kv=8, d=128,
+                            seed=91)
+    st = oracle_run(w, kv_dtype="fp8", k_scale=K_SCALE, v_scale=V_SCALE)
+    res = gpu_run(w, kv_dtype="fp8", k_scale=K_SCALE, v_scale=V_SCALE, partition=16)
+    _, d_out, p_out = _run_mixed_fp8(w, res, partition=16)
+    assert torch.equal(d_out.view(torch.int16), res["decode"].view(torch.int16))
+    assert torch.equal(p_out.view(torch.int16), res["prefill"].view(torch.int16))
+    err = assert_close(d_out, decode_reference(w, st), "fp8 mixed decode, one-block partitions")
+    assert_close(p_out, prefill_reference(w, st), "fp8 mixed prefill")
+    log(f"fp8 mixed, one-block partitions: decode {err:.2e}")
+
+
 def test_fp8_config5_mixed_launch_and_scale_checks():
     """The long-context step over FP8 pools at full size: bitwise the separate
     FP8 launches; both outputs against the oracle in full.  Non-positive or

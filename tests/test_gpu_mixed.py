@@ -49,6 +49,11 @@ def bitwise_equal(a, b):
     ([2000], 90, 50, 16, 1, 128, 512),                 # G = 16
     ([300, 45, 1100], 250, 130, 8, 2, 64, 512),        # head_dim 64
     ([4096, 3, 129], 4093, 512, 32, 8, 128, 512),      # several key splits
+    # many units per decode walk (one-block partitions): several units per
+    # wavefront pair, pairs of one workgroup with different unit counts
+    ([8000, 6000, 3000, 900, 40, 2], 300, 64, 32, 8, 128, 16),
+    # G = 16: three pairs per workgroup and a 2-unit result ring that wraps
+    ([12000, 12000, 12000, 1000], 100, 64, 16, 1, 128, 16),
 ])
 def test_mixed_equals_separate_launches_and_oracle(decode_lengths, q_start, chunk, n_q, n_kv,
                                                     d, partition):
@@ -139,3 +144,38 @@ def test_mixed_with_one_part_empty():
         pa.pa_paged_attention_mixed(dec, chunk, res["cache"].kv, w.n_q - 1, w.scale,
                                     plan.workspace, plan.ws_bytes)
     assert np.isfinite(d_out.float().cpu().numpy()).all()
+
+
+def test_mixed_decode_give_up_writes_nan_not_stale_rows(monkeypatch):
+    """The mixed launch's decode walks have the decode launch's bounded LDS
+    slot wait.  With the bound forced to 0 rounds from the host (a test hook;
+    every wait still ends) a wavefront that finds a slot still busy gives up:
+    every decode row is then NaN or bitwise the normal run's, the chunk's rows
+    are exact, and a normal launch afterwards is bitwise the separate
+    launches again."""
+    w = make_mixed_workload([8000, 6000, 3000, 900, 40, 2], 300, 64, n_q=32, n_kv=8, d=128,
+                            seed=83)
+    res = gpu_run(w, partition=16)
+    plan, d_out, p_out = run_mixed(w, res, 16)
+    assert bitwise_equal(d_out, res["decode"]) and bitwise_equal(p_out, res["prefill"])
+    good = d_out.float().cpu().numpy()
+    q = torch.from_numpy(w.q).to(res["cache"].device)
+    qc = torch.from_numpy(w.prefill.q).to(res["cache"].device)
+    monkeypatch.setenv("PA_DECODE_SPIN_LIMIT", "0")
+    nan_rows = 0
+    for rep in range(5):
+        plan.dec.out.fill_(3.0)              # stale contents the give-up must not leave
+        a, b = plan.run(q, qc)
+        torch.cuda.synchronize()
+        got = a.float().cpu().numpy()
+        is_nan = np.isnan(got).all(axis=-1)
+        same = (got.view(np.uint32) == good.view(np.uint32)).all(axis=-1)
+        assert (is_nan | same).all(), "a decode row is neither NaN nor the normal result"
+        assert bitwise_equal(b, p_out), "the chunk's rows changed"
+        nan_rows += int(is_nan.sum())
+    monkeypatch.delenv("PA_DECODE_SPIN_LIMIT")
+    a, b = plan.run(q, qc)
+    torch.cuda.synchronize()
+    assert bitwise_equal(a, res["decode"]) and bitwise_equal(b, res["prefill"])
+    log(f"mixed give-up: {nan_rows} of {5 * good.shape[0] * good.shape[1]} decode rows NaN "
+        f"over 5 runs")
