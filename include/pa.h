@@ -388,6 +388,22 @@ pa_status pa_host_device_pointer(const void* host, void** device);
  * size that is not a multiple of 16.  Async on `stream`. */
 pa_status pa_stage_copy(const void* src, void* dst, uint64_t bytes, void* stream);
 
+/* pa_stage_copy plus word updates, in one launch: `bytes` from src to dst as
+ * pa_stage_copy moves them, and for each of the n_updates int32 pairs
+ * (index, value) at `updates`, target[index] = value.  For a device-resident
+ * block table refreshed each step ([lens] scheduler skeleton) with only the
+ * entries that changed since the previous step (a request that took a new
+ * block or a copy-on-write replacement), instead of the whole padded table.
+ * src, updates: device addresses (those of pinned host memory included);
+ * src, dst 16-byte aligned, bytes a multiple of 16; updates 8-byte aligned;
+ * target: device int32 [target_len], 4-byte aligned.  Indices outside
+ * [0, target_len) are skipped; the indices should be distinct (a repeated
+ * one takes one of its values).  dst and target must not overlap.
+ * PA_ERR_INVALID on a null pointer with a nonzero count, misalignment, a
+ * negative count or target_len > INT32_MAX.  Async on `stream`. */
+pa_status pa_stage_update(const void* src, void* dst, uint64_t bytes, const int32_t* updates,
+                          int64_t n_updates, int32_t* target, int64_t target_len, void* stream);
+
 /* Swap transfers: whole K and V tiles (all kv heads) of n blocks between the
  * pools and contiguous buffers [n][num_kv_heads][16*D] fp16 in the pools'
  * tile order (a bit copy; the caller moves the buffers to and from host

@@ -155,6 +155,7 @@ _SIGS = {
     "pa_seq_swap_in": (C.c_int, [_P, _I64, _I32, _P, _I32, C.POINTER(_I32)]),
     "pa_host_device_pointer": (C.c_int, [_P, C.POINTER(C.c_void_p)]),
     "pa_stage_copy": (C.c_int, [_P, _P, C.c_uint64, _P]),
+    "pa_stage_update": (C.c_int, [_P, _P, C.c_uint64, _P, C.c_int64, _P, C.c_int64, _P]),
     "pa_gather_blocks": (C.c_int, [_P, _I32, pa_kv_view, _P, _P, _P]),
     "pa_scatter_blocks": (C.c_int, [_P, _I32, pa_kv_view, _P, _P, _P]),
     "pa_gather_blocks_fp8": (C.c_int, [_P, _I32, pa_kv_view_fp8, _P, _P, _P]),
@@ -620,6 +621,13 @@ def pa_host_device_pointer(host) -> int:
 def pa_stage_copy(src, dst, nbytes: int, stream=None) -> None:
     _check(LIB.pa_stage_copy(_dptr(src), _dptr(dst), int(nbytes), _stream(stream)),
            "pa_stage_copy")
+
+
+def pa_stage_update(src, dst, nbytes: int, updates, n_updates: int, target, target_len: int,
+                    stream=None) -> None:
+    _check(LIB.pa_stage_update(_dptr(src), _dptr(dst), int(nbytes), _dptr(updates),
+                               int(n_updates), _dptr(target), int(target_len), _stream(stream)),
+           "pa_stage_update")
 
 
 def pa_gather_blocks(blocks, n: int, kv, k_out, v_out, stream=None) -> None:

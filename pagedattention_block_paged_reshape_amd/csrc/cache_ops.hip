@@ -360,6 +360,30 @@ __global__ __launch_bounds__(256) void stage_copy_kernel(const u32x4* __restrict
 
 }  // namespace pa
 
+namespace pa {
+
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+
+// The staging copy plus word updates: threads below n copy 16-byte chunks
+// as stage_copy_kernel does; update j (an (index, value) int32 pair) is
+// applied by thread j, target[index] = value when the index is in range.
+__global__ __launch_bounds__(256) void stage_update_kernel(const u32x4* __restrict__ src,
+                                                           u32x4* __restrict__ dst, int64_t n,
+                                                           const i32x2* __restrict__ updates,
+                                                           int64_t n_updates,
+                                                           int32_t* __restrict__ target,
+                                                           int64_t target_len) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  for (int64_t i = t0; i < n; i += stride) dst[i] = __builtin_nontemporal_load(src + i);
+  for (int64_t j = t0; j < n_updates; j += stride) {
+    const i32x2 u = __builtin_nontemporal_load(updates + j);
+    if (u[0] >= 0 && u[0] < target_len) target[u[0]] = u[1];
+  }
+}
+
+}  // namespace pa
+
 extern "C" pa_status pa_stage_copy(const void* src, void* dst, uint64_t bytes, void* stream) {
   if (src == nullptr || dst == nullptr) return PA_ERR_INVALID;
   if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst) | bytes) & 15u)
@@ -372,3 +396,25 @@ extern "C" pa_status pa_stage_copy(const void* src, void* dst, uint64_t bytes, v
       reinterpret_cast<const pa::u32x4*>(src), reinterpret_cast<pa::u32x4*>(dst), n);
   return pa::launch_status();
 }
+
+extern "C" pa_status pa_stage_update(const void* src, void* dst, uint64_t bytes,
+                                     const int32_t* updates, int64_t n_updates, int32_t* target,
+                                     int64_t target_len, void* stream) {
+  if (n_updates < 0 || target_len < 0 || target_len > INT32_MAX) return PA_ERR_INVALID;
+  if (bytes > 0 && (src == nullptr || dst == nullptr)) return PA_ERR_INVALID;
+  if (n_updates > 0 && (updates == nullptr || target == nullptr)) return PA_ERR_INVALID;
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst) | bytes) & 15u)
+    return PA_ERR_INVALID;
+  if ((reinterpret_cast<uintptr_t>(updates) & 7u) || (reinterpret_cast<uintptr_t>(target) & 3u))
+    return PA_ERR_INVALID;
+  const int64_t n = static_cast<int64_t>(bytes / 16);
+  const int64_t work = n > n_updates ? n : n_updates;
+  if (work == 0) return PA_OK;
+  const int64_t wgs = work < 256 * 256 ? (work + 255) / 256 : 256;
+  pa::stage_update_kernel<<<dim3(static_cast<uint32_t>(wgs)), dim3(256), 0,
+                            static_cast<hipStream_t>(stream)>>>(
+      reinterpret_cast<const pa::u32x4*>(src), reinterpret_cast<pa::u32x4*>(dst), n,
+      reinterpret_cast<const pa::i32x2*>(updates), n_updates, target, target_len);
+  return pa::launch_status();
+}
+

@@ -5,15 +5,20 @@ the step's new K/V (``pa_reshape_and_cache``, or its FP8 form for FP8
 pools), refreshes the device block tables (``pa_block_tables``) and attends
 (``pa_paged_attention_decode`` / ``_fp8``), all enqueued on one stream (the
 scheduler loop of ta-paperlens: blocks are reserved for every running
-request before the step's forward pass).  The step's slots, tables, lengths
-and work list sit in one pinned host buffer and go to device memory in one
-``pa_stage_copy`` launch on the step's stream.  Measured per config-3 step:
-the runtime's copy from pinned memory (several launches) 262 us, this copy
-250 us, the kernels reading the pinned buffer in place 249 us but with the
-decode kernel itself ~10 us slower (its table reads cross the host link);
-this copy on a second stream, overlapping the previous step and waited for
-by events, 253 vs 249 us serial.  Host buffers are used round-robin: the
-host fills buffer i+1 while the GPU still runs step i.
+request before the step's forward pass).  The step's slots, lengths and
+work list sit in one pinned host buffer; the block table stays in device
+memory and only its entries that changed since the previous step (a request
+that took a new block, a copy-on-write replacement) travel, as (index,
+value) pairs, so one ``pa_stage_update`` launch on the step's stream moves
+both.  The first step, or one that changes more entries than the update
+list holds, copies the whole table.  Measured per config-3 step before the
+update list: the runtime's copy from pinned memory (several launches)
+262 us, one ``pa_stage_copy`` of the whole padded table 250 us, the kernels
+reading the pinned buffer in place 249 us but with the decode kernel itself
+~10 us slower (its table reads cross the host link); that copy on a second
+stream, overlapping the previous step and waited for by events, 253 vs
+249 us serial.  Host buffers are used round-robin: the host fills buffer
+i+1 while the GPU still runs step i.
 """
 from __future__ import annotations
 
@@ -38,23 +43,33 @@ class DecodeStepper:
         self.max_blocks = -(-self.max_len_cap // L.BLOCK_SIZE)
         dev = cache.device
         self.depth = depth
-        # one int32 staging layout, host and device: slots, tables, lengths,
-        # work list (each section starting on a 64-byte boundary; the work
-        # list last, so a step copies only the entries it uses)
+        # one int32 staging layout in pinned host memory: slots, lengths and
+        # work list (copied every step, so they come first and the work list
+        # last: a step copies only the entries it uses), then table updates
+        # ((index, value) pairs), then a whole table for full uploads; each
+        # section starts on a 64-byte boundary
         p_cap = -(-self.max_len_cap // self.partition)
         up = lambda n: -(-n // 16) * 16
-        self.o_tab = up(self.B)
-        self.o_len = self.o_tab + up(self.B * self.max_blocks)
+        n_tab = self.B * self.max_blocks
+        self.upd_cap = max(1024, 4 * self.B)
+        self.o_len = up(self.B)
         self.o_items = self.o_len + up(self.B)
-        total = up(self.o_items + self.B * p_cap)
+        self.o_upd = up(self.o_items + self.B * p_cap)
+        self.o_full = self.o_upd + up(2 * self.upd_cap)
+        total = self.o_full + up(n_tab)
         self.h_buf = [torch.empty(total, dtype=torch.int32, pin_memory=True) for _ in range(depth)]
         self.h_dev = [L.pa_host_device_pointer(b) for b in self.h_buf]
-        self.d_buf = torch.empty(total, dtype=torch.int32, device=dev)
+        self.d_buf = torch.empty(self.o_upd, dtype=torch.int32, device=dev)
         self.d_slots = self.d_buf[:self.B]
-        self.d_tab = self.d_buf[self.o_tab:self.o_tab + self.B * self.max_blocks].view(
-            self.B, self.max_blocks)
         self.d_len = self.d_buf[self.o_len:self.o_len + self.B]
         self.d_items = self.d_buf[self.o_items:]
+        # the device block table, and what the launches enqueued so far leave
+        # in it (None: nothing yet)
+        self.d_tab_buf = torch.empty(up(n_tab), dtype=torch.int32, device=dev)
+        self.d_tab = self.d_tab_buf[:n_tab].view(self.B, self.max_blocks)
+        self.shadow: Optional[np.ndarray] = None
+        self.full_uploads = 0
+        self.updated_entries = 0
         # event r: the copy out of host buffer r has completed
         self.done = [torch.cuda.Event() for _ in range(depth)]
         self.used = [False] * depth
@@ -76,17 +91,40 @@ class DecodeStepper:
         h = self.h_buf[r].numpy()
         slots_np = h[:self.B]
         _, copies = L.pa_append_slots(self.cache.pool, self.ids, self.ones, slots_out=slots_np)
-        tab_np = h[self.o_tab:self.o_tab + self.B * self.max_blocks].reshape(self.B, self.max_blocks)
+        n_tab = self.B * self.max_blocks
+        tab_np = h[self.o_full:self.o_full + n_tab]
         len_np = h[self.o_len:self.o_len + self.B]
-        L.pa_block_tables(self.cache.pool, self.ids, self.max_blocks, tables=tab_np, lens=len_np)
+        L.pa_block_tables(self.cache.pool, self.ids, self.max_blocks,
+                          tables=tab_np.reshape(self.B, self.max_blocks), lens=len_np)
         max_len = int(len_np.max())
         if max_len > self.max_len_cap:
             raise ValueError("a request outgrew the stepper's max_len_cap")
         self.last_lens = len_np.copy()
         n_items = len(L.pa_decode_work_items(len_np, self.partition, out=h[self.o_items:]))
         nbytes = -(-(self.o_items + n_items) // 4) * 16  # whole 16-byte chunks
+        changed = None
+        if self.shadow is not None:
+            changed = np.flatnonzero(tab_np != self.shadow)
+            if len(changed) > self.upd_cap:
+                changed = None
         with torch.cuda.stream(stream):
-            L.pa_stage_copy(self.h_dev[r], self.d_buf, nbytes, stream)
+            if changed is None:
+                # whole table (16-byte chunks; the device buffer is padded)
+                L.pa_stage_copy(self.h_dev[r] + 4 * self.o_full, self.d_tab_buf,
+                                4 * self.d_tab_buf.numel(), stream)
+                L.pa_stage_copy(self.h_dev[r], self.d_buf, nbytes, stream)
+                self.shadow = tab_np.copy()
+                self.full_uploads += 1
+            else:
+                n_upd = len(changed)
+                upd = h[self.o_upd:self.o_upd + 2 * n_upd].reshape(n_upd, 2)
+                upd[:, 0] = changed
+                upd[:, 1] = tab_np[changed]
+                L.pa_stage_update(self.h_dev[r], self.d_buf, nbytes,
+                                  self.h_dev[r] + 4 * self.o_upd, n_upd, self.d_tab, n_tab,
+                                  stream)
+                self.shadow[changed] = tab_np[changed]
+                self.updated_entries += n_upd
             self.done[r].record(stream)
             self.used[r] = True
             if events is not None:

@@ -1,14 +1,16 @@
 """The decode step the benchmark times, as its stepper runs it: slots
-reserved on the host, tables, lengths and work list moved from pinned host
-memory by one pa_stage_copy launch, the step's K/V stored, then the
-work-list decode (ta-paperlens "LLM serving
-from scratch", scheduler skeleton: blocks are reserved for every running
-request before the forward pass; "fragmentation and PagedAttention": the
-kernel reads K/V through the block table).
+reserved on the host, lengths and work list moved from pinned host memory
+and the device block table brought up to date (its changed entries only)
+by one pa_stage_update launch, the step's K/V stored, then the work-list
+decode (ta-paperlens "LLM serving from scratch", scheduler skeleton: blocks
+are reserved for every running request before the forward pass;
+"fragmentation and PagedAttention": the kernel reads K/V through the block
+table).
 
 The first step must equal the fp64 oracle's decode of the same workload
 step; later steps (the pool grown by one token per request each time) must
-equal, bitwise, a decode planned from scratch on the same pool.
+equal, bitwise, a decode planned from scratch on the same pool, and the
+device table the host library's table of that moment.
 """
 import numpy as np
 import pytest
@@ -22,13 +24,15 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("cfg", ["2", "3"])
 def test_decode_stepper_matches_oracle_then_fresh_plans(cfg):
+    """Config 2 runs 20 steps (every request takes a new block at least once,
+    and one step is forced to copy the whole table again); config 3 runs 3."""
     from pagedattention_block_paged_reshape_amd.cache import (DecodePlan, PagedKVCache,
                                                               run_program)
     from pagedattention_block_paged_reshape_amd.stepper import DecodeStepper
     w = shared_workload(cfg)
     assert list(w.step_ids) == list(w.decode_ids) and set(np.asarray(w.step_n_new)) == {1}
     dev = torch.device("cuda:0")
-    steps = 3
+    steps = 20 if cfg == "2" else 3
     extra = w.batch * (steps // 16 + 2)
     free_order = np.concatenate([np.arange(w.num_blocks, w.num_blocks + extra, dtype=np.int32),
                                  np.asarray(w.free_order, dtype=np.int32)])
@@ -53,16 +57,66 @@ def test_decode_stepper_matches_oracle_then_fresh_plans(cfg):
     err = assert_close(out, ref, f"config {cfg} stepper decode")
     log(f"[stepper] config {cfg} step 1: max err {err:.2e}")
 
+    import pagedattention_block_paged_reshape_amd._lib as L
+    forced = 10 if steps >= 10 else None
     for i in range(2, steps + 1):
+        if i == forced:
+            stepper.upd_cap = 0                 # more changes than the list holds: whole table
         out = stepper.step(q, sk, sv).clone()
         torch.cuda.synchronize()
+        if i == forced:
+            stepper.upd_cap = max(1024, 4 * w.batch)
         lens = stepper.last_lens
         assert (lens == np.asarray([cache.seq_len(int(s)) for s in w.decode_ids])).all()
+        tab, _ = L.pa_block_tables(cache.pool, np.asarray(w.decode_ids, dtype=np.int64),
+                                   stepper.max_blocks)
+        assert np.array_equal(stepper.d_tab.cpu().numpy(), tab), f"step {i}: device table"
         plan = DecodePlan(cache, w.decode_ids, w.n_q, w.scale, 512)
         fresh = plan.run(q).clone()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), fresh.view(torch.int16)), f"step {i}"
         log(f"[stepper] config {cfg} step {i}: bitwise equal to a fresh plan")
+    assert stepper.full_uploads == (2 if forced else 1)
+    if cfg == "2":
+        assert stepper.updated_entries >= w.batch   # every request took a new block
+    log(f"[stepper] config {cfg}: {stepper.full_uploads} whole-table copies, "
+        f"{stepper.updated_entries} entries updated in {steps} steps")
+
+
+def test_stage_update_copies_and_applies_updates_exactly():
+    """pa_stage_update: the dense bytes as pa_stage_copy moves them, and
+    every in-range (index, value) pair applied to the target, from pinned
+    host memory; out-of-range indices are skipped and nothing else changes."""
+    import pagedattention_block_paged_reshape_amd as pa
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    rng = np.random.default_rng(11)
+    n_dense, n_target = 4096 + 64, 70000
+    host = torch.empty(n_dense + 2 * 100000, dtype=torch.int32, pin_memory=True)
+    h = host.numpy()
+    h[:] = rng.integers(-2**31, 2**31 - 1, h.size, dtype=np.int64).astype(np.int32)
+    base = pa.pa_host_device_pointer(host)
+    for n_bytes, n_upd in ((4 * n_dense, 5000), (0, 777), (4 * n_dense, 0), (64, 60000),
+                           (4 * n_dense, 1)):
+        idx = rng.permutation(n_target + 500)[:n_upd].astype(np.int32) - 250  # some out of range
+        vals = rng.integers(-2**31, 2**31 - 1, n_upd, dtype=np.int64).astype(np.int32)
+        pairs = h[n_dense:n_dense + 2 * n_upd].reshape(n_upd, 2)
+        pairs[:, 0] = idx
+        pairs[:, 1] = vals
+        dst = torch.full((n_dense,), -7, dtype=torch.int32, device=dev)
+        target0 = rng.integers(-2**31, 2**31 - 1, n_target, dtype=np.int64).astype(np.int32)
+        target = torch.from_numpy(target0.copy()).to(dev)
+        pa.pa_stage_update(base, dst, n_bytes, base + 4 * n_dense, n_upd, target, n_target,
+                           stream)
+        torch.cuda.synchronize()
+        got = dst.cpu().numpy()
+        k = n_bytes // 4
+        assert np.array_equal(got[:k], h[:k]) and (got[k:] == -7).all()
+        want = target0.copy()
+        ok = (idx >= 0) & (idx < n_target)
+        want[idx[ok]] = vals[ok]
+        assert np.array_equal(target.cpu().numpy(), want)
+        log(f"stage update: {n_bytes} bytes, {n_upd} updates ({int(ok.sum())} in range)")
 
 
 def test_stage_copy_moves_pinned_host_bytes_exactly():

@@ -48,6 +48,20 @@ def test_staging_helpers_reject_bad_arguments_before_any_device_call():
     assert _lib.LIB.pa_stage_copy(256, 512, 20, None) == _lib.PA_ERR_INVALID
     # nothing to copy: no launch
     assert _lib.LIB.pa_stage_copy(256, 512, 0, None) == _lib.PA_OK
+    # pa_stage_update: the copy's rules, plus the update list's
+    up = _lib.LIB.pa_stage_update
+    assert up(None, 512, 16, 1024, 1, 2048, 8, None) == _lib.PA_ERR_INVALID
+    assert up(256 + 4, 512, 16, 1024, 1, 2048, 8, None) == _lib.PA_ERR_INVALID
+    assert up(256, 512, 20, 1024, 1, 2048, 8, None) == _lib.PA_ERR_INVALID
+    assert up(256, 512, 16, None, 1, 2048, 8, None) == _lib.PA_ERR_INVALID
+    assert up(256, 512, 16, 1024, 1, None, 8, None) == _lib.PA_ERR_INVALID
+    assert up(256, 512, 16, 1024 + 4, 1, 2048, 8, None) == _lib.PA_ERR_INVALID
+    assert up(256, 512, 16, 1024, 1, 2048 + 2, 8, None) == _lib.PA_ERR_INVALID
+    assert up(256, 512, 16, 1024, -1, 2048, 8, None) == _lib.PA_ERR_INVALID
+    assert up(256, 512, 16, 1024, 1, 2048, -1, None) == _lib.PA_ERR_INVALID
+    assert up(256, 512, 16, 1024, 1, 2048, 1 << 31, None) == _lib.PA_ERR_INVALID
+    # nothing to copy and no updates: no launch (null pointers allowed then)
+    assert up(None, None, 0, None, 0, None, 0, None) == _lib.PA_OK
 
 
 def test_status_strings_and_kv_bytes():
