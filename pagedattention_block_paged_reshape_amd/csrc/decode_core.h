@@ -565,18 +565,20 @@ template <int D>
 __device__ __forceinline__ void store_rows(const DecodeArgs& a, int g, int b, int p,
                                            int n_parts, int h, int d0, f16x8 r, float m,
                                            float l) {
-  // Streaming (non-temporal) stores: nothing in this launch reads the rows
-  // back, so they should not take cache lines from the K/V gather.
+  // Output rows: streaming (non-temporal) stores, since nothing on the GPU
+  // reads them back.  Partials: plain stores, since the reduce launch that
+  // follows reads them, on the same XCD (both grids put kv head g there);
+  // measured on the Llama-3-70B-shaped layer, 240.3 vs 243.2 us per launch.
   const int G = a.G;
   if (n_parts <= 1) {
     const int64_t qh = static_cast<int64_t>(b) * a.n_kv * G + g * G + h;
     __builtin_nontemporal_store(r, reinterpret_cast<f16x8*>(a.out + qh * D + d0));
   } else {
     const int64_t slot = ((static_cast<int64_t>(b) * a.n_kv + g) * a.p_max + p) * G + h;
-    __builtin_nontemporal_store(r, reinterpret_cast<f16x8*>(a.ws_o + slot * D + d0));
+    *reinterpret_cast<f16x8*>(a.ws_o + slot * D + d0) = r;
     if (d0 == 0) {
-      __builtin_nontemporal_store(m, a.ws_m + slot);
-      __builtin_nontemporal_store(l, a.ws_l + slot);
+      a.ws_m[slot] = m;
+      a.ws_l[slot] = l;
     }
   }
 }
