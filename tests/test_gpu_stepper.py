@@ -83,6 +83,52 @@ def test_decode_stepper_matches_oracle_then_fresh_plans(cfg):
         f"{stepper.updated_entries} entries updated in {steps} steps")
 
 
+def test_fp8_decode_stepper_matches_oracle_then_fresh_plans():
+    """The same stepper over FP8 (E4M3) pools on config 2: the step's K/V are
+    quantised by the store, the first step matches the oracle attending the
+    dequantised pool, and 17 more steps (every request takes a new block)
+    equal fresh plans bitwise, with the device table equal to the host
+    library's each time."""
+    import pagedattention_block_paged_reshape_amd._lib as L
+    from pagedattention_block_paged_reshape_amd.cache import (DecodePlan, PagedKVCache,
+                                                              run_program)
+    from pagedattention_block_paged_reshape_amd.stepper import DecodeStepper
+    k_scale, v_scale = 5.5 / 448, 4.75 / 448
+    w = shared_workload("2")
+    dev = torch.device("cuda:0")
+    steps = 18
+    extra = w.batch * (steps // 16 + 2)
+    free_order = np.concatenate([np.arange(w.num_blocks, w.num_blocks + extra, dtype=np.int32),
+                                 np.asarray(w.free_order, dtype=np.int32)])
+    cache = PagedKVCache(w.num_blocks + extra, w.n_kv, w.d, free_order, dev, kv_dtype="fp8",
+                         k_scale=k_scale, v_scale=v_scale)
+    dk = torch.from_numpy(w.setup_k).to(dev)
+    dv = torch.from_numpy(w.setup_v).to(dev)
+    run_program(cache, w.setup, dk, dv)
+    del dk, dv
+    sk = torch.from_numpy(w.step_k[:w.batch]).to(dev)
+    sv = torch.from_numpy(w.step_v[:w.batch]).to(dev)
+    q = torch.from_numpy(w.q).to(dev)
+    cap = max(cache.seq_len(int(s)) for s in w.decode_ids) + steps
+    stepper = DecodeStepper(cache, w.decode_ids, w.n_q, w.scale, cap, 512)
+    out = stepper.step(q, sk, sv).clone()
+    torch.cuda.synchronize()
+    ref = decode_reference(w, oracle_run(w, "fp8", k_scale, v_scale))
+    err = assert_close(out, ref, "fp8 config 2 stepper decode")
+    ids = np.asarray(w.decode_ids, dtype=np.int64)
+    for i in range(2, steps + 1):
+        out = stepper.step(q, sk, sv).clone()
+        torch.cuda.synchronize()
+        tab, _ = L.pa_block_tables(cache.pool, ids, stepper.max_blocks)
+        assert np.array_equal(stepper.d_tab.cpu().numpy(), tab), f"step {i}: device table"
+        fresh = DecodePlan(cache, w.decode_ids, w.n_q, w.scale, 512).run(q).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), fresh.view(torch.int16)), f"step {i}"
+    assert stepper.full_uploads == 1 and stepper.updated_entries >= w.batch
+    log(f"[stepper] fp8 config 2: step 1 max err {err:.2e}; {steps - 1} more steps bitwise "
+        f"equal to fresh plans, {stepper.updated_entries} table entries updated")
+
+
 def test_stage_update_copies_and_applies_updates_exactly():
     """pa_stage_update: the dense bytes as pa_stage_copy moves them, and
     every in-range (index, value) pair applied to the target, from pinned
