@@ -644,11 +644,14 @@ uint64_t pa_mixed_workspace_bytes(const pa_decode_batch* dec, const pa_prefill_c
  * chunk `pf`, with the results of pa_paged_attention_decode (bitwise the
  * same outputs) and pa_paged_attention_prefill (bitwise the same outputs),
  * with one attention kernel instead of two: its first workgroups compute the
- * chunk's tiles and its remaining workgroups the decode units (two per
- * workgroup, work list order); then the merges of the chunk's key splits and
- * of the decode partitions (two small kernels).  Decode units run on CUs as
- * soon as prefill tiles retire, so memory-bound decode fills the
- * compute-bound chunk's tail.
+ * chunk's tiles and the rest, as many as stay resident, walk the decode work
+ * list as the decode launch's work-list form does (one walk per wavefront
+ * pair, several pairs per workgroup); then the merges of the chunk's key
+ * splits and of the decode partitions (two small kernels).  Decode
+ * workgroups start on CUs as soon as prefill tiles retire, so memory-bound
+ * decode fills the compute-bound chunk's tail.  The decode part's bounded
+ * LDS waits behave as in pa_paged_attention_decode: a give-up leaves that
+ * walk's remaining rows NaN, never stale.
  *   kv: one fp16 pool; num_q_heads and scale apply to both parts.
  *   dec, pf: host structs (read during the call only); a part with batch 0 /
  *   chunk_len 0 is skipped.  dec->work_items must be non-NULL when batch > 0
